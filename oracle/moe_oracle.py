@@ -1,0 +1,258 @@
+"""CPU oracle of the sparse top-k MoE FFN forward (test infrastructure).
+
+This is the plain, slow, obviously-correct reference the HIP path is judged
+against.  It is *test infrastructure*: only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import or
+run it.  The product library never calls it and shares no code with it.
+
+Everything is numpy in float64.  Inputs arrive as float32 arrays (bf16 inputs
+are widened to float32 exactly by the caller), so every product of two inputs
+is exact in float64 and each dot product carries only float64 summation error.
+
+Page legend (titles of the pages the steps are taken from):
+  [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
+  [Hunyuan page]   "混合专家架构大模型Hunyuan-Large：原理剖析与实现机制"
+
+Readings taken where the pages leave a step open (each is listed with its
+reason in the design notes of the repository):
+  * top-k orders experts by descending logit, ties to the lowest expert index,
+    slot j holding the (j+1)-th largest; selection is made on logits, which
+    gives the same set and order as selecting on the softmax probabilities
+    because softmax is strictly increasing;
+  * the routing weight multiplies the expert output after the down
+    projection (the weighted sum of expert outputs of [Qwen3-MoE page] §1,
+    phase 4), and is optionally renormalised over the k selected experts;
+  * the expert MLP is SwiGLU: W2 @ (silu(Wg @ x) * (Wu @ x)), with W13[e]
+    holding the gate rows Wg first and the up rows Wu after them;
+  * the permutation is stable over the flat assignment index f = t*k + j.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+something other than itself (brute force, closed forms, library routines,
+special cases, invariants, metamorphic relations).  Nothing is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Steps 1-3: router linear layer, softmax over all experts, top-k.
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """Router linear layer: l[t,e] = sum_h x[t,h] * W_r[e,h] + b[e].
+
+    [Qwen3-MoE page] §1 forward listing: the gate is a linear layer applied
+    to the flattened hidden states; [Hunyuan page] §二.1 gating formula: the
+    gate is W_g x + b_g.  W_r is stored (out, in) = [E, H].
+    """
+    l = _f64(x) @ _f64(w_router).T
+    if bias is not None:
+        l = l + _f64(bias)[None, :]
+    return l
+
+
+def softmax_all(logits) -> np.ndarray:
+    """Softmax over *all* experts of each token, in float64.
+
+    [Qwen3-MoE page] §1 forward listing (softmax along the expert dimension,
+    before top-k); [Hunyuan page] §二.1 gating formula G(x) = Softmax(W_g x + b_g).
+    The max is subtracted first; this does not change the value.
+    """
+    l = _f64(logits)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def topk_ids(logits, k: int) -> np.ndarray:
+    """Per-token top-k expert ids, int32 [T, k].
+
+    [Qwen3-MoE page] §1 forward listing (topk over the routing scores).
+    Order: descending logit, ties to the lowest expert index, slot j = rank j.
+    numpy's lexsort sorts by the last key first: key (-logit), then expert id.
+    """
+    l = _f64(logits)
+    T, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    eid = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((eid, -l), axis=-1)
+    return np.ascontiguousarray(order[:, :k]).astype(np.int32)
+
+
+def route(x, w_router, bias, k: int, renormalize: bool):
+    """Steps 1-3 together: returns ids [T,k] int32 and weights [T,k] float64.
+
+    The weight of slot j is the softmax probability of the chosen expert
+    ([Qwen3-MoE page] §1 forward listing keeps the top-k probabilities);
+    with ``renormalize`` the k weights of a token are divided by their sum.
+    Also returns the logits and probabilities for the tests.
+    """
+    l = router_logits(x, w_router, bias)
+    p = softmax_all(l)
+    ids = topk_ids(l, k)
+    w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids, w, l, p
+
+
+# ---------------------------------------------------------------------------
+# Step 4: permutation that groups assignment rows by expert.
+# ---------------------------------------------------------------------------
+
+def permute(ids, E: int):
+    """Expert histogram, offsets and the stable expert-sorted permutation.
+
+    [Qwen3-MoE page] §2.2 memory-access optimisation (reorder the tokens by
+    their assigned expert so each expert reads a contiguous block) and its
+    optimised forward pseudocode (sort by expert, gather, scatter back).
+
+    For the flat assignment index f = t*k + j (token t, slot j):
+      counts[e]   = number of f with ids.flat[f] == e
+      offsets     = [0, cumsum(counts)]            (length E+1)
+      perm[r]     = f of the r-th row in (expert, f) order   (stable)
+      inv_perm[f] = r such that perm[r] == f
+    """
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    if counts.shape[0] != E:
+        raise ValueError("expert id out of range")
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable").astype(np.int32)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.shape[0], dtype=np.int32)
+    return counts, offsets.astype(np.int32), perm, inv
+
+
+def gather_rows(x, perm, k: int) -> np.ndarray:
+    """x_perm[r] = x[perm[r] // k]: the reordered hidden states.
+
+    [Qwen3-MoE page] §2.2 optimised forward pseudocode (reordered states).
+    """
+    return np.asarray(x)[np.asarray(perm, dtype=np.int64) // k]
+
+
+# ---------------------------------------------------------------------------
+# Steps 5-6: per-expert SwiGLU MLP over the rows each expert owns.
+# ---------------------------------------------------------------------------
+
+def silu(z) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)), float64."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_mlp(xe, w13_e, w2_e) -> np.ndarray:
+    """One expert's SwiGLU MLP on rows xe [n,H]: W2 (silu(Wg x) * (Wu x)).
+
+    The pages only call each expert a small MLP ([Qwen3-MoE page] §1); the
+    SwiGLU form, with gate rows then up rows stacked in W13 [2I,H] and the
+    down weight W2 [H,I], is the reading taken for this block.
+    """
+    w13_e = _f64(w13_e)
+    I = w13_e.shape[0] // 2
+    xe = _f64(xe)
+    g = xe @ w13_e[:I].T
+    u = xe @ w13_e[I:].T
+    h = silu(g) * u
+    return h @ _f64(w2_e).T
+
+
+def experts(x, perm, offsets, w13, w2, k: int) -> np.ndarray:
+    """Grouped expert compute: Y[r] = expert_{e(r)}(x[perm[r] // k]).
+
+    [Qwen3-MoE page] §1 forward listing (loop over experts, each applied to
+    the tokens routed to it) and §2.1 (all experts in one batched compute);
+    the rows of expert e are offsets[e]..offsets[e+1]-1 of the permutation.
+    Empty experts are skipped and their weights never read.
+    """
+    x = _f64(x)
+    M = int(offsets[-1])
+    H = x.shape[1]
+    Y = np.zeros((M, H), dtype=np.float64)
+    E = len(offsets) - 1
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        rows = np.asarray(perm[r0:r1], dtype=np.int64) // k
+        Y[r0:r1] = expert_mlp(x[rows], w13[e], w2[e])
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# Step 7: routing-weighted combine back to token order.
+# ---------------------------------------------------------------------------
+
+def combine(Y, inv_perm, weights, T: int, k: int) -> np.ndarray:
+    """out[t] = sum_{j<k} w[t,j] * Y[inv_perm[t*k + j]].
+
+    [Qwen3-MoE page] §1 phase 4 (outputs summed with the routing weights)
+    and §2.2 pseudocode (scatter the expert outputs back to token order).
+    """
+    Y = _f64(Y)
+    w = _f64(weights).reshape(T, k)
+    inv = np.asarray(inv_perm, dtype=np.int64).reshape(T, k)
+    out = np.zeros((T, Y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * Y[inv[:, j]]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Whole block.
+# ---------------------------------------------------------------------------
+
+def forward(x, w_router, bias, w13, w2, k: int, renormalize: bool) -> Dict[str, np.ndarray]:
+    """The MoE block forward: route, permute, grouped SwiGLU, combine.
+
+    Step order of the optimised forward pseudocode of [Qwen3-MoE page] §2.2
+    (routing, reorder by expert, batched expert compute, scatter back).
+    Returns the output and every intermediate, all float64 / int32.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    ids, w, l, p = route(x, w_router, bias, k, renormalize)
+    counts, offsets, perm, inv = permute(ids, E)
+    Y = experts(x, perm, offsets, w13, w2, k)
+    out = combine(Y, inv, w, T, k)
+    return dict(out=out, ids=ids, weights=w, logits=l, probs=p, counts=counts,
+                offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
+
+
+def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],
+                   to_f32=None) -> np.ndarray:
+    """Block output for a subset of tokens, one token at a time.
+
+    A token's output depends only on its own row, its k ids and weights
+    ([Qwen3-MoE page] §1: each selected expert processes the token, the
+    results are summed with the routing weights), so large workloads are
+    checked on sampled tokens.  ``ids``/``weights`` are the oracle's routing
+    of those tokens (row i belongs to tokens[i]).  ``to_f32`` widens stored
+    weights (e.g. bf16 bit patterns) expert by expert so a large weight set
+    never has to be widened at once.
+    """
+    conv = to_f32 if to_f32 is not None else (lambda a: a)
+    tokens = [int(t) for t in tokens]
+    ids = np.asarray(ids).reshape(len(tokens), -1)
+    weights = _f64(weights).reshape(len(tokens), -1)
+    H = np.asarray(x).shape[1]
+    out = np.zeros((len(tokens), H), dtype=np.float64)
+    xs = _f64(conv(np.asarray(x)[tokens]))
+    for e in np.unique(ids):
+        sel = np.nonzero(ids == e)
+        rows, slots = sel[0], sel[1]
+        y = expert_mlp(xs[rows], conv(w13[e]), conv(w2[e]))
+        out[rows] += weights[rows, slots][:, None] * y
+    return out

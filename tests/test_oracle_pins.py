@@ -1,0 +1,448 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each pin is a plain function ``pin_*()`` so that ``test_planted_mistakes``
+can plant plausible mistakes into the oracle (on the CPU) and show that at
+least one pin catches every one of them.
+
+Page legend:
+  [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
+  [Hunyuan page]   "混合专家架构大模型Hunyuan-Large：原理剖析与实现机制"
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def _rand_case(T=7, H=6, E=5, k=2, I=3, seed=0, bias=True, ties=False):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((T, H))
+    wr = r.standard_normal((E, H)) / math.sqrt(H)
+    if ties:   # dyadic grid -> many exactly tied logits
+        x = np.round(x * 2) / 2
+        wr = np.round(wr * 2) / 2
+    b = r.standard_normal(E) * 0.5 if bias else None
+    w13 = r.standard_normal((E, 2 * I, H)) / math.sqrt(H)
+    w2 = r.standard_normal((E, H, I)) / math.sqrt(I)
+    return x, wr, b, w13, w2
+
+
+def _torch_swiglu(x, w13_e, w2_e):
+    """Textbook SwiGLU MLP through torch's own float64 ops (a library routine)."""
+    xt = torch.as_tensor(np.asarray(x, np.float64))
+    w = torch.as_tensor(np.asarray(w13_e, np.float64))
+    I = w.shape[0] // 2
+    g = torch.nn.functional.linear(xt, w[:I])
+    u = torch.nn.functional.linear(xt, w[I:])
+    h = torch.nn.functional.silu(g) * u
+    return torch.nn.functional.linear(h, torch.as_tensor(np.asarray(w2_e, np.float64))).numpy()
+
+
+# --------------------------------------------------------------------------
+# Worked example (hand-derived, tests/golden/worked_example.json)
+# --------------------------------------------------------------------------
+
+def pin_worked_example():
+    g = json.load(open(GOLDEN))
+    x, wr, b = np.array(g["x"], float), np.array(g["w_router"], float), np.array(g["bias"], float)
+    w13, w2, k = np.array(g["w13"], float), np.array(g["w2"], float), g["k"]
+    res = O.forward(x, wr, b, w13, w2, k, renormalize=False)
+    assert np.array_equal(res["logits"], np.array(g["expected_logits"], float))
+    assert np.array_equal(res["ids"], np.array(g["expected_ids"]))
+    assert np.array_equal(res["counts"], np.array(g["expected_counts"]))
+    assert np.array_equal(res["offsets"], np.array(g["expected_offsets"]))
+    assert np.array_equal(res["perm"], np.array(g["expected_perm"]))
+    assert np.array_equal(res["inv_perm"], np.array(g["expected_inv_perm"]))
+    e = math.e
+    silu = lambda z: z / (1 + math.exp(-z))  # noqa: E731  (scalar textbook SiLU)
+    # hand-derived outputs (gate value g, up value u of each chosen expert):
+    # t0 -> experts 0 (g=1,u=0) and 2 (g=-1,u=2); both have p = e/(3e+1)
+    p0 = e / (3 * e + 1)
+    out0 = p0 * 0.0 + p0 * (silu(-1.0) * 2.0) * np.array([0.5, 0.5])
+    # t1 -> experts 1 (g=.5,u=1) and 3 (g=.75,u=-1); Z = 1 + 2e + 1/e, both p = e/Z
+    Z1 = 1 + 2 * e + 1 / e
+    out1 = (e / Z1) * silu(0.5) * np.array([-1.0, 1.0]) + (e / Z1) * (-silu(0.75)) * np.array([3.0, -2.0])
+    # t2 -> experts 3 (g=1,u=0) and 0 (g=1,u=1); Z = 2e + 1 + e^1.5
+    Z2 = 2 * e + 1 + math.exp(1.5)
+    out2 = (math.exp(1.5) / Z2) * 0.0 + (e / Z2) * silu(1.0) * np.array([1.0, 2.0])
+    want = np.stack([out0, out1, out2])
+    assert np.allclose(res["out"], want, rtol=1e-14, atol=1e-15)
+    want_w = np.array([[p0, p0], [e / Z1, e / Z1], [math.exp(1.5) / Z2, e / Z2]])
+    assert np.allclose(res["weights"], want_w, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Router, softmax, top-k
+# --------------------------------------------------------------------------
+
+def pin_logits_exact_dyadic():
+    # integers / halves: the exact dot product is known, any summation order gives it
+    x = np.array([[1.0, -2.0, 0.5], [3.0, 0.0, -1.0]])
+    wr = np.array([[2.0, 1.0, 4.0], [-1.0, 0.5, 0.0]])
+    b = np.array([0.25, -1.0])
+    want = np.array([[2 - 2 + 2 + 0.25, -1 - 1 + 0 - 1.0], [6 + 0 - 4 + 0.25, -3 + 0 + 0 - 1.0]])
+    assert np.array_equal(O.router_logits(x, wr, b), want)
+
+
+def pin_softmax_closed_forms():
+    r = np.random.default_rng(1)
+    l = r.standard_normal((9, 6)) * 3
+    p = O.softmax_all(l)
+    assert np.all(p > 0)
+    assert np.allclose(p.sum(1), 1.0, atol=1e-15)
+    # ratio of probabilities is exp of the logit difference (a dropped or
+    # negated term breaks it)
+    assert np.allclose(p[:, 1] / p[:, 4], np.exp(l[:, 1] - l[:, 4]), rtol=1e-13)
+    # two experts: softmax reduces to the logistic function of the gap
+    l2 = r.standard_normal((5, 2))
+    p2 = O.softmax_all(l2)
+    assert np.allclose(p2[:, 0], 1 / (1 + np.exp(l2[:, 1] - l2[:, 0])), rtol=1e-14)
+    # equal logits -> uniform; huge logits do not overflow
+    assert np.allclose(O.softmax_all(np.zeros((2, 8))), 1 / 8)
+    big = O.softmax_all(np.array([[1000.0, 999.0]]))
+    assert np.allclose(big[0, 0], 1 / (1 + math.exp(-1)), rtol=1e-14)
+
+
+def _brute_topk(l, k):
+    """Exhaustive search over ordered k-tuples for the lexicographically best
+    (value desc, id asc) sequence; independent of any sort routine."""
+    E = len(l)
+    best, best_key = None, None
+    for tup in itertools.permutations(range(E), k):
+        key = tuple((l[e], -e) for e in tup)
+        if best_key is None or key > best_key:
+            best, best_key = tup, key
+    return list(best)
+
+
+def pin_topk_bruteforce():
+    for seed, ties in [(2, False), (3, True), (4, True)]:
+        x, wr, b, _, _ = _rand_case(T=12, H=4, E=6, seed=seed, ties=ties, bias=False)
+        l = O.router_logits(x, wr, None)
+        for k in (1, 2, 3, 6):
+            ids = O.topk_ids(l, k)
+            for t in range(l.shape[0]):
+                assert list(ids[t]) == _brute_topk(l[t], k), (seed, k, t)
+
+
+def pin_topk_special_cases():
+    # zero router: every logit ties, ids are 0..k-1 and weights are 1/E
+    x = np.random.default_rng(5).standard_normal((4, 8))
+    ids, w, _, _ = O.route(x, np.zeros((6, 8)), None, 3, False)
+    assert np.array_equal(ids, np.tile(np.arange(3), (4, 1)))
+    assert np.allclose(w, 1 / 6)
+    # duplicated router rows: the lower index of a tied pair comes first
+    wr = np.random.default_rng(6).standard_normal((5, 8))
+    wr[4] = wr[1]
+    l = O.router_logits(x, wr, None)
+    ids = O.topk_ids(l, 5)
+    for t in range(4):
+        pos = list(ids[t])
+        assert pos.index(1) + 1 == pos.index(4)
+    # bias acts inside the softmax: a huge bias on one expert always selects it
+    # with weight ~1 (Hunyuan gating formula)
+    b = np.zeros(5)
+    b[3] = 100.0
+    ids, w, _, _ = O.route(x, wr, b, 1, False)
+    assert np.all(ids[:, 0] == 3) and np.allclose(w[:, 0], 1.0)
+
+
+def pin_route_invariants():
+    for seed in range(3):
+        x, wr, b, _, _ = _rand_case(T=20, H=8, E=7, seed=seed)
+        for k, ren in [(1, False), (3, False), (3, True), (7, True)]:
+            ids, w, l, p = O.route(x, wr, b, k, ren)
+            assert ids.dtype == np.int32 and ids.shape == (20, k)
+            for t in range(20):
+                assert len(set(ids[t])) == k
+                sel = l[t, ids[t]]
+                rest = np.delete(l[t], ids[t])
+                assert rest.size == 0 or sel.min() >= rest.max()
+                assert np.all(np.diff(sel) <= 0)
+            if ren:
+                assert np.allclose(w.sum(1), 1.0)
+                assert np.allclose(w, p[np.arange(20)[:, None], ids] /
+                                   p[np.arange(20)[:, None], ids].sum(1, keepdims=True))
+            else:
+                assert np.array_equal(w, np.take_along_axis(p, ids.astype(np.int64), 1))
+
+
+# --------------------------------------------------------------------------
+# Permutation
+# --------------------------------------------------------------------------
+
+def _brute_permute(ids, E):
+    flat = [int(v) for v in np.asarray(ids).ravel()]
+    M = len(flat)
+    counts = [sum(1 for v in flat if v == e) for e in range(E)]
+    offsets = [sum(counts[:e]) for e in range(E + 1)]
+    perm = [None] * M
+    for f in range(M):
+        rank = sum(1 for g in range(M) if (flat[g], g) < (flat[f], f))
+        perm[rank] = f
+    inv = [perm.index(f) for f in range(M)]
+    return counts, offsets, perm, inv
+
+
+def pin_permute_bruteforce():
+    r = np.random.default_rng(7)
+    for T, k, E in [(1, 1, 1), (5, 2, 3), (9, 3, 8), (16, 4, 4), (0, 2, 3)]:
+        ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]) if T else \
+            np.zeros((0, k), np.int32)
+        c, o, p, i = O.permute(ids, E)
+        bc, bo, bp, bi = _brute_permute(ids, E)
+        assert list(c) == bc and list(o) == bo and list(p) == bp and list(i) == bi
+
+
+def pin_permute_invariants():
+    r = np.random.default_rng(8)
+    T, k, E = 50, 3, 6
+    ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)])
+    c, o, p, i = O.permute(ids, E)
+    assert c.sum() == T * k and o[-1] == T * k and np.all(np.diff(o) == c)
+    assert np.array_equal(np.sort(p), np.arange(T * k))
+    assert np.array_equal(i[p], np.arange(T * k)) and np.array_equal(p[i], np.arange(T * k))
+    e_of_row = ids.ravel()[p]
+    assert np.all(np.diff(e_of_row) >= 0)
+    for e in range(E):
+        seg = p[o[e]:o[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    # each token appears exactly k times
+    assert np.array_equal(np.bincount(p // k, minlength=T), np.full(T, k))
+    xg = O.gather_rows(np.arange(T)[:, None] * np.ones((1, 2)), p, k)
+    assert np.array_equal(xg[:, 0], p // k)
+
+
+# --------------------------------------------------------------------------
+# Experts, combine, whole block
+# --------------------------------------------------------------------------
+
+def pin_silu_closed_forms():
+    z = np.linspace(-6, 6, 25)
+    s = O.silu(z)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert np.allclose(s - O.silu(-z), z, atol=1e-14)            # silu(z) - silu(-z) = z
+    assert np.isclose(O.silu(np.array([math.log(3)]))[0], 0.75 * math.log(3), rtol=1e-15)
+    assert O.silu(np.array([60.0]))[0] == 60.0
+    assert abs(O.silu(np.array([-800.0]))[0]) < 1e-300
+
+
+def pin_expert_mlp_textbook():
+    r = np.random.default_rng(9)
+    H, I = 5, 3
+    xe = r.standard_normal((4, H))
+    w13 = r.standard_normal((2 * I, H))
+    w2 = r.standard_normal((H, I))
+    assert np.allclose(O.expert_mlp(xe, w13, w2), _torch_swiglu(xe, w13, w2), rtol=1e-13, atol=1e-14)
+    # H != I on purpose: a transposed weight would not even broadcast
+
+
+def _brute_dense(x, ids, weights, w13, w2):
+    """Every expert runs on every token; the one-hot top-k mask keeps the
+    chosen ones ([Qwen3-MoE page] §1 forward listing builds that mask)."""
+    T = x.shape[0]
+    E = w13.shape[0]
+    mask = np.zeros((T, E))
+    wt = np.zeros((T, E))
+    for t in range(T):
+        for j, e in enumerate(ids[t]):
+            mask[t, e] = 1.0
+            wt[t, e] = weights[t, j]
+    out = np.zeros_like(np.asarray(x, np.float64))
+    for e in range(E):
+        ye = _torch_swiglu(x, w13[e], w2[e])
+        out += (mask[:, e] * wt[:, e])[:, None] * ye
+    return out
+
+
+def pin_block_vs_brute_dense():
+    for seed, (T, H, E, k, I, ren) in enumerate([(6, 4, 3, 1, 2, False), (11, 6, 5, 2, 3, False),
+                                                 (13, 5, 8, 3, 4, True), (9, 4, 4, 4, 6, False)]):
+        x, wr, b, w13, w2 = _rand_case(T, H, E, k, I, seed=10 + seed)
+        res = O.forward(x, wr, b, w13, w2, k, ren)
+        want = _brute_dense(x, res["ids"], res["weights"], w13, w2)
+        assert np.allclose(res["out"], want, rtol=1e-12, atol=1e-13)
+        # token-at-a-time form used for sampled checks agrees too
+        toks = [0, T - 1, T // 2]
+        sub = O.forward_tokens(x, res["ids"][toks], res["weights"][toks], w13, w2, toks)
+        assert np.allclose(sub, want[toks], rtol=1e-12, atol=1e-13)
+
+
+def pin_special_case_dense_mlp():
+    # E = 1, k = 1: probability 1, the block is the textbook SwiGLU MLP
+    x, wr, b, w13, w2 = _rand_case(T=8, H=5, E=1, k=1, I=3, seed=20)
+    out = O.forward(x, wr, b, w13, w2, 1, False)["out"]
+    assert np.allclose(out, _torch_swiglu(x, w13[0], w2[0]), rtol=1e-13, atol=1e-14)
+
+
+def pin_special_case_identical_experts():
+    # identical experts + renormalised weights: output is MLP(x) whatever the routing
+    x, wr, b, w13, w2 = _rand_case(T=10, H=6, E=5, k=3, I=4, seed=21)
+    w13 = np.repeat(w13[:1], 5, axis=0)
+    w2 = np.repeat(w2[:1], 5, axis=0)
+    out = O.forward(x, wr, b, w13, w2, 3, True)["out"]
+    assert np.allclose(out, _torch_swiglu(x, w13[0], w2[0]), rtol=1e-12, atol=1e-13)
+
+
+def pin_special_case_soft_moe():
+    # k = E without renormalisation: the dense soft mixture sum_e p_e MLP_e(x)
+    x, wr, b, w13, w2 = _rand_case(T=7, H=4, E=4, k=4, I=3, seed=22)
+    out = O.forward(x, wr, b, w13, w2, 4, False)["out"]
+    lt = torch.nn.functional.linear(torch.as_tensor(x), torch.as_tensor(wr), torch.as_tensor(b))
+    p = torch.softmax(lt, dim=1).numpy()
+    want = sum(p[:, e:e + 1] * _torch_swiglu(x, w13[e], w2[e]) for e in range(4))
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_metamorphic():
+    x, wr, b, w13, w2 = _rand_case(T=12, H=5, E=6, k=2, I=3, seed=23)
+    base = O.forward(x, wr, b, w13, w2, 2, False)
+    # relabel experts consistently -> same output, ids relabelled
+    s = np.array([3, 0, 5, 1, 4, 2])          # new expert n is old expert s[n]
+    rel = O.forward(x, wr[s], b[s], w13[s], w2[s], 2, False)
+    assert np.allclose(rel["out"], base["out"], rtol=1e-13, atol=1e-14)
+    assert np.array_equal(s[rel["ids"]], base["ids"])
+    # permute tokens -> permuted output
+    q = np.random.default_rng(24).permutation(12)
+    pt = O.forward(x[q], wr, b, w13, w2, 2, False)
+    assert np.allclose(pt["out"], base["out"][q], rtol=1e-13, atol=1e-14)
+    # the output is linear in the down weights
+    sc = O.forward(x, wr, b, w13, 3.0 * w2, 2, False)
+    assert np.allclose(sc["out"], 3.0 * base["out"], rtol=1e-13, atol=1e-14)
+
+
+def pin_combine_direct():
+    # combine alone on a hand-built Y: out[t] = sum_j w[t,j] Y[inv[t*k+j]]
+    T, k, H = 3, 2, 2
+    inv = np.array([5, 0, 1, 4, 2, 3])
+    Y = np.arange(12, dtype=float).reshape(6, 2)
+    w = np.array([[1.0, 2.0], [0.5, 0.25], [3.0, -1.0]])
+    out = O.combine(Y, inv, w, T, k)
+    want = np.array([[1 * 10 + 2 * 0, 1 * 11 + 2 * 1],
+                     [0.5 * 2 + 0.25 * 8, 0.5 * 3 + 0.25 * 9],
+                     [3 * 4 - 6, 3 * 5 - 7]], dtype=float)
+    assert np.array_equal(out, want)
+
+
+PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes: each plausible slip in the oracle must fail some pin.
+# --------------------------------------------------------------------------
+
+def _orig(name):
+    return getattr(O, name)
+
+
+def _mut_topk_ties_high(l, k):
+    l = np.asarray(l, float)
+    E = l.shape[1]
+    order = np.lexsort((-np.broadcast_to(np.arange(E), l.shape), -l), axis=-1)
+    return np.ascontiguousarray(order[:, :k]).astype(np.int32)
+
+
+def _mut_topk_ascending_slots(l, k):
+    return _orig_topk(l, k)[:, ::-1].copy()
+
+
+_orig_topk = O.topk_ids
+_orig_softmax = O.softmax_all
+_orig_permute = O.permute
+_orig_expert = O.expert_mlp
+_orig_logits = O.router_logits
+_orig_combine = O.combine
+
+
+def _mut_no_bias(x, w, b=None):
+    return _orig_logits(x, w, None)
+
+
+def _mut_softmax_no_max_sub_wrong(l):
+    z = np.exp(np.asarray(l, float))
+    return z / z.sum(axis=0, keepdims=True)      # normalised over the wrong axis
+
+
+def _mut_permute_unstable(ids, E):
+    c, o, p, i = _orig_permute(ids, E)
+    p = p.copy()
+    for e in range(E):                            # reverse within each expert
+        p[o[e]:o[e + 1]] = p[o[e]:o[e + 1]][::-1]
+    inv = np.empty_like(p)
+    inv[p] = np.arange(p.size, dtype=np.int32)
+    return c, o, p, inv
+
+
+def _mut_offsets_inclusive(ids, E):
+    c, o, p, i = _orig_permute(ids, E)
+    o = o.copy()
+    o[:-1] = o[1:]
+    return c, o, p, i
+
+
+def _mut_swap_gate_up(xe, w13_e, w2_e):
+    I = np.asarray(w13_e).shape[0] // 2
+    sw = np.concatenate([w13_e[I:], w13_e[:I]], axis=0)
+    return _orig_expert(xe, sw, w2_e)
+
+
+def _mut_no_silu(xe, w13_e, w2_e):
+    w13_e = np.asarray(w13_e, float)
+    I = w13_e.shape[0] // 2
+    return ((xe @ w13_e[:I].T) * (xe @ w13_e[I:].T)) @ np.asarray(w2_e, float).T
+
+
+def _mut_combine_perm_for_inv(Y, inv, w, T, k):
+    p = np.empty_like(np.asarray(inv))
+    p[np.asarray(inv)] = np.arange(len(inv))
+    return _orig_combine(Y, p, w, T, k)
+
+
+def _mut_combine_unweighted(Y, inv, w, T, k):
+    return _orig_combine(Y, inv, np.ones_like(np.asarray(w, float)), T, k)
+
+
+def _mut_silu_sign(z):
+    z = np.asarray(z, float)
+    return z / (1.0 + np.exp(z))
+
+
+MUTATIONS = {
+    "topk ties to the highest index": ("topk_ids", _mut_topk_ties_high),
+    "topk slots ascending": ("topk_ids", _mut_topk_ascending_slots),
+    "router bias dropped": ("router_logits", _mut_no_bias),
+    "softmax over tokens": ("softmax_all", _mut_softmax_no_max_sub_wrong),
+    "unstable permutation": ("permute", _mut_permute_unstable),
+    "inclusive offsets": ("permute", _mut_offsets_inclusive),
+    "gate and up swapped": ("expert_mlp", _mut_swap_gate_up),
+    "activation dropped": ("expert_mlp", _mut_no_silu),
+    "perm used for inv_perm in combine": ("combine", _mut_combine_perm_for_inv),
+    "routing weight dropped": ("combine", _mut_combine_unweighted),
+    "silu sign flipped": ("silu", _mut_silu_sign),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:  # AssertionError or a shape error both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake '{name}' passed every pin"
