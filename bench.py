@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE block forward on one MI355X.
+
+One step = one moe_forward over one batch of synthetic input (router, softmax,
+top-k, permutation, gate/up grouped GEMM + SwiGLU, down grouped GEMM,
+combine), inputs resident in HBM.  W untimed warm-up steps, then exactly K
+timed steps between synchronisations; per-stage times come from HIP events
+recorded by the library on the stream the kernels run on.  Prints one JSON
+line.  The CPU oracle is timed on a bounded token sample as a reported
+baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + grouped-GEMM % bf16 MFMA peak, 1× MI355X"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+BM = 256                       # rows per grouped-GEMM tile (bf16 kernels)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SOURCES = ["sparse_mixture_experts_19_amd/csrc/gemm_bf16.hip",
+                "sparse_mixture_experts_19_amd/csrc/moe_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic(wl, counts):
+    """Algorithmic flops / bytes per launch of every stage (real rows only;
+    only the weights of experts that own rows are counted)."""
+    b = 2 if wl.dtype == "bf16" else 4
+    T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
+    M = T * k
+    active = int(sum(1 for c in counts if c > 0))
+    st = {}
+    st["route"] = dict(bytes=T * H * b + E * H * b + 8 * M, flops=2 * T * H * E)
+    st["permute"] = dict(bytes=4 * M + 4 * M + 4 * M + 8 * E, flops=0)
+    st["schedule"] = dict(bytes=8 * E, flops=0)
+    st["gemm_gate_up_swiglu"] = dict(flops=4 * M * H * I,
+                                     bytes=2 * active * I * H * b + M * H * b + M * I * b + 4 * M)
+    st["gemm_down"] = dict(flops=2 * M * I * H, bytes=active * H * I * b + M * I * b + M * H * b)
+    st["combine"] = dict(bytes=M * H * b + T * H * b + 8 * M, flops=0)
+    return st
+
+
+def padding_waste(counts, bm=BM):
+    tiles = sum((c + bm - 1) // bm for c in counts)
+    return 1.0 - sum(counts) / (tiles * bm) if tiles else 0.0
+
+
+def cpu_baseline(inp, sample_tokens: int):
+    """Time the oracle as it stands on the first ``sample_tokens`` tokens."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl = inp.wl
+    S = min(sample_tokens, wl.T)
+    x = inp.f32("x")[:S]
+    wr, w13, w2 = inp.f32("w_router"), inp.f32("w13"), inp.f32("w2")
+    t0 = time.perf_counter()
+    res = O.forward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(res["out"]).all()
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {wl.T} tokens of {wl.name}, float64 numpy oracle "
+                      f"(route+permute+experts+combine), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="coarse_bf16")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens for the CPU oracle baseline (default: sized per workload)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--report", default=None, help="also append the JSON record to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every box has one MI355X; see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_19_amd import binding as B
+    from sparse_mixture_experts_19_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {wl.name} ...")
+    t0 = time.perf_counter()
+    inp = W.make_inputs(wl)
+    log(f"[bench] inputs in {time.perf_counter() - t0:.1f} s; uploading")
+
+    def up(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x, wr, w13, w2 = up(inp.x), up(inp.w_router), up(inp.w13), up(inp.w2)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    dt_code = B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
+    out = torch.empty((wl.T, wl.H), dtype=x.dtype, device=dev)
+    ws = torch.empty(B.workspace_size(B.ENTRY_FORWARD, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code),
+                     dtype=torch.uint8, device=dev)
+    nst = len(B.PROFILE_STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.PROFILE_EVENTS)]
+           for _ in range(max(args.steps, 1))]
+    for row in evs:
+        for e in row:
+            e.record()   # creates the underlying HIP event
+    torch.cuda.synchronize()
+
+    def step(i):
+        B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
+                               evs[i % len(evs)])
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stage_ms = {s: 0.0 for s in B.PROFILE_STAGES}
+    for i in range(args.steps):
+        for j, s in enumerate(B.PROFILE_STAGES):
+            stage_ms[s] += evs[i][j].elapsed_time(evs[i][j + 1]) / args.steps
+    mid = B.forward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
+    counts = mid["counts"].cpu().numpy().tolist()
+
+    alg = algorithmic(wl, counts)
+    detail = {}
+    for s in B.PROFILE_STAGES:
+        t = stage_ms[s] * 1e-3
+        d = {"ms": round(stage_ms[s], 5)}
+        if alg[s]["bytes"]:
+            d["GB/s"] = round(alg[s]["bytes"] / t / 1e9, 1)
+        if alg[s]["flops"]:
+            d["TFLOP/s"] = round(alg[s]["flops"] / t / 1e12, 1)
+        detail[s] = d
+    g_t = (stage_ms["gemm_gate_up_swiglu"] + stage_ms["gemm_down"]) * 1e-3
+    g_flops = alg["gemm_gate_up_swiglu"]["flops"] + alg["gemm_down"]["flops"]
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    grouped_tflops = g_flops / g_t / 1e12
+
+    # dominant kernel roofline
+    dom = max(B.PROFILE_STAGES, key=lambda s: stage_ms[s])
+    a = alg[dom]
+    tdom = stage_ms[dom] * 1e-3
+    ai = a["flops"] / a["bytes"] if a["bytes"] else 0.0
+    if a["flops"] and (wl.dtype != "bf16" or ai >= RIDGE_BF16):
+        roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": a["flops"] / tdom / 1e12,
+                "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": a["bytes"] / tdom / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["achieved"] = round(roof["achieved"], 2)
+    roof["frac"] = round(roof["frac"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        rec = tr.get(wl.name, {}).get(dom)
+        if rec and rec.get("source_sha256") == gemm_source_hash():
+            roof["traffic"] = rec["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+
+    rec = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
+        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                   "top_k": wl.k, "intermediate": wl.I, "renormalize": wl.renormalize,
+                   "router_bias": wl.bias, "parallelism": "single GPU"},
+        "grouped_gemm": {"TFLOP/s": round(grouped_tflops, 1),
+                         "frac_of_peak": round(grouped_tflops / peak, 4),
+                         "padding_waste_bm256": round(padding_waste(counts), 4)},
+        "stages": detail,
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        sample = args.cpu_sample or {"tiny_f32": 512, "coarse_bf16": 256, "fine_bf16": 2048,
+                                     "vfine_bf16": 1024, "skewed_bf16": 4096}.get(wl.name, 512)
+        log(f"[bench] CPU oracle baseline on {sample} tokens")
+        rec["cpu_baseline"] = cpu_baseline(inp, sample)
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

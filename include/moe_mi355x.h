@@ -1,0 +1,241 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse top-k Mixture-of-Experts FFN forward
+ * for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * Page legend (titles of the pages that define the operations):
+ *   [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
+ *   [Hunyuan page]   "混合专家架构大模型Hunyuan-Large：原理剖析与实现机制"
+ *   [SonicMoE page]  "SonicMoE与传统MoE架构对比：Token舍入技术如何实现训练效率跃升"
+ *
+ * The block computes, for hidden states x [T,H]:
+ *   1. router logits  l = x W_r^T + b      ([Hunyuan page] §二.1 gating formula)
+ *   2. softmax over all E experts           (same formula; [Qwen3-MoE page] §1 forward listing)
+ *   3. per-token top-k of the logits         ([Qwen3-MoE page] §1 forward listing)
+ *   4. an expert-sorted permutation of the T*k assignments ([Qwen3-MoE page] §2.2)
+ *   5. per expert, SwiGLU  h = silu(x Wg^T) * (x Wu^T), then y = h W2^T
+ *      (one grouped compute over all experts: [Qwen3-MoE page] §2.1)
+ *   6. out[t] = sum_j w[t,j] * y[row of (t,j)]   ([Qwen3-MoE page] §1, phase 4)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Device pointers point to memory of the current HIP device; host pointers
+ *   are marked as such.  Arrays of the bulk dtype (x, weights, h, y, x_perm,
+ *   out) and workspaces must be 16-byte aligned (the moe_forward workspace
+ *   256-byte aligned); int32 and fp32 index/weight arrays 4-byte aligned.
+ *   A misaligned pointer is rejected with MOE_ERR_INVALID_ARG.
+ * - All arrays are dense, row-major, contiguous.  Weights are (out, in):
+ *   w_router [E,H]; w13 [E,2I,H] holding, per expert, the I gate rows and
+ *   then the I up rows; w2 [E,H,I].
+ * - dtype MOE_DTYPE_BF16: x, weights, h, y, x_perm and out are bf16; every
+ *   product is accumulated in fp32; h and y are rounded to bf16 once (round
+ *   to nearest even).  MOE_DTYPE_F32: everything is fp32, computed with fp32
+ *   fused multiply-adds (no reduced-precision matrix path).
+ *   router_bias and topk_weights are always fp32; indices are int32.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   validates on the host and enqueues kernels on `stream`: it does not
+ *   allocate, copy to the host or synchronise.  The caller owns every buffer;
+ *   the library keeps no device memory and no mutable global state besides a
+ *   per-device cache of device properties, so calls on different streams may
+ *   run concurrently as long as their buffers do not overlap.
+ * - Results are deterministic: identical inputs give bitwise identical
+ *   outputs (no floating-point atomics anywhere).
+ * - Limits: 1 <= k <= E, E <= 256, k <= 8, H and I multiples of 64,
+ *   H <= 16384, I <= 65536, T*k <= 2^31-1.  T == 0 is a valid no-op.
+ * - Errors are returned before anything is enqueued; the output buffers are
+ *   then untouched.  moe_last_error() gives a message for the calling thread.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = 2,   /* outside the limits above, unknown dtype, not a gfx950 device */
+    MOE_ERR_WORKSPACE = 3,     /* workspace null or smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_DTYPE_F32 = 0,
+    MOE_DTYPE_BF16 = 1
+} moe_dtype;
+
+typedef enum moe_entry {
+    MOE_ENTRY_ROUTE = 0,
+    MOE_ENTRY_PERMUTE = 1,
+    MOE_ENTRY_GROUPED_GEMM = 2,
+    MOE_ENTRY_COMBINE = 3,
+    MOE_ENTRY_FORWARD = 4
+} moe_entry;
+
+/*
+ * moe_route -- steps 1-3: router linear layer, softmax over all E experts,
+ * per-token top-k.  Defined by the gating formula G(x) = Softmax(W_g x + b_g)
+ * of [Hunyuan page] §二.1 and the softmax-then-topk of the forward listing of
+ * [Qwen3-MoE page] §1.
+ *
+ *   x            [T,H] dtype, device.
+ *   w_router     [E,H] dtype, device.
+ *   router_bias  [E] fp32, device, or NULL for no bias.
+ *   topk_ids     [T,k] int32, device, output.  Slot j holds the expert with
+ *                the (j+1)-th largest logit; ties go to the lowest expert
+ *                index.  The selection is that of the exact logits: tokens
+ *                whose fp32 logits are too close to order safely (closer
+ *                than a rigorous bound on the fp32 summation error) are
+ *                re-ranked with float64 dot products.
+ *   topk_weights [T,k] fp32, device, output: the softmax probability of the
+ *                chosen expert; with renormalize != 0 divided by the sum of
+ *                the token's k probabilities.
+ *   workspace    device scratch of moe_workspace_size(MOE_ENTRY_ROUTE, ...)
+ *                bytes; contents on entry are ignored.
+ */
+int moe_route(const void* x, const void* w_router, const float* router_bias,
+              int64_t T, int32_t H, int32_t E, int32_t k, int32_t dtype,
+              int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute -- step 4: group the T*k assignments by expert
+ * ([Qwen3-MoE page] §2.2: reorder tokens by their expert, gather the states,
+ * scatter the results back).  With f = t*k + j the flat assignment index:
+ *
+ *   topk_ids       [T,k] int32, device; every id must lie in [0,E) (ids out
+ *                  of range are a caller error with undefined results).
+ *   expert_counts  [E] int32, device, output: assignments per expert.
+ *   expert_offsets [E+1] int32, device, output: exclusive prefix sum of the
+ *                  counts; rows of expert e are offsets[e]..offsets[e+1]-1.
+ *   perm           [T*k] int32, device, output: perm[r] = f of row r, rows in
+ *                  (expert, f) order -- a stable sort by expert.
+ *   inv_perm       [T*k] int32, device, output: inv_perm[perm[r]] = r.
+ *   x, x_perm      optional (both NULL or both set): x [T,H] dtype, device;
+ *                  x_perm [T*k,H] dtype, device, output: x_perm[r] = x[perm[r]/k].
+ *   workspace      moe_workspace_size(MOE_ENTRY_PERMUTE, ...) bytes, device.
+ */
+int moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int32_t H,
+                int32_t E, int32_t k, int32_t dtype, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                void* x_perm, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * moe_grouped_swiglu_gemm -- steps 5-6: every expert's SwiGLU MLP over its
+ * rows, in one grouped compute ([Qwen3-MoE page] §2.1: stacked expert
+ * weights, one batched launch scheduled over the compute units).
+ *
+ *   x_perm          [M,H] dtype, device: rows grouped by expert.
+ *   expert_offsets  [E+1] int32, device: rows of expert e are
+ *                   offsets[e]..offsets[e+1]-1; offsets[0] = 0, offsets[E] = M,
+ *                   non-decreasing (empty experts cost nothing and their
+ *                   weights are never read).
+ *   w13             [E,2I,H] dtype, device.   w2 [E,H,I] dtype, device.
+ *   h               [M,I] dtype, device, output: silu(x Wg^T) * (x Wu^T).
+ *   y               [M,H] dtype, device, output: h W2^T.
+ *   workspace       moe_workspace_size(MOE_ENTRY_GROUPED_GEMM, T=M, ..., k=1)
+ *                   bytes, device (tile schedule).
+ */
+int moe_grouped_swiglu_gemm(const void* x_perm, const int32_t* expert_offsets,
+                            const void* w13, const void* w2, int64_t M,
+                            int32_t H, int32_t I, int32_t E, int32_t dtype,
+                            void* h, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine -- step 7: out[t] = sum_{j<k} w[t,j] * y[inv_perm[t*k+j]],
+ * the routing-weighted sum of expert outputs ([Qwen3-MoE page] §1 phase 4,
+ * §2.2 scatter back).  Summed in fp32 in slot order j = 0..k-1 and rounded
+ * once; no atomics.
+ *
+ *   y [T*k,H] dtype, inv_perm [T*k] int32, topk_weights [T,k] fp32,
+ *   out [T,H] dtype (output); all device.
+ */
+int moe_combine(const void* y, const int32_t* inv_perm,
+                const float* topk_weights, int64_t T, int32_t H, int32_t k,
+                int32_t dtype, void* out, void* stream);
+
+/*
+ * moe_forward -- the whole block: route, permute, grouped SwiGLU, combine.
+ * The grouped GEMM reads the rows of x through the permutation directly (no
+ * x_perm copy).  Every intermediate is left in the workspace at the offsets
+ * moe_forward_workspace_layout() reports, so each step can be inspected.
+ *
+ *   x [T,H], w_router [E,H], router_bias [E] fp32 or NULL, w13 [E,2I,H],
+ *   w2 [E,H,I], out [T,H] (output); all device.
+ *   workspace  moe_workspace_size(MOE_ENTRY_FORWARD, ...) bytes, device.
+ */
+int moe_forward(const void* x, const void* w_router, const float* router_bias,
+                const void* w13, const void* w2, int64_t T, int32_t H,
+                int32_t I, int32_t E, int32_t k, int32_t dtype,
+                int32_t renormalize, void* out, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward_profiled -- moe_forward that also records caller-created HIP
+ * events on `stream` around its stages, for per-kernel timing on the stream
+ * the kernels run on.  events: host array of n_events hipEvent_t handles
+ * (passed as void*), n_events == MOE_PROFILE_EVENTS.  events[i] is recorded
+ * before stage i and events[MOE_PROFILE_EVENTS-1] after the last stage:
+ *   0 router (logits, softmax, top-k, float64 re-rank)
+ *   1 permutation (histogram, scan, stable scatter)
+ *   2 tile schedule of the grouped GEMMs
+ *   3 gate/up grouped GEMM with the SiLU(gate)*up epilogue
+ *   4 down grouped GEMM
+ *   5 combine
+ * Arguments and results are otherwise those of moe_forward.
+ */
+#define MOE_PROFILE_EVENTS 7
+int moe_forward_profiled(const void* x, const void* w_router,
+                         const float* router_bias, const void* w13,
+                         const void* w2, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, int32_t dtype,
+                         int32_t renormalize, void* out, void* workspace,
+                         size_t workspace_bytes, void* const* events,
+                         int32_t n_events, void* stream);
+
+/* Byte offsets of the intermediates inside the moe_forward workspace. */
+typedef struct moe_forward_layout {
+    size_t topk_ids;        /* [T,k] int32 */
+    size_t topk_weights;    /* [T,k] fp32 */
+    size_t expert_counts;   /* [E] int32 */
+    size_t expert_offsets;  /* [E+1] int32 */
+    size_t perm;            /* [T*k] int32 */
+    size_t inv_perm;        /* [T*k] int32 */
+    size_t h;               /* [T*k,I] dtype */
+    size_t y;               /* [T*k,H] dtype */
+    size_t scratch;         /* internal */
+    size_t total;           /* == moe_workspace_size(MOE_ENTRY_FORWARD, ...) */
+} moe_forward_layout;
+
+/* Host-only.  Fills *layout; same validation as moe_forward's sizes. */
+int moe_forward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E,
+                                 int32_t k, int32_t dtype,
+                                 moe_forward_layout* layout);
+
+/*
+ * Host-only.  Workspace bytes needed by `entry` (a moe_entry) for these
+ * sizes, written to *bytes (host pointer).  For MOE_ENTRY_GROUPED_GEMM pass
+ * T = M and k = 1.  Sizes that the entry ignores may be given as 1.
+ */
+int moe_workspace_size(int32_t entry, int64_t T, int32_t H, int32_t I,
+                       int32_t E, int32_t k, int32_t dtype, size_t* bytes);
+
+/* Host-only.  Static string naming a moe_status value. */
+const char* moe_status_string(int status);
+
+/* Host-only.  Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Host-only.  ABI version: major*100 + minor. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

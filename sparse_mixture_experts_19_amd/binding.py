@@ -1,0 +1,253 @@
+"""ctypes binding of libmoe_mi355x (the C ABI in include/moe_mi355x.h).
+
+Argument marshalling only: torch tensors supply device pointers, the current
+HIP stream supplies the stream, and every step of the block runs in the HIP
+kernels of the library.  There is no fallback: if the library is missing or
+the device is not gfx950 the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_GROUPED_GEMM, ENTRY_COMBINE, ENTRY_FORWARD = range(5)
+
+_c_i32, _c_i64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} [{status}]")
+        self.status = status
+
+
+class ForwardLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "topk_ids", "topk_weights", "expert_counts", "expert_offsets", "perm", "inv_perm",
+        "h", "y", "scratch", "total")]
+
+
+_SIGS = {
+    "moe_route": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_permute": [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_grouped_swiglu_gemm": [_vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_combine": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _vp, _vp],
+    "moe_forward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
+    "moe_forward_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_workspace_size": [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_forward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
+    "moe_status_string": [_c_i32],
+    "moe_last_error": [],
+    "moe_version": [],
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once (torch first, so its HIP runtime is the one used)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_mixture_experts_19_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name in ("moe_status_string", "moe_last_error") else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        L = lib()
+        raise MoeError(status, f"{L.moe_status_string(status).decode()}: {L.moe_last_error().decode()}")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t == torch.float32:
+        return MOE_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == MOE_DTYPE_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def version() -> int:
+    return lib().moe_version()
+
+
+def workspace_size(entry: int, T: int, H: int, I: int, E: int, k: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(entry, T, H, I, E, k, dtype, ctypes.byref(n)))
+    return n.value
+
+
+def forward_layout(T: int, H: int, I: int, E: int, k: int, dtype: int) -> ForwardLayout:
+    L = ForwardLayout()
+    _check(lib().moe_forward_workspace_layout(T, H, I, E, k, dtype, ctypes.byref(L)))
+    return L
+
+
+def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+def moe_route(x, w_router, router_bias, k: int, renormalize: bool, topk_ids=None,
+              topk_weights=None, workspace=None):
+    """Router logits, softmax over all experts, top-k -> (ids [T,k] int32, weights [T,k] f32)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_size(ENTRY_ROUTE, T, H, 64, E, k, dt), dev, workspace)
+    _check(lib().moe_route(_ptr(x), _ptr(w_router), _ptr(router_bias), T, H, E, k, dt,
+                           int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_weights), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(dev)))
+    return topk_ids, topk_weights
+
+
+def moe_permute(topk_ids, E: int, x=None, workspace=None):
+    """Expert histogram, offsets, stable expert-sorted permutation and its inverse;
+    with ``x`` also the reordered rows.  Returns (counts, offsets, perm, inv, x_perm)."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    H = x.shape[1] if x is not None else 64
+    dt = _dtype_code(x.dtype) if x is not None else MOE_DTYPE_BF16
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev) if x is not None else None
+    ws = _workspace(workspace_size(ENTRY_PERMUTE, T, H, 64, E, k, dt), dev, workspace)
+    _check(lib().moe_permute(_ptr(topk_ids), _ptr(x), T, H, E, k, dt, _ptr(counts), _ptr(offsets),
+                             _ptr(perm), _ptr(inv), _ptr(x_perm), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(dev)))
+    return counts, offsets, perm, inv, x_perm
+
+
+def moe_grouped_swiglu_gemm(x_perm, expert_offsets, w13, w2, h=None, y=None, workspace=None):
+    """Every expert's SwiGLU MLP over its rows of ``x_perm`` -> (h [M,I], y [M,H])."""
+    M, H = x_perm.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x_perm.dtype)
+    dev = x_perm.device
+    if h is None:
+        h = torch.empty((M, I), dtype=x_perm.dtype, device=dev)
+    if y is None:
+        y = torch.empty((M, H), dtype=x_perm.dtype, device=dev)
+    ws = _workspace(workspace_size(ENTRY_GROUPED_GEMM, M, H, I, E, 1, dt), dev, workspace)
+    _check(lib().moe_grouped_swiglu_gemm(_ptr(x_perm), _ptr(expert_offsets), _ptr(w13), _ptr(w2),
+                                         M, H, I, E, dt, _ptr(h), _ptr(y), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(dev)))
+    return h, y
+
+
+def moe_combine(y, inv_perm, topk_weights, out=None):
+    """out[t] = sum_j w[t,j] * y[inv_perm[t*k+j]]."""
+    T, k = topk_weights.shape
+    H = y.shape[1]
+    dev = y.device
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=dev)
+    _check(lib().moe_combine(_ptr(y), _ptr(inv_perm), _ptr(topk_weights), T, H, k,
+                             _dtype_code(y.dtype), _ptr(out), _stream(dev)))
+    return out
+
+
+def moe_forward(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, out=None,
+                workspace=None):
+    """The whole MoE block forward.  Returns (out, workspace); the intermediates
+    can be read from the workspace with ``forward_intermediates``."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    ws = _workspace(workspace_size(ENTRY_FORWARD, T, H, I, E, k, dt), dev, workspace)
+    _check(lib().moe_forward(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2), T, H,
+                             I, E, k, dt, int(bool(renormalize)), _ptr(out), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(dev)))
+    return out, ws
+
+
+PROFILE_EVENTS = 7
+PROFILE_STAGES = ("route", "permute", "schedule", "gemm_gate_up_swiglu", "gemm_down", "combine")
+
+
+def moe_forward_profiled(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, out,
+                         workspace, events):
+    """moe_forward recording ``events`` (7 torch.cuda.Event, timing enabled) on the
+    current stream before each stage and after the last; see PROFILE_STAGES."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if len(events) != PROFILE_EVENTS:
+        raise ValueError(f"need {PROFILE_EVENTS} events")
+    handles = (ctypes.c_void_p * PROFILE_EVENTS)(*[ev.cuda_event for ev in events])
+    _check(lib().moe_forward_profiled(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2),
+                                      T, H, I, E, k, dt, int(bool(renormalize)), _ptr(out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      handles, PROFILE_EVENTS, _stream(dev)))
+    return out
+
+
+def forward_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int, dtype: int):
+    """Typed views of the intermediates moe_forward leaves in its workspace."""
+    L = forward_layout(T, H, I, E, k, dtype)
+    M = T * k
+    eb = 2 if dtype == MOE_DTYPE_BF16 else 4
+
+    def view(off, n, dt, esz, shape):
+        return ws[off:off + n * esz].view(dt).view(shape)
+
+    tdt = _torch_dtype(dtype)
+    return dict(
+        ids=view(L.topk_ids, M, torch.int32, 4, (T, k)),
+        weights=view(L.topk_weights, M, torch.float32, 4, (T, k)),
+        counts=view(L.expert_counts, E, torch.int32, 4, (E,)),
+        offsets=view(L.expert_offsets, E + 1, torch.int32, 4, (E + 1,)),
+        perm=view(L.perm, M, torch.int32, 4, (M,)),
+        inv_perm=view(L.inv_perm, M, torch.int32, 4, (M,)),
+        h=view(L.h, M * I, tdt, eb, (M, I)),
+        y=view(L.y, M * H, tdt, eb, (M, H)),
+    )

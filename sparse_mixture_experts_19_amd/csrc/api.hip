@@ -1,0 +1,440 @@
+// Host side of libmoe_mi355x: argument validation, workspace carving, launch
+// sequencing on the caller's stream.  The ABI is declared, with the meaning
+// of every argument, in include/moe_mi355x.h.
+#include "moe_mi355x.h"
+#include "moe_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- devices
+struct DevInfo {
+  int state;   // 0 unknown, 1 gfx950, 2 other
+  int cu;
+};
+constexpr int kMaxDev = 64;
+std::mutex g_dev_mu;
+DevInfo g_dev[kMaxDev];
+
+int current_device(int* dev_out, int* cu_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev)
+    return fail(MOE_ERR_UNSUPPORTED, "no usable HIP device (%s)", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (d.state == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.state = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    d.cu = p.multiProcessorCount;
+  }
+  if (d.state != 1) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+  if (dev_out) *dev_out = dev;
+  if (cu_out) *cu_out = d.cu;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------- validation
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int elem_bytes(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int check_sizes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t dtype, bool need_I) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (H <= 0) return fail(MOE_ERR_INVALID_ARG, "H must be > 0 (got %d)", H);
+  if (need_I && I <= 0) return fail(MOE_ERR_INVALID_ARG, "I must be > 0 (got %d)", I);
+  if (E <= 0) return fail(MOE_ERR_INVALID_ARG, "E must be > 0 (got %d)", E);
+  if (k <= 0) return fail(MOE_ERR_INVALID_ARG, "k must be > 0 (got %d)", k);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k (%d) must not exceed E (%d)", k, E);
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (E > moe::kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E (%d) > %d", E, moe::kMaxE);
+  if (k > moe::kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k (%d) > %d", k, moe::kMaxK);
+  if (H % 64) return fail(MOE_ERR_UNSUPPORTED, "H (%d) must be a multiple of 64", H);
+  if (H > 16384) return fail(MOE_ERR_UNSUPPORTED, "H (%d) > 16384", H);
+  if (need_I && I % 64) return fail(MOE_ERR_UNSUPPORTED, "I (%d) must be a multiple of 64", I);
+  if (need_I && I > 65536) return fail(MOE_ERR_UNSUPPORTED, "I (%d) > 65536", I);
+  if (T * static_cast<int64_t>(k) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "T*k (%lld) exceeds 2^31-1", (long long)(T * k));
+  if (need_I) {
+    // the persistent GEMM numbers its tiles with 32-bit ints
+    const int64_t M = T * k;
+    const int64_t bm = dtype == MOE_DTYPE_BF16 ? moe::kGemmBM : moe::kF32BM;
+    const int64_t nt1 = dtype == MOE_DTYPE_BF16 ? (I + 127) / 128 : (I + 63) / 64;
+    const int64_t nt2 = dtype == MOE_DTYPE_BF16 ? (H + 255) / 256 : (H + 63) / 64;
+    const int64_t tiles = ((M + bm - 1) / bm + E) * (nt1 > nt2 ? nt1 : nt2);
+    if (tiles > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "problem too large for the tile schedule");
+  }
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)              \
+  do {                               \
+    const int _st = (expr);          \
+    if (_st != MOE_OK) return _st;   \
+  } while (0)
+
+#define MOE_HIP(expr)                                                              \
+  do {                                                                             \
+    const hipError_t _e = (expr);                                                  \
+    if (_e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+int need_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (misaligned(p, align)) return fail(MOE_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ workspaces
+size_t gemm_scratch(int E) { return moe::align_up(static_cast<size_t>(E + 1) * 4, 256); }
+
+struct Carver {
+  size_t o = 0;
+  size_t take(size_t bytes) {
+    const size_t at = o;
+    o = moe::align_up(o + bytes, 256);
+    return at;
+  }
+};
+
+moe_forward_layout forward_layout(int64_t T, int H, int I, int E, int k, int dtype) {
+  const size_t M = static_cast<size_t>(T) * k;
+  const size_t eb = elem_bytes(dtype);
+  Carver c;
+  moe_forward_layout L;
+  L.topk_ids = c.take(M * 4);
+  L.topk_weights = c.take(M * 4);
+  L.expert_counts = c.take(static_cast<size_t>(E) * 4);
+  L.expert_offsets = c.take(static_cast<size_t>(E + 1) * 4);
+  L.perm = c.take(M * 4);
+  L.inv_perm = c.take(M * 4);
+  L.h = c.take(M * I * eb);
+  L.y = c.take(M * H * eb);
+  const size_t shared_sz = moe::route_scratch_bytes(T, E) > moe::permute_scratch_bytes(M, E)
+                               ? moe::route_scratch_bytes(T, E)
+                               : moe::permute_scratch_bytes(M, E);
+  L.scratch = c.take(gemm_scratch(E) + shared_sz);
+  L.total = c.o;
+  return L;
+}
+
+// Router scratch carved from `base`.
+void carve_route(char* base, int64_t T, int E, moe::RouteArgs& a) {
+  Carver c;
+  a.flag = reinterpret_cast<int32_t*>(base + c.take(static_cast<size_t>(T) * 4));
+  a.meta = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 16));
+  a.logits = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * E * 4));
+}
+
+int run_route(const void* x, const void* w_router, const float* bias, int64_t T, int H, int E,
+              int k, int dtype, int renorm, int32_t* ids, float* weights, char* scratch,
+              hipStream_t s) {
+  moe::RouteArgs a{};
+  a.x = x; a.w = w_router; a.bias = bias; a.T = T; a.H = H; a.E = E; a.k = k; a.renorm = renorm;
+  a.ids = ids; a.weights = weights;
+  carve_route(scratch, T, E, a);
+  MOE_HIP(moe::launch_route(a, dtype == MOE_DTYPE_BF16, s));
+  return MOE_OK;
+}
+
+int run_permute(const int32_t* ids, int64_t M, int E, int k, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* inv, char* scratch, hipStream_t s) {
+  moe::PermuteArgs a{};
+  a.ids = ids; a.M = M; a.E = E; a.k = k; a.counts = counts; a.offsets = offsets;
+  a.perm = perm; a.inv = inv; a.block_hist = reinterpret_cast<int32_t*>(scratch);
+  MOE_HIP(moe::launch_permute(a, s));
+  return MOE_OK;
+}
+
+int run_experts(const void* a_rows, const int32_t* gather, int gather_div, const int32_t* offsets,
+                const void* w13, const void* w2, int H, int I, int E, int dtype, void* h, void* y,
+                int32_t* prefix, int cu, hipStream_t s) {
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, prefix, s));
+  moe::GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I;
+  if (bf16) {
+    g.grid = cu >= 8 ? cu / 8 * 8 : 8;
+  } else {
+    g.grid = cu * 2;
+  }
+  // gate/up + SwiGLU
+  g.A = a_rows; g.gather = gather; g.gather_div = gather_div;
+  g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
+  g.C = h; g.N = I; g.K = H;
+  MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
+  // down
+  g.A = h; g.gather = nullptr; g.gather_div = 1;
+  g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
+  g.C = y; g.N = H; g.K = I;
+  MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+int device_cu_count() {
+  int cu = 0;
+  if (current_device(nullptr, &cu) != MOE_OK || cu <= 0) return 256;
+  return cu;
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_workspace_size(int32_t entry, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                       int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  switch (entry) {
+    case MOE_ENTRY_ROUTE:
+      MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
+      *bytes = moe::route_scratch_bytes(T, E);
+      return ok();
+    case MOE_ENTRY_PERMUTE:
+      MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
+      *bytes = moe::permute_scratch_bytes(T * k, E);
+      return ok();
+    case MOE_ENTRY_GROUPED_GEMM:
+      MOE_CHECK(check_sizes(T, H, I, E, 1, dtype, true));
+      *bytes = gemm_scratch(E);
+      return ok();
+    case MOE_ENTRY_COMBINE:
+      MOE_CHECK(check_sizes(T, H, 64, k, k, dtype, false));
+      *bytes = 0;
+      return ok();
+    case MOE_ENTRY_FORWARD:
+      MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+      *bytes = forward_layout(T, H, I, E, k, dtype).total;
+      return ok();
+    default:
+      return fail(MOE_ERR_INVALID_ARG, "unknown entry %d", entry);
+  }
+}
+
+int moe_forward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                 int32_t dtype, moe_forward_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  *layout = forward_layout(T, H, I, E, k, dtype);
+  return ok();
+}
+
+int moe_route(const void* x, const void* w_router, const float* router_bias, int64_t T, int32_t H,
+              int32_t E, int32_t k, int32_t dtype, int32_t renormalize, int32_t* topk_ids,
+              float* topk_weights, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(x, "x", 16));
+  MOE_CHECK(need_ptr(w_router, "w_router", 16));
+  if (router_bias) MOE_CHECK(need_ptr(router_bias, "router_bias", 4));
+  MOE_CHECK(need_ptr(topk_ids, "topk_ids", 4));
+  MOE_CHECK(need_ptr(topk_weights, "topk_weights", 4));
+  const size_t need = moe::route_scratch_bytes(T, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 16));
+  MOE_CHECK(current_device(nullptr, nullptr));
+  MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, topk_ids,
+                      topk_weights, static_cast<char*>(workspace), static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int32_t H, int32_t E, int32_t k,
+                int32_t dtype, int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                int32_t* inv_perm, void* x_perm, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x and x_perm must both be set or both be NULL");
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(topk_ids, "topk_ids", 4));
+  MOE_CHECK(need_ptr(expert_counts, "expert_counts", 4));
+  MOE_CHECK(need_ptr(expert_offsets, "expert_offsets", 4));
+  MOE_CHECK(need_ptr(perm, "perm", 4));
+  MOE_CHECK(need_ptr(inv_perm, "inv_perm", 4));
+  if (x) {
+    MOE_CHECK(need_ptr(x, "x", 16));
+    MOE_CHECK(need_ptr(x_perm, "x_perm", 16));
+  }
+  const int64_t M = T * k;
+  const size_t need = moe::permute_scratch_bytes(M, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "permute needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 16));
+  MOE_CHECK(current_device(nullptr, nullptr));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_CHECK(run_permute(topk_ids, M, E, k, expert_counts, expert_offsets, perm, inv_perm,
+                        static_cast<char*>(workspace), s));
+  if (x) MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, elem_bytes(dtype), x_perm, s));
+  return ok();
+}
+
+int moe_grouped_swiglu_gemm(const void* x_perm, const int32_t* expert_offsets, const void* w13,
+                            const void* w2, int64_t M, int32_t H, int32_t I, int32_t E,
+                            int32_t dtype, void* h, void* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  MOE_CHECK(check_sizes(M, H, I, E, 1, dtype, true));
+  if (M == 0) return ok();
+  MOE_CHECK(need_ptr(x_perm, "x_perm", 16));
+  MOE_CHECK(need_ptr(expert_offsets, "expert_offsets", 4));
+  MOE_CHECK(need_ptr(w13, "w13", 16));
+  MOE_CHECK(need_ptr(w2, "w2", 16));
+  MOE_CHECK(need_ptr(h, "h", 16));
+  MOE_CHECK(need_ptr(y, "y", 16));
+  const size_t need = gemm_scratch(E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "grouped gemm needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 16));
+  int cu = 0;
+  MOE_CHECK(current_device(nullptr, &cu));
+  MOE_CHECK(run_experts(x_perm, nullptr, 1, expert_offsets, w13, w2, H, I, E, dtype, h, y,
+                        static_cast<int32_t*>(workspace), cu, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int moe_combine(const void* y, const int32_t* inv_perm, const float* topk_weights, int64_t T,
+                int32_t H, int32_t k, int32_t dtype, void* out, void* stream) {
+  MOE_CHECK(check_sizes(T, H, 64, k, k, dtype, false));
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(y, "y", 16));
+  MOE_CHECK(need_ptr(inv_perm, "inv_perm", 4));
+  MOE_CHECK(need_ptr(topk_weights, "topk_weights", 4));
+  MOE_CHECK(need_ptr(out, "out", 16));
+  MOE_CHECK(current_device(nullptr, nullptr));
+  MOE_HIP(moe::launch_combine(y, inv_perm, topk_weights, T, H, k, dtype == MOE_DTYPE_BF16, out,
+                              static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
+                 const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                 int32_t dtype, int32_t renormalize, void* out, void* workspace,
+                 size_t workspace_bytes, void* const* events, hipStream_t s) {
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(x, "x", 16));
+  MOE_CHECK(need_ptr(w_router, "w_router", 16));
+  if (router_bias) MOE_CHECK(need_ptr(router_bias, "router_bias", 4));
+  MOE_CHECK(need_ptr(w13, "w13", 16));
+  MOE_CHECK(need_ptr(w2, "w2", 16));
+  MOE_CHECK(need_ptr(out, "out", 16));
+  const moe_forward_layout L = forward_layout(T, H, I, E, k, dtype);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", L.total,
+                workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 256));
+  if (events)
+    for (int i = 0; i < MOE_PROFILE_EVENTS; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  int cu = 0;
+  MOE_CHECK(current_device(nullptr, &cu));
+  char* w = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(w + L.topk_ids);
+  float* wts = reinterpret_cast<float*>(w + L.topk_weights);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + L.expert_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.expert_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(w + L.inv_perm);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.scratch);
+  char* shared = w + L.scratch + gemm_scratch(E);
+  const int64_t M = T * k;
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  auto mark = [&](int i) -> int {
+    if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
+    return MOE_OK;
+  };
+
+  MOE_CHECK(mark(0));
+  MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared, s));
+  MOE_CHECK(mark(1));
+  MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
+  MOE_CHECK(mark(2));
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, prefix, s));
+  MOE_CHECK(mark(3));
+  moe::GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I;
+  g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
+  g.A = x; g.gather = perm; g.gather_div = k;
+  g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
+  g.C = w + L.h; g.N = I; g.K = H;
+  MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
+  MOE_CHECK(mark(4));
+  g.A = w + L.h; g.gather = nullptr; g.gather_div = 1;
+  g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
+  g.C = w + L.y; g.N = H; g.K = I;
+  MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
+  MOE_CHECK(mark(5));
+  MOE_HIP(moe::launch_combine(w + L.y, inv, wts, T, H, k, bf16, out, s));
+  MOE_CHECK(mark(6));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void* x, const void* w_router, const float* router_bias, const void* w13,
+                const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                int32_t dtype, int32_t renormalize, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_profiled(const void* x, const void* w_router, const float* router_bias,
+                         const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, int32_t dtype, int32_t renormalize, void* out,
+                         void* workspace, size_t workspace_bytes, void* const* events,
+                         int32_t n_events, void* stream) {
+  if (!events || n_events != MOE_PROFILE_EVENTS)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS (%d) handles",
+                MOE_PROFILE_EVENTS);
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+// Ragged grouped GEMMs of the expert SwiGLU MLPs on bf16 MFMA (gfx950).
+//
+// Page legend:
+//   [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
+//   [SonicMoE page]  "SonicMoE与传统MoE架构对比：Token舍入技术如何实现训练效率跃升"
+//
+// [Qwen3-MoE page] §2.1 computes all experts in one batched launch over the
+// stacked expert weights, scheduled over the compute units; the rows of each
+// expert are the contiguous block offsets[e]..offsets[e+1]-1 of the
+// permutation (§2.2).  Two kernels:
+//   swiglu: h[r, n]  = silu(sum_k A[r,k] Wg[e,n,k]) * (sum_k A[r,k] Wu[e,n,k])
+//   down:   y[r, n]  = sum_k h[r,k] W2[e,n,k]
+// Row r of A is either row r of a grouped buffer or, for the fused forward,
+// row gather[r] / k of x (the permutation is applied while loading).
+//
+// Design (CDNA4): one persistent workgroup per CU walks a list of 256x256
+// output tiles.  Tiles are numbered expert by expert; inside an expert, G
+// m-tiles form a group that is walked n-tile-major, so the ~32 tiles an XCD
+// runs at once share their weight panels and their rows.  The tile list is
+// cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8),
+// so each range is served by one L2.  Tail m-tiles are masked: no padded rows
+// exist in memory ([SonicMoE page] §核心差异 3 counts the padding such tails
+// cost; it is reported, never materialised).  Empty experts own no tiles and
+// their weights are never read.
+//
+// Per tile: 4 waves in 2x2, each 128x128 outputs = 4x4 MFMA 32x32x16 tiles
+// with fp32 accumulators; K advances in 64-wide stages through two LDS
+// buffers (register prefetch of stage s+1 while stage s is multiplied).  LDS
+// rows are 128 bytes with the 16-byte chunks XOR-swizzled by row.  The MFMA
+// takes the weight rows as its A operand and the token rows as B, so each
+// lane ends with 4 consecutive output columns of one row: the epilogue
+// applies silu(g)*u in registers and stores 8-byte bf16 quads.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = kGemmBM;   // 256 rows
+constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
+constexpr int BK = kGemmBK;   // 64
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  uint2 o;
+  o.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  o.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  return o;
+}
+
+template <bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+  __shared__ uint4 As[2][BM * 8];
+  __shared__ uint4 Bs[2][BN * 8];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_pre[kMaxE + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int E = a.E;
+  for (int i = tid; i <= E; i += 256) { s_off[i] = a.offsets[i]; s_pre[i] = a.prefix[i]; }
+  __syncthreads();
+
+  constexpr int NOUT = SWIGLU ? BN / 2 : BN;   // output columns per tile
+  const int N = a.N, K = a.K;
+  const int NT = (N + NOUT - 1) / NOUT;
+  const int total = s_pre[E] * NT;
+  int G = 32 / NT;
+  G = G < 1 ? 1 : (G > 16 ? 16 : G);
+
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int begin = xcd * chunk;
+  const int end = (begin + chunk < total) ? begin + chunk : total;
+
+  const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
+  const uint16_t* Bb = static_cast<const uint16_t*>(a.B);
+  uint16_t* Cb = static_cast<uint16_t*>(a.C);
+  const int lrow = tid >> 3, lc = tid & 7;
+  const int nk = K / BK;
+
+  for (int L = begin + slot; L < end; L += nslot) {
+    // ---- decode tile L -> (expert, m-tile, n-tile)
+    const int q = L / NT;
+    int lo = 0, hi = E;            // largest e with s_pre[e] <= q
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] <= q) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int local = L - s_pre[e] * NT;
+    const int mte = s_pre[e + 1] - s_pre[e];
+    const int g = local / (G * NT);
+    const int rem = local - g * G * NT;
+    const int gsz = (mte - g * G < G) ? mte - g * G : G;
+    const int nt = rem / gsz;
+    const int mt = g * G + rem % gsz;
+    const int r0 = s_off[e] + mt * BM;
+    const int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
+    const int n0 = nt * NOUT;
+
+    // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds
+    const uint16_t* ap[8];
+    const uint16_t* bp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ri = lrow + 32 * j;
+      const int rr = r0 + (ri < rows ? ri : rows - 1);
+      int64_t src = rr;
+      if constexpr (GATHER) src = a.gather[rr] / a.gather_div;
+      ap[j] = Ab + src * K + lc * 8;
+      int64_t wr;
+      if constexpr (SWIGLU) {
+        const int n = n0 + lrow + 32 * (j & 3);
+        wr = (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
+      } else {
+        const int n = n0 + lrow + 32 * j;
+        wr = n < N ? n : N - 1;
+      }
+      bp[j] = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lc * 8;
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    uint4 ra[8], rb[8];
+    auto gload = [&](int kc) {
+      const int ko = kc * BK;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ra[j] = *reinterpret_cast<const uint4*>(ap[j] + ko);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rb[j] = *reinterpret_cast<const uint4*>(bp[j] + ko);
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) As[buf][swz(lrow + 32 * j, lc)] = ra[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Bs[buf][swz(lrow + 32 * j, lc)] = rb[j];
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+      const int buf = kc & 1;
+      if (kc + 1 < nk) gload(kc + 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 2 * s + (lane >> 5);
+        bf16x8_t xf[4], wf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xf[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][swz(wm * 128 + i * 32 + (lane & 31), c)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int wrow;
+          if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
+          else wrow = wn * 128 + j * 32;
+          wf[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][swz(wrow + (lane & 31), c)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+      }
+      if (kc + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue: lane holds row m, columns 8*grp + 4*(lane>>5) + 0..3 of each 32x32 tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 128 + i * 32 + (lane & 31);
+      if (m >= rows) continue;
+      uint16_t* crow = Cb + static_cast<int64_t>(r0 + m) * N;
+      if constexpr (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int n = n0 + wn * 64 + j * 32 + 8 * grp + 4 * (lane >> 5);
+            if (n >= N) continue;
+            const f32x16_t& gg = acc[i][j];
+            const f32x16_t& uu = acc[i][j + 2];
+            const int b = grp * 4;
+            *reinterpret_cast<uint2*>(crow + n) =
+                pack4_bf16(silu_f(gg[b]) * uu[b], silu_f(gg[b + 1]) * uu[b + 1],
+                           silu_f(gg[b + 2]) * uu[b + 2], silu_f(gg[b + 3]) * uu[b + 3]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int n = n0 + wn * 128 + j * 32 + 8 * grp + 4 * (lane >> 5);
+            if (n >= N) continue;
+            const f32x16_t& cc = acc[i][j];
+            const int b = grp * 4;
+            *reinterpret_cast<uint2*>(crow + n) = pack4_bf16(cc[b], cc[b + 1], cc[b + 2], cc[b + 3]);
+          }
+      }
+    }
+  }
+}
+
+template <bool SWIGLU, bool GATHER>
+hipError_t launch(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s) {
+  return a.gather ? launch<true, true>(a, s) : launch<true, false>(a, s);
+}
+
+hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s) {
+  return launch<false, false>(a, s);
+}
+
+}  // namespace moe

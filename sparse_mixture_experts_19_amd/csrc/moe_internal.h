@@ -1,0 +1,102 @@
+// Internal declarations shared by the HIP translation units of libmoe_mi355x.
+// Nothing here is part of the public C ABI (include/moe_mi355x.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- constants
+constexpr int kWave = 64;              // CDNA wavefront width
+constexpr int kMaxE = 256;             // experts supported
+constexpr int kMaxK = 8;               // top-k supported
+constexpr int kRouteTok = 32;          // tokens per router workgroup
+constexpr int kPermChunk = 1024;       // assignments per permutation workgroup
+constexpr int kGemmBM = 256;           // bf16 grouped GEMM: rows per tile
+constexpr int kGemmBN = 256;           // bf16 grouped GEMM: weight rows per tile
+constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage
+constexpr int kF32BM = 64;             // fp32 grouped GEMM tile
+constexpr int kF32BN = 64;
+constexpr int kF32BK = 16;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------ router (route.hip)
+struct RouteArgs {
+  const void* x;          // [T,H]
+  const void* w;          // [E,H]
+  const float* bias;      // [E] or null
+  int64_t T;
+  int H, E, k, renorm;
+  int32_t* ids;           // [T,k]
+  float* weights;         // [T,k]
+  int32_t* flag;          // [T]     1 = needs the float64 re-rank
+  float* meta;            // [T,4]   max, sum, delta, unused
+  float* logits;          // [T,E]   fp32 logits of flagged tokens
+};
+size_t route_scratch_bytes(int64_t T, int E);
+hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
+
+// ------------------------------------------------- permutation (permute.hip)
+struct PermuteArgs {
+  const int32_t* ids;     // [M] flat topk ids
+  int64_t M;
+  int E, k;
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* perm;          // [M]
+  int32_t* inv;           // [M]
+  int32_t* block_hist;    // [nblocks, E] scratch
+};
+size_t permute_scratch_bytes(int64_t M, int E);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
+                              int elem_bytes, void* x_perm, hipStream_t s);
+
+// Tile schedule of the grouped GEMMs: prefix[e] = sum_{e'<e} ceil(count_e'/bm).
+hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int32_t* prefix,
+                                hipStream_t s);
+
+// --------------------------------------------- grouped GEMMs (gemm_*.hip)
+struct GemmArgs {
+  const void* A;          // rows: [*,K] (x, x_perm or h)
+  const int32_t* gather;  // null: row r of A is r; else row r is gather[r] / gather_div
+  int gather_div;
+  const void* B;          // stacked weights, expert stride b_stride elements
+  int64_t b_stride;
+  void* C;                // [M, N]
+  int N, K;               // output columns, reduction length
+  int I;                  // SwiGLU: rows of the gate block (up rows follow)
+  int E;
+  const int32_t* offsets; // [E+1]
+  const int32_t* prefix;  // [E+1] tile prefix for this kernel's BM
+  int grid;               // persistent workgroups launched
+};
+hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32_swiglu(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32_down(const GemmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------ combine (combine.hip)
+hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t T, int H,
+                          int k, bool bf16, void* out, hipStream_t s);
+
+// ------------------------------------------------------------ device query
+int device_cu_count();
+
+}  // namespace moe

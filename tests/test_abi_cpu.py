@@ -1,0 +1,132 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol,
+sizes its workspaces and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+from sparse_mixture_experts_19_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libmoe_mi355x.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu_gemm", "moe_combine", "moe_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = B.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                             text=True).stdout
+        exported = set(re.findall(r"\sT\s(moe_\w+)$", out, flags=re.M))
+        assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    L = B.lib()
+    assert L.moe_version() == 100
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+    assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def test_workspace_sizes_and_layout():
+    T, H, I, E, k = 4096, 4096, 14336, 8, 2
+    for entry in range(5):
+        assert B.workspace_size(entry, T, H, I, E, k, B.MOE_DTYPE_BF16) >= 0
+    Lay = B.forward_layout(T, H, I, E, k, B.MOE_DTYPE_BF16)
+    offs = [Lay.topk_ids, Lay.topk_weights, Lay.expert_counts, Lay.expert_offsets, Lay.perm,
+            Lay.inv_perm, Lay.h, Lay.y, Lay.scratch, Lay.total]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    M = T * k
+    assert Lay.y - Lay.h >= M * I * 2 and Lay.scratch - Lay.y >= M * H * 2
+    assert Lay.total == B.workspace_size(B.ENTRY_FORWARD, T, H, I, E, k, B.MOE_DTYPE_BF16)
+
+
+FAKE = 0x10000   # aligned, never dereferenced: validation fails first
+
+
+def _route(**kw):
+    a = dict(x=FAKE, w=FAKE, b=None, T=16, H=64, E=8, k=2, dt=1, ren=0, ids=FAKE, wts=FAKE,
+             ws=FAKE, wsb=1 << 30, s=None)
+    a.update(kw)
+    return B.lib().moe_route(a["x"], a["w"], a["b"], a["T"], a["H"], a["E"], a["k"], a["dt"],
+                             a["ren"], a["ids"], a["wts"], a["ws"], a["wsb"], a["s"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9, E=8), B.MOE_ERR_INVALID_ARG),       # k > E
+    (dict(k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(E=300, k=2), B.MOE_ERR_UNSUPPORTED),     # E > 256
+    (dict(E=16, k=9), B.MOE_ERR_UNSUPPORTED),      # k > 8
+    (dict(H=100), B.MOE_ERR_UNSUPPORTED),          # H % 64
+    (dict(dt=7), B.MOE_ERR_UNSUPPORTED),
+    (dict(x=None), B.MOE_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), B.MOE_ERR_INVALID_ARG),     # misaligned
+    (dict(ids=None), B.MOE_ERR_INVALID_ARG),
+    (dict(wsb=16), B.MOE_ERR_WORKSPACE),
+    (dict(ws=None), B.MOE_ERR_WORKSPACE),
+    (dict(T=0, x=None, ids=None), B.MOE_OK),       # T == 0: valid no-op
+])
+def test_route_argument_errors(kw, status):
+    assert _route(**kw) == status
+    if status != B.MOE_OK:
+        assert len(B.lib().moe_last_error()) > 0
+
+
+def test_other_entries_argument_errors():
+    L = B.lib()
+    # permute: x and x_perm must come together
+    assert L.moe_permute(FAKE, FAKE, 8, 64, 4, 2, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, None, 8, 64, 4, 2, 1, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 20,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, None, 8, 64, 4, 2, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4,
+                         None) == B.MOE_ERR_WORKSPACE
+    # grouped gemm: I must be a multiple of 64, workspace large enough
+    assert L.moe_grouped_swiglu_gemm(FAKE, FAKE, FAKE, FAKE, 64, 64, 100, 4, 1, FAKE, FAKE, FAKE,
+                                     1 << 20, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_swiglu_gemm(FAKE, FAKE, FAKE, FAKE, 64, 64, 128, 4, 1, FAKE, FAKE, FAKE,
+                                     8, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_swiglu_gemm(FAKE, FAKE, FAKE, FAKE, 0, 64, 128, 4, 1, None, None, None,
+                                     0, None) == B.MOE_OK
+    # combine
+    assert L.moe_combine(FAKE, FAKE, FAKE, 8, 64, 2, 1, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(FAKE, FAKE, FAKE, 8, 64, 0, 1, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    # forward
+    assert L.moe_forward(FAKE, FAKE, None, FAKE, FAKE, 8, 64, 128, 4, 5, 1, 0, FAKE, FAKE, 1 << 30,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(FAKE, FAKE, None, FAKE, FAKE, 8, 64, 128, 4, 2, 1, 0, FAKE, FAKE, 64,
+                         None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward(FAKE, FAKE, None, FAKE, FAKE, 0, 64, 128, 4, 2, 1, 0, None, None, 0,
+                         None) == B.MOE_OK
+    size = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(9, 8, 64, 64, 4, 2, 1, ctypes.byref(size)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(0, 8, 64, 64, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_gpu_is_unsupported():
+    assert _route() == B.MOE_ERR_UNSUPPORTED
