@@ -169,25 +169,25 @@ int run_permute(const int32_t* ids, int64_t M, int E, int k, int32_t* counts, in
   return MOE_OK;
 }
 
-int run_experts(const void* a_rows, const int32_t* gather, int gather_div, const int32_t* offsets,
-                const void* w13, const void* w2, int H, int I, int E, int dtype, void* h, void* y,
-                int32_t* prefix, int cu, hipStream_t s) {
+int run_experts(const void* a_ptr, int64_t a_rows, const int32_t* gather, int gather_div,
+                const int32_t* offsets, const void* w13, const void* w2, int64_t M, int H, int I,
+                int E, int dtype, void* h, void* y, int32_t* prefix, int cu, hipStream_t s) {
   const bool bf16 = dtype == MOE_DTYPE_BF16;
-  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, prefix, s));
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, M, prefix, s));
   moe::GemmArgs g{};
-  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I;
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = a_rows;
   if (bf16) {
     g.grid = cu >= 8 ? cu / 8 * 8 : 8;
   } else {
     g.grid = cu * 2;
   }
   // gate/up + SwiGLU
-  g.A = a_rows; g.gather = gather; g.gather_div = gather_div;
+  g.A = a_ptr; g.gather = gather; g.gather_div = gather_div;
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
   g.C = h; g.N = I; g.K = H;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
   // down
-  g.A = h; g.gather = nullptr; g.gather_div = 1;
+  g.A = h; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
   g.C = y; g.N = H; g.K = I;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
@@ -327,7 +327,7 @@ int moe_grouped_swiglu_gemm(const void* x_perm, const int32_t* expert_offsets, c
   MOE_CHECK(need_ptr(workspace, "workspace", 16));
   int cu = 0;
   MOE_CHECK(current_device(nullptr, &cu));
-  MOE_CHECK(run_experts(x_perm, nullptr, 1, expert_offsets, w13, w2, H, I, E, dtype, h, y,
+  MOE_CHECK(run_experts(x_perm, M, nullptr, 1, expert_offsets, w13, w2, M, H, I, E, dtype, h, y,
                         static_cast<int32_t*>(workspace), cu, static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -393,17 +393,17 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   MOE_CHECK(mark(1));
   MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
   MOE_CHECK(mark(2));
-  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, prefix, s));
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, M, prefix, s));
   MOE_CHECK(mark(3));
   moe::GemmArgs g{};
-  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I;
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = T;
   g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
   g.A = x; g.gather = perm; g.gather_div = k;
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
   g.C = w + L.h; g.N = I; g.K = H;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
   MOE_CHECK(mark(4));
-  g.A = w + L.h; g.gather = nullptr; g.gather_div = 1;
+  g.A = w + L.h; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
   g.C = w + L.y; g.N = H; g.K = I;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));

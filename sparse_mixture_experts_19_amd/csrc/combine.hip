@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
     for (int j = 0; j < k; ++j) {
-      const int64_t r = inv[t * k + j];
+      int64_t r = inv[t * k + j];
+      r = r < 0 ? 0 : (r >= T * k ? T * k - 1 : r);   // malformed inv_perm stays in bounds
       const float wj = w[t * k + j];
       const uint4 q = y[r * chunks + c];
       if constexpr (BF16) {

@@ -101,7 +101,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int nt = rem / gsz;
     const int mt = g * G + rem % gsz;
     const int r0 = s_off[e] + mt * BM;
-    const int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
+    int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
+    if (r0 < 0 || r0 >= a.M) continue;             // malformed offsets: skip, never fault
+    if (rows > a.M - r0) rows = static_cast<int>(a.M - r0);
+    if (rows <= 0) continue;
     const int n0 = nt * NOUT;
 
     // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds
@@ -112,7 +115,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       const int ri = lrow + 32 * j;
       const int rr = r0 + (ri < rows ? ri : rows - 1);
       int64_t src = rr;
-      if constexpr (GATHER) src = a.gather[rr] / a.gather_div;
+      if constexpr (GATHER) {
+        src = a.gather[rr] / a.gather_div;
+        src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
+      }
       ap[j] = Ab + src * K + lc * 8;
       int64_t wr;
       if constexpr (SWIGLU) {

@@ -47,12 +47,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     }
     const int e = lo;
     const int r0 = s_off[e] + (q - s_pre[e]) * BM;
-    const int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
+    int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
+    if (r0 < 0 || r0 >= a.M) continue;             // malformed offsets: skip, never fault
+    if (rows > a.M - r0) rows = static_cast<int>(a.M - r0);
+    if (rows <= 0) continue;
     const int n0 = nt * BN;
 
     const int rr = r0 + (lr < rows ? lr : rows - 1);
     int64_t src = rr;
-    if constexpr (GATHER) src = a.gather[rr] / a.gather_div;
+    if constexpr (GATHER) {
+      src = a.gather[rr] / a.gather_div;
+      src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
+    }
     const float* ap = Ab + src * K + lk;
     const float* bp[BR / 64];
 #pragma unroll

@@ -69,14 +69,16 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int
                               int elem_bytes, void* x_perm, hipStream_t s);
 
 // Tile schedule of the grouped GEMMs: prefix[e] = sum_{e'<e} ceil(count_e'/bm).
-hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int32_t* prefix,
-                                hipStream_t s);
+hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int64_t M,
+                                int32_t* prefix, hipStream_t s);
 
 // --------------------------------------------- grouped GEMMs (gemm_*.hip)
 struct GemmArgs {
   const void* A;          // rows: [*,K] (x, x_perm or h)
   const int32_t* gather;  // null: row r of A is r; else row r is gather[r] / gather_div
   int gather_div;
+  int64_t a_rows;         // rows of A (gathered row indices are clamped to it)
+  int64_t M;              // rows of C (tile rows are clamped to it)
   const void* B;          // stacked weights, expert stride b_stride elements
   int64_t b_stride;
   void* C;                // [M, N]

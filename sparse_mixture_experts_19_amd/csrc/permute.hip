@@ -59,7 +59,9 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(PermuteArgs a, int nbloc
     off[a.E] = s;
   }
   __syncthreads();
-  if (e <= a.E) a.offsets[e] = off[e];
+  // E may equal the workgroup size (256): the last offset is written separately
+  if (e < a.E) a.offsets[e] = off[e];
+  if (e == 0) a.offsets[a.E] = off[a.E];
   if (e < a.E) {
     const int base = off[e];
     for (int b = 0; b < nblocks; ++b) a.block_hist[static_cast<int64_t>(b) * a.E + e] += base;
@@ -113,23 +115,29 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a) {
 // x_perm[r] = x[perm[r] / k], 16-byte chunks.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
-                                                          int64_t M, int chunks, int k,
-                                                          uint4* __restrict__ xp) {
+                                                          int64_t M, int64_t T, int chunks,
+                                                          int k, uint4* __restrict__ xp) {
   const int64_t total = M * chunks;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t r = i / chunks;
     const int c = static_cast<int>(i - r * chunks);
-    const int64_t src = perm[r] / k;
+    int64_t src = perm[r] / k;
+    src = src < 0 ? 0 : (src >= T ? T - 1 : src);   // malformed perm stays in bounds
     xp[i] = x[src * chunks + c];
   }
 }
 
 __global__ __launch_bounds__(256) void tile_schedule_kernel(const int32_t* offsets, int E, int bm,
-                                                            int32_t* prefix) {
+                                                            int64_t M, int32_t* prefix) {
   __shared__ int mt[kMaxE];
   const int e = threadIdx.x;
-  if (e < E) mt[e] = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  if (e < E) {
+    // rows of expert e, clamped to [0, M] so malformed offsets stay in bounds
+    int64_t c = static_cast<int64_t>(offsets[e + 1]) - offsets[e];
+    c = c < 0 ? 0 : (c > M ? M : c);
+    mt[e] = static_cast<int>((c + bm - 1) / bm);
+  }
   __syncthreads();
   if (e == 0) {
     int s = 0;
@@ -162,13 +170,14 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), perm, M, chunks, k, static_cast<uint4*>(x_perm));
+                     static_cast<const uint4*>(x), perm, M, M / k, chunks, k,
+                     static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 
-hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int32_t* prefix,
+hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int64_t M, int32_t* prefix,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(256), 0, s, offsets, E, bm, prefix);
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(256), 0, s, offsets, E, bm, M, prefix);
   return hipGetLastError();
 }
 
