@@ -25,8 +25,10 @@
 //
 // Per tile: 4 waves in 2x2, each 128x128 outputs = 4x4 MFMA 32x32x16 tiles
 // with fp32 accumulators; K advances in 64-wide stages through two LDS
-// buffers (register prefetch of stage s+1 while stage s is multiplied).  LDS
-// rows are 128 bytes with the 16-byte chunks XOR-swizzled by row.  The MFMA
+// buffers.  Stage s+1 is fetched straight from HBM into LDS
+// (global_load_lds_dwordx4, no staging registers) while stage s is
+// multiplied.  LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
+// row.  The MFMA
 // takes the weight rows as its A operand and the token rows as B, so each
 // lane ends with 4 consecutive output columns of one row: the epilogue
 // applies silu(g)*u in registers and stores 8-byte bf16 quads.
@@ -42,7 +44,14 @@ constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
 constexpr int BK = kGemmBK;   // 64
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// s_waitcnt vmcnt(0): wait for this lane's outstanding vector-memory loads,
+// including the direct-to-LDS ones (expcnt / lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
@@ -55,8 +64,13 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ uint4 As[2][BM * 8];
-  __shared__ uint4 Bs[2][BN * 8];
+  // two LDS stages per operand as four distinct arrays: the compiler's
+  // memory-model tracking can then see that a DMA into one stage never
+  // aliases reads of the other and adds no wait of its own
+  __shared__ uint4 As0[BM * 8];
+  __shared__ uint4 As1[BM * 8];
+  __shared__ uint4 Bs0[BN * 8];
+  __shared__ uint4 Bs1[BN * 8];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -107,7 +121,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     if (rows <= 0) continue;
     const int n0 = nt * NOUT;
 
-    // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds
+    // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds.  Each
+    // lane fetches the 16-byte chunk that lands, through the swizzle, at its
+    // own slot of the direct-to-LDS write (slot = lane & 7 of row r), i.e.
+    // chunk (lane & 7) ^ (r & 7) with r & 7 == (lane >> 3) & 7.
+    const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
     const uint16_t* ap[8];
     const uint16_t* bp[8];
 #pragma unroll
@@ -119,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         src = a.gather[rr] / a.gather_div;
         src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
       }
-      ap[j] = Ab + src * K + lc * 8;
+      ap[j] = Ab + src * K + lchunk * 8;
       int64_t wr;
       if constexpr (SWIGLU) {
         const int n = n0 + lrow + 32 * (j & 3);
@@ -128,7 +146,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int n = n0 + lrow + 32 * j;
         wr = n < N ? n : N - 1;
       }
-      bp[j] = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lc * 8;
+      bp[j] = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lchunk * 8;
     }
 
     f32x16_t acc[4][4];
@@ -139,40 +157,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 ra[8], rb[8];
-    auto gload = [&](int kc) {
+    // K stage kc -> LDS stage (Ad, Bd): global_load_lds_dwordx4, 8 per operand
+    // per lane; wave w's j-th load fills rows 32j + 8w .. 32j + 8w + 7.
+    auto issue = [&](int kc, uint4* Ad, uint4* Bd) {
       const int ko = kc * BK;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ra[j] = *reinterpret_cast<const uint4*>(ap[j] + ko);
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void*)(ap[j] + ko), (lds_void*)&Ad[(j * 4 + wave) * 64],
+                                         16, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rb[j] = *reinterpret_cast<const uint4*>(bp[j] + ko);
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void*)(bp[j] + ko), (lds_void*)&Bd[(j * 4 + wave) * 64],
+                                         16, 0, 0);
     };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) As[buf][swz(lrow + 32 * j, lc)] = ra[j];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Bs[buf][swz(lrow + 32 * j, lc)] = rb[j];
-    };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-      const int buf = kc & 1;
-      if (kc + 1 < nk) gload(kc + 1);
+    auto compute = [&](const uint4* Asrc, const uint4* Bsrc) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 2 * s + (lane >> 5);
         bf16x8_t xf[4], wf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          xf[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][swz(wm * 128 + i * 32 + (lane & 31), c)]);
+          xf[i] = *reinterpret_cast<const bf16x8_t*>(&Asrc[swz(wm * 128 + i * 32 + (lane & 31), c)]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           int wrow;
           if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
           else wrow = wn * 128 + j * 32;
-          wf[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][swz(wrow + (lane & 31), c)]);
+          wf[j] = *reinterpret_cast<const bf16x8_t*>(&Bsrc[swz(wrow + (lane & 31), c)]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -180,9 +191,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
       }
-      if (kc + 1 < nk) sstore(buf ^ 1);
+    };
+
+    // stage kc lives in stage buffer kc & 1; one barrier per stage both
+    // publishes stage kc and frees the buffer stage kc+1 is loaded into
+    issue(0, As0, Bs0);
+    int kc = 0;
+    for (; kc + 1 < nk; kc += 2) {
+      wait_vmem();
       __syncthreads();
+      issue(kc + 1, As1, Bs1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      compute(As0, Bs0);
+      wait_vmem();
+      __syncthreads();
+      if (kc + 2 < nk) issue(kc + 2, As0, Bs0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(As1, Bs1);
     }
+    if (kc < nk) {          // odd number of stages: the last one sits in stage buffer 0
+      wait_vmem();
+      __syncthreads();
+      compute(As0, Bs0);
+    }
+    __syncthreads();        // all reads of this tile's buffers done before the next tile's loads
 
     // ---- epilogue: lane holds row m, columns 8*grp + 4*(lane>>5) + 0..3 of each 32x32 tile
 #pragma unroll

@@ -47,6 +47,7 @@ def test_permute_parity(T, E, k):
 def test_permute_skewed_and_empty_experts():
     E = 64
     zipf = np.array([(r + 1.0) ** -2.5 for r in range(E)])
+    zipf[-10:] = 0.0                       # ten experts never chosen
     ids = _random_ids(5000, E, 4, seed=11, skew=zipf)
     assert (np.bincount(ids.ravel(), minlength=E) == 0).any()
     _check(ids, E)
