@@ -14,9 +14,9 @@
 // row gather[r] / k of x (the permutation is applied while loading).
 //
 // Design (CDNA4): one persistent workgroup per CU walks a list of 256x256
-// output tiles.  Tiles are numbered expert by expert; inside an expert, G
-// m-tiles form a group that is walked n-tile-major, so the ~32 tiles an XCD
-// runs at once share their weight panels and their rows.  The tile list is
+// output tiles.  Tiles are numbered expert by expert; inside an expert, up to
+// 8 m-tiles form a group that is walked n-tile-major, so the ~32 tiles an
+// XCD runs at once share their weight panels and their rows.  The tile list is
 // cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8),
 // so each range is served by one L2.  Tail m-tiles are masked: no padded rows
 // exist in memory ([SonicMoE page] §核心差异 3 counts the padding such tails
@@ -43,6 +43,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
 constexpr int BK = kGemmBK;   // 64
+constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -84,8 +85,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int N = a.N, K = a.K;
   const int NT = (N + NOUT - 1) / NOUT;
   const int total = s_pre[E] * NT;
-  int G = 32 / NT;
-  G = G < 1 ? 1 : (G > 16 ? 16 : G);
 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
   const int chunk = (total + 7) >> 3;
@@ -109,6 +108,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int e = lo;
     const int local = L - s_pre[e] * NT;
     const int mte = s_pre[e + 1] - s_pre[e];
+    // group up to kGroupM m-tiles of the expert: the ~32 tiles an XCD runs at
+    // once then cover every m-tile of a weight panel, so each panel streams
+    // from HBM once per group instead of once per m-tile
+    const int G = mte < kGroupM ? mte : kGroupM;
     const int g = local / (G * NT);
     const int rem = local - g * G * NT;
     const int gsz = (mte - g * G < G) ? mte - g * G : G;
