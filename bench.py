@@ -101,6 +101,8 @@ def main():
                     help="tokens for the CPU oracle baseline (default: sized per workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--report", default=None, help="also append the JSON record to this file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run device-to-device copies of MB MiB (scales HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,9 +117,19 @@ def main():
     from sparse_mixture_experts_19_amd import binding as B
     from sparse_mixture_experts_19_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
+
+    wl = W.WORKLOADS[args.workload]
     log(f"[bench] generating {wl.name} ...")
     t0 = time.perf_counter()
     inp = W.make_inputs(wl)

@@ -28,7 +28,7 @@
 // buffers.  Stage s+1 is fetched straight from HBM into LDS
 // (global_load_lds_dwordx4, no staging registers) while stage s is
 // multiplied.  LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
-// row.  The MFMA
+// row pairs so that MFMA operand reads are free of bank conflicts.  The MFMA
 // takes the weight rows as its A operand and the token rows as B, so each
 // lane ends with 4 consecutive output columns of one row: the epilogue
 // applies silu(g)*u in registers and stores 8-byte bf16 quads.
@@ -48,7 +48,10 @@ constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// 16-byte chunk c (0..7) of row r of a 128-byte-row LDS tile sits in slot
+// c ^ ((r >> 1) & 7): the 16 lanes an LDS cycle serves (16 consecutive rows,
+// same chunk) then cover all 64 banks exactly once.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // s_waitcnt vmcnt(0): wait for this lane's outstanding vector-memory loads,
 // including the direct-to-LDS ones (expcnt / lgkmcnt left at their maxima).
@@ -126,9 +129,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 
     // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds.  Each
     // lane fetches the 16-byte chunk that lands, through the swizzle, at its
-    // own slot of the direct-to-LDS write (slot = lane & 7 of row r), i.e.
-    // chunk (lane & 7) ^ (r & 7) with r & 7 == (lane >> 3) & 7.
-    const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
+    // own slot of the direct-to-LDS write (slot lane & 7 of row
+    // r = 32 j + 8 wave + lane / 8), i.e. chunk (lane & 7) ^ ((r >> 1) & 7),
+    // and (r >> 1) & 7 == (4 wave + lane / 16) & 7 for every j.
+    const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
     const uint16_t* ap[8];
     const uint16_t* bp[8];
 #pragma unroll
