@@ -24,11 +24,13 @@
 // their weights are never read.
 //
 // Per tile: 4 waves in 2x2, each 128x128 outputs = 4x4 MFMA 32x32x16 tiles
-// with fp32 accumulators; K advances in 64-wide stages through two LDS
-// buffers.  Stage s+1 is fetched straight from HBM into LDS
-// (global_load_lds_dwordx4, no staging registers) while stage s is
-// multiplied.  LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
-// row pairs so that MFMA operand reads are free of bank conflicts.  The MFMA
+// with fp32 accumulators.  K advances in 32-wide stages through four LDS
+// stage buffers; stages are fetched straight from HBM into LDS
+// (global_load_lds_dwordx4, no staging registers) three stages ahead of the
+// MFMAs, and the first three stages of a workgroup's next tile are issued
+// before the current tile's epilogue, so loads overlap the stores.  LDS rows
+// are 64 bytes whose 16-byte chunks are XOR-swizzled by row quads, which
+// keeps the MFMA operand reads free of bank conflicts.  The MFMA
 // takes the weight rows as its A operand and the token rows as B, so each
 // lane ends with 4 consecutive output columns of one row: the epilogue
 // applies silu(g)*u in registers and stores 8-byte bf16 quads.
@@ -42,20 +44,53 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
-constexpr int BK = kGemmBK;   // 64
+constexpr int BK = kGemmBK;   // 32
 constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
+constexpr int kLoadsPerStage = 8;   // DMA instructions per lane per stage (4 A + 4 B)
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// 16-byte chunk c (0..7) of row r of a 128-byte-row LDS tile sits in slot
-// c ^ ((r >> 1) & 7): the 16 lanes an LDS cycle serves (16 consecutive rows,
+// 16-byte chunk c (0..3) of row r of a 64-byte-row LDS tile sits in slot
+// c ^ ((r >> 2) & 3): the 16 lanes an LDS cycle serves (16 consecutive rows,
 // same chunk) then cover all 64 banks exactly once.
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
-// s_waitcnt vmcnt(0): wait for this lane's outstanding vector-memory loads,
-// including the direct-to-LDS ones (expcnt / lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(8 n) (expcnt / lgkmcnt left at their maxima).  A stage is
+// 8 DMA loads per lane and vector-memory loads of a wave complete in issue
+// order, so waiting until at most 8 n are outstanding guarantees that every
+// stage but the newest n has landed, whatever stores are interleaved.
+__device__ __forceinline__ void wait_stages_outstanding(int n) {
+  if (n >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+}
+
+// One 16-byte-per-lane DMA global -> LDS (global_load_lds_dwordx4): lane i's
+// 16 bytes land at LDS byte address lds + 16 i.  lds must be wave-uniform.
+// Issued from asm so that the compiler's LDS-DMA bookkeeping, which merges
+// stages conservatively at loop back-edges and then drains the whole queue
+// (vmcnt(0)), stays out of the pipeline; completion is tracked explicitly with
+// wait_stages_outstanding().  The instruction writes no VGPR.  M0 is set right
+// before it (one wait state apart) and is not used by any other code of these
+// kernels.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)p));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those wait for every outstanding vector-memory op (vmcnt(0)), which would
+// drain the prefetch queue.  LDS reads are complete (lgkmcnt(0)) and DMA
+// stages are waited for explicitly; the memory clobber keeps the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
@@ -66,15 +101,21 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   return o;
 }
 
+struct Tile {
+  int e, r0, rows, n0;
+};
+
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
-  // two LDS stages per operand as four distinct arrays: the compiler's
-  // memory-model tracking can then see that a DMA into one stage never
-  // aliases reads of the other and adds no wait of its own
-  __shared__ uint4 As0[BM * 8];
-  __shared__ uint4 As1[BM * 8];
-  __shared__ uint4 Bs0[BN * 8];
-  __shared__ uint4 Bs1[BN * 8];
+  // four stage buffers per operand as distinct arrays: the compiler's memory
+  // model then sees that a DMA into one stage never aliases reads of another
+  // and adds no wait of its own
+  // (each holds the A rows then the B rows of one stage; few distinct DMA
+  // targets keep the compiler's per-target tracking exact)
+  __shared__ uint4 S0[(BM + BN) * 4];
+  __shared__ uint4 S1[(BM + BN) * 4];
+  __shared__ uint4 S2[(BM + BN) * 4];
+  __shared__ uint4 S3[(BM + BN) * 4];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -88,6 +129,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int N = a.N, K = a.K;
   const int NT = (N + NOUT - 1) / NOUT;
   const int total = s_pre[E] * NT;
+  const int nk = K / BK;
 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
   const int chunk = (total + 7) >> 3;
@@ -97,11 +139,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
   const uint16_t* Bb = static_cast<const uint16_t*>(a.B);
   uint16_t* Cb = static_cast<uint16_t*>(a.C);
-  const int lrow = tid >> 3, lc = tid & 7;
-  const int nk = K / BK;
 
-  for (int L = begin + slot; L < end; L += nslot) {
-    // ---- decode tile L -> (expert, m-tile, n-tile)
+  // tile L -> (expert, first row, rows, first output column); false for
+  // tiles that malformed offsets would place outside [0, M)
+  auto decode = [&](int L, Tile& t) -> bool {
     const int q = L / NT;
     int lo = 0, hi = E;            // largest e with s_pre[e] <= q
     while (hi - lo > 1) {
@@ -111,34 +152,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int e = lo;
     const int local = L - s_pre[e] * NT;
     const int mte = s_pre[e + 1] - s_pre[e];
-    // group up to kGroupM m-tiles of the expert: the ~32 tiles an XCD runs at
-    // once then cover every m-tile of a weight panel, so each panel streams
-    // from HBM once per group instead of once per m-tile
+    // up to kGroupM m-tiles of the expert walked n-tile-major: the ~32 tiles
+    // an XCD runs at once cover every m-tile of a weight panel, so a panel
+    // streams from HBM once per group instead of once per m-tile
     const int G = mte < kGroupM ? mte : kGroupM;
     const int g = local / (G * NT);
     const int rem = local - g * G * NT;
     const int gsz = (mte - g * G < G) ? mte - g * G : G;
     const int nt = rem / gsz;
     const int mt = g * G + rem % gsz;
-    const int r0 = s_off[e] + mt * BM;
-    int rows = (s_off[e + 1] - r0 < BM) ? s_off[e + 1] - r0 : BM;
-    if (r0 < 0 || r0 >= a.M) continue;             // malformed offsets: skip, never fault
-    if (rows > a.M - r0) rows = static_cast<int>(a.M - r0);
-    if (rows <= 0) continue;
-    const int n0 = nt * NOUT;
+    t.e = e;
+    t.r0 = s_off[e] + mt * BM;
+    t.rows = (s_off[e + 1] - t.r0 < BM) ? s_off[e + 1] - t.r0 : BM;
+    t.n0 = nt * NOUT;
+    if (t.r0 < 0 || t.r0 >= a.M) return false;
+    if (t.rows > a.M - t.r0) t.rows = static_cast<int>(a.M - t.r0);
+    return t.rows > 0;
+  };
 
-    // ---- per-thread source rows (8 of A, 8 of B), clamped in bounds.  Each
-    // lane fetches the 16-byte chunk that lands, through the swizzle, at its
-    // own slot of the direct-to-LDS write (slot lane & 7 of row
-    // r = 32 j + 8 wave + lane / 8), i.e. chunk (lane & 7) ^ ((r >> 1) & 7),
-    // and (r >> 1) & 7 == (4 wave + lane / 16) & 7 for every j.
-    const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-    const uint16_t* ap[8];
-    const uint16_t* bp[8];
+  // Per-lane source rows.  Wave w's j-th DMA of a stage fills LDS rows
+  // 64 j + 16 w .. +15 (16 rows x 4 slots = 64 lanes x 16 bytes); the lane
+  // writes slot lane & 3 of row 64 j + 16 w + lane / 4 and so fetches chunk
+  // (lane & 3) ^ ((row >> 2) & 3) == (lane & 3) ^ ((lane >> 4) & 3).
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int lrow = 16 * wave + (lane >> 2);
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
+  auto set_rows = [&](const Tile& t) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int ri = lrow + 32 * j;
-      const int rr = r0 + (ri < rows ? ri : rows - 1);
+    for (int j = 0; j < 4; ++j) {
+      const int ri = lrow + 64 * j;
+      const int rr = t.r0 + (ri < t.rows ? ri : t.rows - 1);
       int64_t src = rr;
       if constexpr (GATHER) {
         src = a.gather[rr] / a.gather_div;
@@ -147,16 +191,129 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       ap[j] = Ab + src * K + lchunk * 8;
       int64_t wr;
       if constexpr (SWIGLU) {
-        const int n = n0 + lrow + 32 * (j & 3);
-        wr = (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
+        const int n = t.n0 + (ri & 127);
+        wr = (n < a.I ? n : a.I - 1) + (j >= 2 ? a.I : 0);
       } else {
-        const int n = n0 + lrow + 32 * j;
+        const int n = t.n0 + ri;
         wr = n < N ? n : N - 1;
       }
-      bp[j] = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lchunk * 8;
+      bp[j] = Bb + static_cast<int64_t>(t.e) * a.b_stride + wr * K + lchunk * 8;
     }
+  };
 
-    f32x16_t acc[4][4];
+  // LDS byte address of stage buffer b for this wave's first DMA
+  const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
+  const uint32_t sb0 = __builtin_amdgcn_readfirstlane(lds_addr(S0) + wofs);
+  const uint32_t sb1 = __builtin_amdgcn_readfirstlane(lds_addr(S1) + wofs);
+  const uint32_t sb2 = __builtin_amdgcn_readfirstlane(lds_addr(S2) + wofs);
+  const uint32_t sb3 = __builtin_amdgcn_readfirstlane(lds_addr(S3) + wofs);
+  auto issue = [&](int kc, uint32_t sb) {
+    const int ko = kc * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(ap[j] + ko, sb + j * 4 * 64 * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(bp[j] + ko, sb + BM * 4 * 16 + j * 4 * 64 * 16);
+  };
+  auto prologue = [&]() {
+    issue(0, sb0);
+    if (1 < nk) issue(1, sb1);
+    if (2 < nk) issue(2, sb2);
+  };
+
+  f32x16_t acc[4][4];
+  struct Frag {
+    bf16x8_t x[4], w[4];
+  };
+  // operand fragments of K16 step s (0, 1) of the stage held in Ss
+  auto load_frags = [&](const uint4* Ss, int s, Frag& F) {
+    const uint4* As = Ss;
+    const uint4* Bs = Ss + BM * 4;
+    const int c = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      F.x[i] = *reinterpret_cast<const bf16x8_t*>(&As[swz(wm * 128 + i * 32 + (lane & 31), c)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int wrow;
+      if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
+      else wrow = wn * 128 + j * 32;
+      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[swz(wrow + (lane & 31), c)]);
+    }
+  };
+  // single-instruction pieces, so that a stage can be written as an
+  // explicit MFMA / memory interleave
+  auto mfma1 = [&](const Frag& F, int t) {
+    const int i = t >> 2, j = t & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[j], F.x[i], acc[i][j], 0, 0, 0);
+  };
+  auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {   // t < 4: x[t], else w[t-4]
+    const int c = 2 * s + (lane >> 5);
+    if (t < 4) {
+      F.x[t] = *reinterpret_cast<const bf16x8_t*>(&Ss[swz(wm * 128 + t * 32 + (lane & 31), c)]);
+    } else {
+      const int j = t - 4;
+      int wrow;
+      if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
+      else wrow = wn * 128 + j * 32;
+      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Ss[BM * 4 + swz(wrow + (lane & 31), c)]);
+    }
+  };
+  auto dma1 = [&](int kc, uint32_t sb, int t) {                  // t < 4: A row j, else B
+    const int ko = kc * BK;
+    if (t < 4) dma16(ap[t] + ko, sb + t * 4 * 64 * 16);
+    else dma16(bp[t - 4] + ko, sb + BM * 4 * 16 + (t - 4) * 4 * 64 * 16);
+  };
+
+  // Stage kc sits in buffer kc % 4.  Iteration kc: this lane waits for its own
+  // DMA of stage kc+1 (stage kc+2 may stay in flight), then the barrier makes
+  // stage kc+1 visible everywhere and retires every read of stage kc-1, so
+  // stage kc+3 can be loaded into that buffer.  Fragments are double-buffered
+  // (step 1 of stage kc loads during step 0, step 0 of stage kc+1 during step
+  // 1) and every LDS read and DMA is issued between two MFMAs, so with one
+  // wave per SIMD the matrix pipe only idles at the barrier.
+  Frag Fa, Fb;
+  auto step = [&](int kc, const uint4* Ss, const uint4* Sn, uint32_t sb3) {
+    if (kc + 1 < nk) wait_stages_outstanding(kc + 2 < nk ? 1 : 0);
+    lds_barrier();
+    const bool dma = kc + 3 < nk;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mfma1(Fa, t);
+      frag1(Ss, 1, Fb, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mfma1(Fa, 8 + t);
+      if (dma) dma1(kc + 3, sb3, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // unconditional: on a tile's last stage the next-stage reads hit a stale
+    // buffer that no DMA targets and are discarded; a branch here would make
+    // the compiler's LDS wait counts conservative
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mfma1(Fb, t);
+      frag1(Sn, 0, Fa, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mfma1(Fb, 8 + t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  Tile cur;
+  int L = begin + slot;
+  bool have = false;
+  for (; L < end; L += nslot)
+    if (decode(L, cur)) { have = true; break; }
+  if (!have) return;
+  set_rows(cur);
+  prologue();
+
+  while (true) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -164,77 +321,47 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // K stage kc -> LDS stage (Ad, Bd): global_load_lds_dwordx4, 8 per operand
-    // per lane; wave w's j-th load fills rows 32j + 8w .. 32j + 8w + 7.
-    auto issue = [&](int kc, uint4* Ad, uint4* Bd) {
-      const int ko = kc * BK;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds((glb_void*)(ap[j] + ko), (lds_void*)&Ad[(j * 4 + wave) * 64],
-                                         16, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds((glb_void*)(bp[j] + ko), (lds_void*)&Bd[(j * 4 + wave) * 64],
-                                         16, 0, 0);
-    };
-    auto compute = [&](const uint4* Asrc, const uint4* Bsrc) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = 2 * s + (lane >> 5);
-        bf16x8_t xf[4], wf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xf[i] = *reinterpret_cast<const bf16x8_t*>(&Asrc[swz(wm * 128 + i * 32 + (lane & 31), c)]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int wrow;
-          if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
-          else wrow = wn * 128 + j * 32;
-          wf[j] = *reinterpret_cast<const bf16x8_t*>(&Bsrc[swz(wrow + (lane & 31), c)]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
-      }
-    };
+    // stage 0 of this tile: own DMA done (stages 1, 2 may be in flight), then
+    // visible to every wave; its first fragments are loaded up front
+    wait_stages_outstanding(nk - 1 < 2 ? nk - 1 : 2);
+    lds_barrier();
+    load_frags(S0, 0, Fa);
 
-    // stage kc lives in stage buffer kc & 1; one barrier per stage both
-    // publishes stage kc and frees the buffer stage kc+1 is loaded into
-    issue(0, As0, Bs0);
     int kc = 0;
-    for (; kc + 1 < nk; kc += 2) {
-      wait_vmem();
-      __syncthreads();
-      issue(kc + 1, As1, Bs1);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
-      compute(As0, Bs0);
-      wait_vmem();
-      __syncthreads();
-      if (kc + 2 < nk) issue(kc + 2, As0, Bs0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(As1, Bs1);
+    for (; kc + 4 <= nk; kc += 4) {
+      step(kc, S0, S1, sb3);
+      step(kc + 1, S1, S2, sb0);
+      step(kc + 2, S2, S3, sb1);
+      step(kc + 3, S3, S0, sb2);
     }
-    if (kc < nk) {          // odd number of stages: the last one sits in stage buffer 0
-      wait_vmem();
-      __syncthreads();
-      compute(As0, Bs0);
+    if (kc < nk) {          // K is a multiple of 64, so 2 stages remain here
+      step(kc, S0, S1, sb3);
+      step(kc + 1, S1, S2, sb0);
     }
-    __syncthreads();        // all reads of this tile's buffers done before the next tile's loads
+
+    // next tile of this workgroup; its first stages load during the epilogue
+    Tile nxt;
+    bool more = false;
+    for (L += nslot; L < end; L += nslot)
+      if (decode(L, nxt)) { more = true; break; }
+    lds_barrier();          // every wave is done reading this tile's stage buffers
+    if (more) {
+      set_rows(nxt);
+      prologue();
+    }
 
     // ---- epilogue: lane holds row m, columns 8*grp + 4*(lane>>5) + 0..3 of each 32x32 tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + (lane & 31);
-      if (m >= rows) continue;
-      uint16_t* crow = Cb + static_cast<int64_t>(r0 + m) * N;
+      if (m >= cur.rows) continue;
+      uint16_t* crow = Cb + static_cast<int64_t>(cur.r0 + m) * N;
       if constexpr (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
-            const int n = n0 + wn * 64 + j * 32 + 8 * grp + 4 * (lane >> 5);
+            const int n = cur.n0 + wn * 64 + j * 32 + 8 * grp + 4 * (lane >> 5);
             if (n >= N) continue;
             const f32x16_t& gg = acc[i][j];
             const f32x16_t& uu = acc[i][j + 2];
@@ -248,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
-            const int n = n0 + wn * 128 + j * 32 + 8 * grp + 4 * (lane >> 5);
+            const int n = cur.n0 + wn * 128 + j * 32 + 8 * grp + 4 * (lane >> 5);
             if (n >= N) continue;
             const f32x16_t& cc = acc[i][j];
             const int b = grp * 4;
@@ -256,6 +383,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           }
       }
     }
+    if (!more) break;
+    cur = nxt;
   }
 }
 
