@@ -24,13 +24,15 @@
 // their weights are never read.
 //
 // Per tile: 4 waves in 2x2, each 128x128 outputs = 4x4 MFMA 32x32x16 tiles
-// with fp32 accumulators.  K advances in 32-wide stages through four LDS
-// stage buffers; stages are fetched straight from HBM into LDS
-// (global_load_lds_dwordx4, no staging registers) three stages ahead of the
-// MFMAs, and the first three stages of a workgroup's next tile are issued
-// before the current tile's epilogue, so loads overlap the stores.  LDS rows
-// are 64 bytes whose 16-byte chunks are XOR-swizzled by row quads, which
-// keeps the MFMA operand reads free of bank conflicts.  The MFMA
+// with fp32 accumulators.  K advances in 64-wide stages through two LDS
+// stage buffers; stage k+1 is fetched straight from L2/HBM into LDS
+// (global_load_lds_dwordx4, no staging registers, whole 128-byte lines per
+// row) while stage k is multiplied, each DMA issued between two MFMAs; the
+// first stage of a workgroup's next tile is issued before the current tile's
+// epilogue, so loads overlap the stores.  Operand fragments are
+// double-buffered across the four K16 steps of a stage.  LDS rows are 128
+// bytes whose 16-byte chunks are XOR-swizzled by row pairs, which keeps the
+// MFMA operand reads free of bank conflicts.  The MFMA
 // takes the weight rows as its A operand and the token rows as B, so each
 // lane ends with 4 consecutive output columns of one row: the epilogue
 // applies silu(g)*u in registers and stores 8-byte bf16 quads.
@@ -44,31 +46,25 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
-constexpr int BK = kGemmBK;   // 32
+constexpr int BK = kGemmBK;   // 64
 constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
-constexpr int kLoadsPerStage = 8;   // DMA instructions per lane per stage (4 A + 4 B)
 
-// 16-byte chunk c (0..3) of row r of a 64-byte-row LDS tile sits in slot
-// c ^ ((r >> 2) & 3): the 16 lanes an LDS cycle serves (16 consecutive rows,
+// 16-byte chunk c (0..7) of row r of a 128-byte-row LDS tile sits in slot
+// c ^ ((r >> 1) & 7): the 16 lanes an LDS cycle serves (16 consecutive rows,
 // same chunk) then cover all 64 banks exactly once.
-__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// s_waitcnt vmcnt(8 n) (expcnt / lgkmcnt left at their maxima).  A stage is
-// 8 DMA loads per lane and vector-memory loads of a wave complete in issue
-// order, so waiting until at most 8 n are outstanding guarantees that every
-// stage but the newest n has landed, whatever stores are interleaved.
-__device__ __forceinline__ void wait_stages_outstanding(int n) {
-  if (n >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
-  else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-  else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
-}
+// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): this lane's
+// DMAs (and any older stores) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // One 16-byte-per-lane DMA global -> LDS (global_load_lds_dwordx4): lane i's
 // 16 bytes land at LDS byte address lds + 16 i.  lds must be wave-uniform.
 // Issued from asm so that the compiler's LDS-DMA bookkeeping, which merges
 // stages conservatively at loop back-edges and then drains the whole queue
-// (vmcnt(0)), stays out of the pipeline; completion is tracked explicitly with
-// wait_stages_outstanding().  The instruction writes no VGPR.  M0 is set right
+// (vmcnt(0)), stays out of the pipeline; completion is waited for explicitly
+// with wait_vmem() before the barrier that publishes a stage.  The
+// instruction writes no VGPR.  M0 is set right
 // before it (one wait state apart) and is not used by any other code of these
 // kernels.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
@@ -107,15 +103,10 @@ struct Tile {
 
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
-  // four stage buffers per operand as distinct arrays: the compiler's memory
-  // model then sees that a DMA into one stage never aliases reads of another
-  // and adds no wait of its own
-  // (each holds the A rows then the B rows of one stage; few distinct DMA
-  // targets keep the compiler's per-target tracking exact)
-  __shared__ uint4 S0[(BM + BN) * 4];
-  __shared__ uint4 S1[(BM + BN) * 4];
-  __shared__ uint4 S2[(BM + BN) * 4];
-  __shared__ uint4 S3[(BM + BN) * 4];
+  // two stage buffers as distinct arrays (each holds the A rows then the B
+  // rows of one 64-wide K stage)
+  __shared__ uint4 S0[(BM + BN) * 8];
+  __shared__ uint4 S1[(BM + BN) * 8];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -171,17 +162,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
 
   // Per-lane source rows.  Wave w's j-th DMA of a stage fills LDS rows
-  // 64 j + 16 w .. +15 (16 rows x 4 slots = 64 lanes x 16 bytes); the lane
-  // writes slot lane & 3 of row 64 j + 16 w + lane / 4 and so fetches chunk
-  // (lane & 3) ^ ((row >> 2) & 3) == (lane & 3) ^ ((lane >> 4) & 3).
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int lrow = 16 * wave + (lane >> 2);
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
+  // 32 j + 8 w .. +7 (8 rows x 8 slots = 64 lanes x 16 bytes); the lane
+  // writes slot lane & 7 of row 32 j + 8 w + lane / 8 and so fetches chunk
+  // (lane & 7) ^ ((row >> 1) & 7) == (lane & 7) ^ ((4 w + lane / 16) & 7).
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow = 8 * wave + (lane >> 3);
+  const uint16_t* ap[8];
+  const uint16_t* bp[8];
   auto set_rows = [&](const Tile& t) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ri = lrow + 64 * j;
+    for (int j = 0; j < 8; ++j) {
+      const int ri = lrow + 32 * j;
       const int rr = t.r0 + (ri < t.rows ? ri : t.rows - 1);
       int64_t src = rr;
       if constexpr (GATHER) {
@@ -192,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       int64_t wr;
       if constexpr (SWIGLU) {
         const int n = t.n0 + (ri & 127);
-        wr = (n < a.I ? n : a.I - 1) + (j >= 2 ? a.I : 0);
+        wr = (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
       } else {
         const int n = t.n0 + ri;
         wr = n < N ? n : N - 1;
@@ -205,48 +196,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
   const uint32_t sb0 = __builtin_amdgcn_readfirstlane(lds_addr(S0) + wofs);
   const uint32_t sb1 = __builtin_amdgcn_readfirstlane(lds_addr(S1) + wofs);
-  const uint32_t sb2 = __builtin_amdgcn_readfirstlane(lds_addr(S2) + wofs);
-  const uint32_t sb3 = __builtin_amdgcn_readfirstlane(lds_addr(S3) + wofs);
-  auto issue = [&](int kc, uint32_t sb) {
+  auto dma1 = [&](int kc, uint32_t sb, int t) {   // t < 8: A rows 32t.., else B rows 32(t-8)..
     const int ko = kc * BK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(ap[j] + ko, sb + j * 4 * 64 * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(bp[j] + ko, sb + BM * 4 * 16 + j * 4 * 64 * 16);
-  };
-  auto prologue = [&]() {
-    issue(0, sb0);
-    if (1 < nk) issue(1, sb1);
-    if (2 < nk) issue(2, sb2);
+    if (t < 8) dma16(ap[t] + ko, sb + t * 4 * 64 * 16);
+    else dma16(bp[t - 8] + ko, sb + BM * 8 * 16 + (t - 8) * 4 * 64 * 16);
   };
 
   f32x16_t acc[4][4];
   struct Frag {
     bf16x8_t x[4], w[4];
   };
-  // operand fragments of K16 step s (0, 1) of the stage held in Ss
-  auto load_frags = [&](const uint4* Ss, int s, Frag& F) {
-    const uint4* As = Ss;
-    const uint4* Bs = Ss + BM * 4;
-    const int c = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      F.x[i] = *reinterpret_cast<const bf16x8_t*>(&As[swz(wm * 128 + i * 32 + (lane & 31), c)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int wrow;
-      if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
-      else wrow = wn * 128 + j * 32;
-      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[swz(wrow + (lane & 31), c)]);
-    }
-  };
-  // single-instruction pieces, so that a stage can be written as an
-  // explicit MFMA / memory interleave
   auto mfma1 = [&](const Frag& F, int t) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[j], F.x[i], acc[i][j], 0, 0, 0);
   };
-  auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {   // t < 4: x[t], else w[t-4]
+  // fragment t (< 4: x[t], else w[t-4]) of K16 step s (0..3) of the stage in Ss
+  auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {
     const int c = 2 * s + (lane >> 5);
     if (t < 4) {
       F.x[t] = *reinterpret_cast<const bf16x8_t*>(&Ss[swz(wm * 128 + t * 32 + (lane & 31), c)]);
@@ -255,51 +220,47 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       int wrow;
       if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
       else wrow = wn * 128 + j * 32;
-      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Ss[BM * 4 + swz(wrow + (lane & 31), c)]);
+      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Ss[BM * 8 + swz(wrow + (lane & 31), c)]);
     }
-  };
-  auto dma1 = [&](int kc, uint32_t sb, int t) {                  // t < 4: A row j, else B
-    const int ko = kc * BK;
-    if (t < 4) dma16(ap[t] + ko, sb + t * 4 * 64 * 16);
-    else dma16(bp[t - 4] + ko, sb + BM * 4 * 16 + (t - 4) * 4 * 64 * 16);
   };
 
-  // Stage kc sits in buffer kc % 4.  Iteration kc: this lane waits for its own
-  // DMA of stage kc+1 (stage kc+2 may stay in flight), then the barrier makes
-  // stage kc+1 visible everywhere and retires every read of stage kc-1, so
-  // stage kc+3 can be loaded into that buffer.  Fragments are double-buffered
-  // (step 1 of stage kc loads during step 0, step 0 of stage kc+1 during step
-  // 1) and every LDS read and DMA is issued between two MFMAs, so with one
-  // wave per SIMD the matrix pipe only idles at the barrier.
+  // Stage kc sits in buffer kc & 1.  Iteration kc: this lane's DMA of stage
+  // kc has landed, the barrier makes it visible everywhere and retires every
+  // read of stage kc-1, whose buffer then receives stage kc+1.  The fragments
+  // of K16 step s+1 are read while step s is multiplied, and every LDS read
+  // and DMA is issued between two MFMAs, so with one wave per SIMD the matrix
+  // pipe idles only at the barrier and the first fragment read of a stage.
   Frag Fa, Fb;
-  auto step = [&](int kc, const uint4* Ss, const uint4* Sn, uint32_t sb3) {
-    if (kc + 1 < nk) wait_stages_outstanding(kc + 2 < nk ? 1 : 0);
+  auto stage = [&](int kc, const uint4* Ss, uint32_t sbn) {
+    wait_vmem();
     lds_barrier();
-    const bool dma = kc + 3 < nk;
+    const bool dma = kc + 1 < nk;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 8; ++t) frag1(Ss, 0, Fa, t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {     // step 0; read step 1, DMA half of stage kc+1
       mfma1(Fa, t);
-      frag1(Ss, 1, Fb, t);
+      if (t < 8) frag1(Ss, 1, Fb, t);
+      else if (dma) dma1(kc + 1, sbn, t - 8);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      mfma1(Fa, 8 + t);
-      if (dma) dma1(kc + 3, sb3, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // unconditional: on a tile's last stage the next-stage reads hit a stale
-    // buffer that no DMA targets and are discarded; a branch here would make
-    // the compiler's LDS wait counts conservative
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 16; ++t) {     // step 1; read step 2, DMA the other half
       mfma1(Fb, t);
-      frag1(Sn, 0, Fa, t);
+      if (t < 8) frag1(Ss, 2, Fa, t);
+      else if (dma) dma1(kc + 1, sbn, t);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      mfma1(Fb, 8 + t);
+    for (int t = 0; t < 16; ++t) {     // step 2; read step 3
+      mfma1(Fa, t);
+      if (t < 8) frag1(Ss, 3, Fb, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {     // step 3
+      mfma1(Fb, t);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -311,7 +272,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     if (decode(L, cur)) { have = true; break; }
   if (!have) return;
   set_rows(cur);
-  prologue();
+#pragma unroll
+  for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
 
   while (true) {
 #pragma unroll
@@ -321,23 +283,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // stage 0 of this tile: own DMA done (stages 1, 2 may be in flight), then
-    // visible to every wave; its first fragments are loaded up front
-    wait_stages_outstanding(nk - 1 < 2 ? nk - 1 : 2);
-    lds_barrier();
-    load_frags(S0, 0, Fa);
-
     int kc = 0;
-    for (; kc + 4 <= nk; kc += 4) {
-      step(kc, S0, S1, sb3);
-      step(kc + 1, S1, S2, sb0);
-      step(kc + 2, S2, S3, sb1);
-      step(kc + 3, S3, S0, sb2);
+    for (; kc + 2 <= nk; kc += 2) {
+      stage(kc, S0, sb1);
+      stage(kc + 1, S1, sb0);
     }
-    if (kc < nk) {          // K is a multiple of 64, so 2 stages remain here
-      step(kc, S0, S1, sb3);
-      step(kc + 1, S1, S2, sb0);
-    }
+    if (kc < nk) stage(kc, S0, sb1);   // odd number of stages: the last one is in S0
 
     // next tile of this workgroup; its first stages load during the epilogue
     Tile nxt;
@@ -347,7 +298,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     lds_barrier();          // every wave is done reading this tile's stage buffers
     if (more) {
       set_rows(nxt);
-      prologue();
+#pragma unroll
+      for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
     }
 
     // ---- epilogue: lane holds row m, columns 8*grp + 4*(lane>>5) + 0..3 of each 32x32 tile

@@ -16,7 +16,7 @@ constexpr int kRouteTok = 32;          // tokens per router workgroup
 constexpr int kPermChunk = 1024;       // assignments per permutation workgroup
 constexpr int kGemmBM = 256;           // bf16 grouped GEMM: rows per tile
 constexpr int kGemmBN = 256;           // bf16 grouped GEMM: weight rows per tile
-constexpr int kGemmBK = 32;            // bf16 grouped GEMM: K per LDS stage
+constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage
 constexpr int kF32BM = 64;             // fp32 grouped GEMM tile
 constexpr int kF32BN = 64;
 constexpr int kF32BK = 16;
