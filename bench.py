@@ -240,8 +240,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu:
-        sample = args.cpu_sample or {"tiny_f32": 512, "coarse_bf16": 256, "fine_bf16": 2048,
-                                     "vfine_bf16": 1024, "skewed_bf16": 4096}.get(wl.name, 512)
+        sample = args.cpu_sample or {"tiny_f32": 512, "coarse_bf16": 4096, "fine_bf16": 4096,
+                                     "vfine_bf16": 4096, "skewed_bf16": 8192}.get(wl.name, 1024)
         log(f"[bench] CPU oracle baseline on {sample} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, sample)
     line = json.dumps(rec)
