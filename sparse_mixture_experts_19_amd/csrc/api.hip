@@ -141,12 +141,15 @@ moe_forward_layout forward_layout(int64_t T, int H, int I, int E, int k, int dty
   return L;
 }
 
-// Router scratch carved from `base`.
-void carve_route(char* base, int64_t T, int E, moe::RouteArgs& a) {
+// Router scratch carved from `base`; returns the bytes used.
+size_t carve_route(char* base, int64_t T, int E, moe::RouteArgs& a) {
   Carver c;
   a.flag = reinterpret_cast<int32_t*>(base + c.take(static_cast<size_t>(T) * 4));
   a.meta = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 16));
   a.logits = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * E * 4));
+  a.xnorm2 = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 4));
+  a.wnorm2 = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(E) * 4));
+  return c.o;
 }
 
 int run_route(const void* x, const void* w_router, const float* bias, int64_t T, int H, int E,
@@ -155,7 +158,8 @@ int run_route(const void* x, const void* w_router, const float* bias, int64_t T,
   moe::RouteArgs a{};
   a.x = x; a.w = w_router; a.bias = bias; a.T = T; a.H = H; a.E = E; a.k = k; a.renorm = renorm;
   a.ids = ids; a.weights = weights;
-  carve_route(scratch, T, E, a);
+  if (carve_route(scratch, T, E, a) > moe::route_scratch_bytes(T, E))
+    return fail(MOE_ERR_WORKSPACE, "internal: router scratch layout exceeds its size");
   MOE_HIP(moe::launch_route(a, dtype == MOE_DTYPE_BF16, s));
   return MOE_OK;
 }

@@ -1,0 +1,54 @@
+// CDNA4 (gfx950) device helpers shared by the MFMA kernels of libmoe_mi355x.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 16-byte chunk c (0..7) of row r of a 128-byte-row LDS tile sits in slot
+// c ^ ((r >> 1) & 7): the 16 lanes an LDS cycle serves (16 consecutive rows,
+// same chunk) then cover all 64 banks exactly once.
+__device__ __forceinline__ int swz128(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// One 16-byte-per-lane DMA global -> LDS (global_load_lds_dwordx4): lane i's
+// 16 bytes land at LDS byte address lds + 16 i.  lds must be wave-uniform.
+// Issued from asm so that the compiler's LDS-DMA bookkeeping, which merges
+// stages conservatively at loop back-edges and then drains the whole queue
+// (vmcnt(0)), stays out of software pipelines; completion is waited for
+// explicitly (vmcnt) before the barrier that publishes a stage.  The
+// instruction writes no VGPR.  M0 is set right before it (one wait state
+// apart) and is not used by any other code of these kernels.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)p));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those wait for every outstanding vector-memory op (vmcnt(0)), which would
+// drain the prefetch queue.  LDS reads are complete (lgkmcnt(0)) and DMA
+// stages are waited for explicitly; the memory clobber keeps the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for the few n the pipelines need (expcnt / lgkmcnt at
+// their maxima; vmcnt is bits [3:0] and [15:14]).  Vector-memory loads of a
+// wave complete in issue order, so "at most n outstanding" means every load
+// but the newest n has landed, whatever stores are interleaved.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmcnt6() { __builtin_amdgcn_s_waitcnt(0x0F76); }
+__device__ __forceinline__ void wait_vmcnt12() { __builtin_amdgcn_s_waitcnt(0x0F7C); }
+
+}  // namespace moe

@@ -37,56 +37,17 @@
 // lane ends with 4 consecutive output columns of one row: the epilogue
 // applies silu(g)*u in registers and stores 8-byte bf16 quads.
 #include "moe_internal.h"
+#include "cdna4.h"
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
 constexpr int BK = kGemmBK;   // 64
 constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
 
-// 16-byte chunk c (0..7) of row r of a 128-byte-row LDS tile sits in slot
-// c ^ ((r >> 1) & 7): the 16 lanes an LDS cycle serves (16 consecutive rows,
-// same chunk) then cover all 64 banks exactly once.
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
-
-// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): this lane's
-// DMAs (and any older stores) have completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// One 16-byte-per-lane DMA global -> LDS (global_load_lds_dwordx4): lane i's
-// 16 bytes land at LDS byte address lds + 16 i.  lds must be wave-uniform.
-// Issued from asm so that the compiler's LDS-DMA bookkeeping, which merges
-// stages conservatively at loop back-edges and then drains the whole queue
-// (vmcnt(0)), stays out of the pipeline; completion is waited for explicitly
-// with wait_vmem() before the barrier that publishes a stage.  The
-// instruction writes no VGPR.  M0 is set right
-// before it (one wait state apart) and is not used by any other code of these
-// kernels.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)p));
-}
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those wait for every outstanding vector-memory op (vmcnt(0)), which would
-// drain the prefetch queue.  LDS reads are complete (lgkmcnt(0)) and DMA
-// stages are waited for explicitly; the memory clobber keeps the compiler
-// from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+__device__ __forceinline__ int swz(int r, int c) { return swz128(r, c); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
@@ -232,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // pipe idles only at the barrier and the first fragment read of a stage.
   Frag Fa, Fb;
   auto stage = [&](int kc, const uint4* Ss, uint32_t sbn) {
-    wait_vmem();
+    wait_vmcnt0();
     lds_barrier();
     const bool dma = kc + 1 < nk;
 #pragma unroll

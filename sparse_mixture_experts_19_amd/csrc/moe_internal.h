@@ -47,7 +47,9 @@ struct RouteArgs {
   float* weights;         // [T,k]
   int32_t* flag;          // [T]     1 = needs the float64 re-rank
   float* meta;            // [T,4]   max, sum, delta, unused
-  float* logits;          // [T,E]   fp32 logits of flagged tokens
+  float* logits;          // [T,E]   fp32 logits (bf16 path: of every token)
+  float* xnorm2;          // [T]     ||x_t||^2 (bf16 path)
+  float* wnorm2;          // [E]     ||W_e||^2 (bf16 path)
 };
 size_t route_scratch_bytes(int64_t T, int E);
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);

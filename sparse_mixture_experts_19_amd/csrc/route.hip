@@ -22,34 +22,16 @@
 // products, float64 sums) over the candidate set {e : L_k - L_e <= 2*delta},
 // which provably contains the exact top-k.
 #include "moe_internal.h"
+#include "cdna4.h"
 
 #include <math.h>
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int RT = kRouteTok;   // tokens per workgroup
-constexpr int KC = 64;          // K elements per LDS stage (bf16 path)
 constexpr float kUlp2 = 1.1920928955078125e-07f;   // 2^-23
 constexpr float kSafety = 1.0009765625f;            // 1 + 2^-10
-
-// 16-byte chunk c (0..7) of row r in an LDS tile of 8-chunk rows, XOR-swizzled
-// so that 8 consecutive rows reading the same chunk hit distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
-
-__device__ __forceinline__ float sumsq8_bf16(const uint4& v) {
-  const uint16_t* p = reinterpret_cast<const uint16_t*>(&v);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float f = bf16_to_f32(p[i]);
-    s = fmaf(f, f, s);
-  }
-  return s;
-}
 
 __device__ __forceinline__ float xor_sum8(float v) {   // sum over an 8-lane group
   v += __shfl_xor(v, 1);
@@ -163,126 +145,183 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
 }
 
 // ---------------------------------------------------------------- bf16 path
-// Workgroup: RT tokens x all experts.  MFMA 32x32x16 bf16 with the router
-// weight rows as the A operand (32 experts) and the tokens as B (32 tokens).
-// Waves split experts (WE groups of NTW 32-expert tiles) and the 4 K16 steps
-// of each 64-wide K stage (WK groups).
-template <int NTW, int WK>
-__global__ __launch_bounds__(256) void route_bf16_kernel(RouteArgs a) {
-  constexpr int WE = 4 / WK;
-  constexpr int EP = 32 * NTW * WE;
-  constexpr int WR = EP / 32;          // W rows loaded per thread per stage
-  constexpr int SPW = 4 / WK;          // K16 steps per wave per stage
-  __shared__ uint4 xs[2][RT * 8];
-  __shared__ uint4 ws[2][EP * 8];
-  __shared__ float lg[RT][EP + 1];
-  __shared__ float xsq_s[RT];
-  __shared__ float delta_s[RT];
-  __shared__ unsigned wmax_bits, bmax_bits;
+// Logits: a workgroup owns 128 tokens x 64 experts; wave w multiplies tokens
+// 32w..32w+31 by both 32-expert halves (MFMA 32x32x16, router rows as A,
+// tokens as B).  K moves in 64-wide stages through four LDS buffers, loaded
+// by direct-to-LDS DMA three stages ahead.  Each stage's four MFMAs start
+// from zero and are then added to the running sum (the summation structure
+// the error bound counts).  Squared norms of the token rows and router rows
+// are summed from the very operand fragments the MFMAs consume.
+constexpr int LT = 128;               // tokens per workgroup
+constexpr int LE = 64;                // experts per workgroup
+constexpr int LBK = 64;               // K per stage
+constexpr int LSTAGE = (LT + LE) * 8; // uint4 per stage buffer
 
+__device__ __forceinline__ float sumsq8(const bf16x8_t& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float f = static_cast<float>(v[i]);
+    s = fmaf(f, f, s);
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(256) void route_logits_bf16_kernel(RouteArgs a) {
+  __shared__ uint4 R0[LSTAGE];
+  __shared__ uint4 R1[LSTAGE];
+  __shared__ uint4 R2[LSTAGE];
+  __shared__ uint4 R3[LSTAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int we = wave % WE, wk = wave / WE;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
+  const int e0 = blockIdx.y * LE;
   const int H = a.H, E = a.E;
+  const int nk = H / LBK;
   const uint16_t* X = static_cast<const uint16_t*>(a.x);
   const uint16_t* W = static_cast<const uint16_t*>(a.w);
 
-  if (tid == 0) { wmax_bits = 0u; bmax_bits = 0u; }
-
-  const int lrow = tid >> 3, lc = tid & 7;
-  const int64_t tl = t0 + lrow;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  uint4 xr, wr[WR];
-  float xsq = 0.f, wsq[WR];
+  // DMA rows of this lane (clamped in bounds; clamped rows are never stored)
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow = 8 * wave + (lane >> 3);
+  const uint16_t* xp[4];
+  const uint16_t* wp[2];
 #pragma unroll
-  for (int i = 0; i < WR; ++i) wsq[i] = 0.f;
-
-  auto gload = [&](int ch) {
-    const int64_t ko = static_cast<int64_t>(ch) * KC + lc * 8;
-    xr = (tl < a.T) ? *reinterpret_cast<const uint4*>(X + tl * H + ko) : zero;
+  for (int j = 0; j < 4; ++j) {
+    int64_t t = t0 + lrow + 32 * j;
+    t = t < a.T ? t : a.T - 1;
+    xp[j] = X + t * H + lchunk * 8;
+  }
 #pragma unroll
-    for (int i = 0; i < WR; ++i) {
-      int er = lrow + 32 * i;
-      wr[i] = (er < E) ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(er) * H + ko) : zero;
-    }
+  for (int j = 0; j < 2; ++j) {
+    int e = e0 + lrow + 32 * j;
+    e = e < E ? e : E - 1;
+    wp[j] = W + static_cast<int64_t>(e) * H + lchunk * 8;
+  }
+  const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
+  const uint32_t rb0 = __builtin_amdgcn_readfirstlane(lds_addr(R0) + wofs);
+  const uint32_t rb1 = __builtin_amdgcn_readfirstlane(lds_addr(R1) + wofs);
+  const uint32_t rb2 = __builtin_amdgcn_readfirstlane(lds_addr(R2) + wofs);
+  const uint32_t rb3 = __builtin_amdgcn_readfirstlane(lds_addr(R3) + wofs);
+  auto issue = [&](int kc, uint32_t rb) {
+    const int ko = kc * LBK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(xp[j] + ko, rb + j * 4 * 64 * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(wp[j] + ko, rb + LT * 8 * 16 + j * 4 * 64 * 16);
   };
-  auto stash = [&](int buf) {
-    xsq += sumsq8_bf16(xr);
-    xs[buf][swz(lrow, lc)] = xr;
-#pragma unroll
-    for (int i = 0; i < WR; ++i) {
-      wsq[i] += sumsq8_bf16(wr[i]);
-      ws[buf][swz(lrow + 32 * i, lc)] = wr[i];
-    }
-  };
 
-  const int nch = H / KC;
-  gload(0);
-  stash(0);
-  __syncthreads();
-
-  f32x16_t acc[NTW];
+  f32x16_t acc[2];
 #pragma unroll
-  for (int n = 0; n < NTW; ++n)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  float xsq = 0.f, wsq[2] = {0.f, 0.f};
 
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nch) gload(ch + 1);
-    f32x16_t part[NTW];
+  auto step = [&](int kc, const uint4* Rs, uint32_t rbn) {
+    const int after = nk - 1 - kc;          // stages issued after kc (at most 2)
+    if (after >= 2) wait_vmcnt12();
+    else if (after == 1) wait_vmcnt6();
+    else wait_vmcnt0();
+    lds_barrier();
+    if (kc + 3 < nk) issue(kc + 3, rbn);
+    f32x16_t part[2];
 #pragma unroll
-    for (int n = 0; n < NTW; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[n][r] = 0.f;
 #pragma unroll
-    for (int ss = 0; ss < SPW; ++ss) {
-      const int s = wk * SPW + ss;
+    for (int s = 0; s < 4; ++s) {
       const int c = 2 * s + (lane >> 5);
-      const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(&xs[buf][swz(lane & 31, c)]);
+      const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(&Rs[swz128(wave * 32 + (lane & 31), c)]);
+      xsq += sumsq8(bx);
 #pragma unroll
-      for (int n = 0; n < NTW; ++n) {
-        const int er = (we * NTW + n) * 32 + (lane & 31);
-        const bf16x8_t aw = *reinterpret_cast<const bf16x8_t*>(&ws[buf][swz(er, c)]);
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8_t aw =
+            *reinterpret_cast<const bf16x8_t*>(&Rs[LT * 8 + swz128(n * 32 + (lane & 31), c)]);
+        wsq[n] += sumsq8(aw);
         part[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx, part[n], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) acc[n] += part[n];
-    if (ch + 1 < nch) stash(buf ^ 1);
-    __syncthreads();
-  }
+    for (int n = 0; n < 2; ++n) acc[n] += part[n];
+  };
 
-  // norms
-  xsq = xor_sum8(xsq);
-  if (lc == 0) xsq_s[lrow] = xsq;
-#pragma unroll
-  for (int i = 0; i < WR; ++i) {
-    float w2 = xor_sum8(wsq[i]);
-    if (lc == 0 && lrow + 32 * i < E) atomicMax(&wmax_bits, __float_as_uint(w2));
+  issue(0, rb0);
+  if (1 < nk) issue(1, rb1);
+  if (2 < nk) issue(2, rb2);
+  int kc = 0;
+  for (; kc + 4 <= nk; kc += 4) {
+    step(kc, R0, rb3);
+    step(kc + 1, R1, rb0);
+    step(kc + 2, R2, rb1);
+    step(kc + 3, R3, rb2);
   }
-  if (a.bias && tid < E) atomicMax(&bmax_bits, __float_as_uint(fabsf(a.bias[tid])));
+  if (kc < nk) step(kc, R0, rb3);       // H is a multiple of 64: 0..3 stages remain
+  if (kc + 1 < nk) step(kc + 1, R1, rb0);
+  if (kc + 2 < nk) step(kc + 2, R2, rb1);
 
-  // partial logits -> LDS, K-split waves added in a fixed order
+  // norms: lanes l and l+32 hold the two K halves of the same row
+  xsq += __shfl_xor(xsq, 32);
 #pragma unroll
-  for (int p = 0; p < WK; ++p) {
-    if (wk == p) {
+  for (int n = 0; n < 2; ++n) wsq[n] += __shfl_xor(wsq[n], 32);
+  const int64_t t = t0 + wave * 32 + (lane & 31);
+  if (blockIdx.y == 0 && lane < 32 && t < a.T) a.xnorm2[t] = xsq;
+  if (blockIdx.x == 0 && wave == 0 && lane < 32) {
 #pragma unroll
-      for (int n = 0; n < NTW; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = (we * NTW + n) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int tk = lane & 31;
-          if (p == 0) lg[tk][e] = acc[n][r];
-          else lg[tk][e] += acc[n][r];
-        }
+    for (int n = 0; n < 2; ++n) {
+      const int e = e0 + n * 32 + lane;
+      if (e < E) a.wnorm2[e] = wsq[n];
     }
-    __syncthreads();
   }
+  // logits: lane holds token t and experts 8(r/4) + 4(lane/32) + (r%4) of each half
+  if (t < a.T) {
+    float* row = a.logits + t * E;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = e0 + n * 32 + 8 * g + 4 * (lane >> 5);
+        if ((E & 3) == 0) {
+          if (e < E)
+            *reinterpret_cast<float4*>(row + e) =
+                make_float4(acc[n][4 * g], acc[n][4 * g + 1], acc[n][4 * g + 2], acc[n][4 * g + 3]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (e + q < E) row[e + q] = acc[n][4 * g + q];
+        }
+      }
+  }
+}
 
+// Softmax + top-k + near-tie flag for 32 tokens per workgroup from the fp32
+// logits, with delta from the squared norms (see the file comment).
+template <int EP>
+__global__ __launch_bounds__(256) void route_select_bf16_kernel(RouteArgs a) {
+  __shared__ float lg[RT][EP + 1];
+  __shared__ float delta_s[RT];
+  __shared__ unsigned wmax_bits, bmax_bits;
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  const int E = a.E;
+  if (tid == 0) { wmax_bits = 0u; bmax_bits = 0u; }
+  __syncthreads();
+  if (tid < E) {
+    atomicMax(&wmax_bits, __float_as_uint(a.wnorm2[tid]));
+    if (a.bias) atomicMax(&bmax_bits, __float_as_uint(fabsf(a.bias[tid])));
+  }
+  for (int i = tid; i < RT * E; i += 256) {
+    const int tk = i / E, e = i - tk * E;
+    const int64_t t = t0 + tk;
+    lg[tk][e] = (t < a.T) ? a.logits[t * E + e] : 0.f;
+  }
+  __syncthreads();
   if (tid < RT) {
-    const int depth = 16 * SPW + nch + WK + 1;
-    delta_s[tid] = route_delta(xsq_s[tid], __uint_as_float(wmax_bits), __uint_as_float(bmax_bits), depth);
+    const int64_t t = t0 + tid;
+    const int nch = a.H / LBK;
+    const int depth = 64 + nch + 2;       // 4 MFMAs per stage, stage sums, bias
+    delta_s[tid] = route_delta(t < a.T ? a.xnorm2[t] : 0.f, __uint_as_float(wmax_bits),
+                               __uint_as_float(bmax_bits), depth);
   }
   __syncthreads();
   route_select<EP>(a, t0, lg, delta_s);
@@ -492,10 +531,10 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
   }
 }
 
-template <int NTW, int WK>
-hipError_t launch_bf16(const RouteArgs& a, hipStream_t s) {
+template <int EP>
+hipError_t launch_select_bf16(const RouteArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.T + RT - 1) / RT);
-  hipLaunchKernelGGL((route_bf16_kernel<NTW, WK>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((route_select_bf16_kernel<EP>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -510,16 +549,25 @@ hipError_t launch_f32(const RouteArgs& a, hipStream_t s) {
 
 size_t route_scratch_bytes(int64_t T, int E) {
   return align_up(static_cast<size_t>(T) * 4, 256) + align_up(static_cast<size_t>(T) * 16, 256) +
-         align_up(static_cast<size_t>(T) * E * 4, 256);
+         align_up(static_cast<size_t>(T) * E * 4, 256) + align_up(static_cast<size_t>(T) * 4, 256) +
+         align_up(static_cast<size_t>(E) * 4, 256);
 }
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
+  // every scratch region must have been carved before anything is launched
+  if (!a.x || !a.w || !a.ids || !a.weights || !a.flag || !a.meta || !a.logits ||
+      (bf16 && (!a.xnorm2 || !a.wnorm2)))
+    return hipErrorInvalidValue;
   hipError_t err;
   if (bf16) {
-    if (a.E <= 32) err = launch_bf16<1, 4>(a, s);
-    else if (a.E <= 64) err = launch_bf16<1, 2>(a, s);
-    else if (a.E <= 128) err = launch_bf16<1, 1>(a, s);
-    else err = launch_bf16<2, 1>(a, s);
+    const dim3 grid(static_cast<unsigned>((a.T + LT - 1) / LT), static_cast<unsigned>((a.E + LE - 1) / LE));
+    hipLaunchKernelGGL(route_logits_bf16_kernel, grid, dim3(256), 0, s, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (a.E <= 32) err = launch_select_bf16<32>(a, s);
+    else if (a.E <= 64) err = launch_select_bf16<64>(a, s);
+    else if (a.E <= 128) err = launch_select_bf16<128>(a, s);
+    else err = launch_select_bf16<256>(a, s);
   } else {
     if (a.E <= 32) err = launch_f32<32>(a, s);
     else if (a.E <= 64) err = launch_f32<64>(a, s);
