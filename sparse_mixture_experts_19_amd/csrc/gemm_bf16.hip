@@ -49,13 +49,32 @@ constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
 
 __device__ __forceinline__ int swz(int r, int c) { return swz128(r, c); }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (1 ulp) in place of
+// an IEEE divide
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// four floats -> four bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  const f32x2_t lo = {a, b}, hi = {c, d};
   uint2 o;
-  o.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  o.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+  o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
   return o;
+}
+
+// Read one accumulator element out of its AGPR at this point of the
+// program.  Plain element accesses let the compiler copy all 256
+// accumulators to VGPRs right after the K loop, which overflows the VGPR
+// file; reading them one tile at a time keeps the epilogue small.
+__device__ __forceinline__ float acc_rd(float v) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
 }
 
 struct Tile {
@@ -119,6 +138,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     t.n0 = nt * NOUT;
     if (t.r0 < 0 || t.r0 >= a.M) return false;
     if (t.rows > a.M - t.r0) t.rows = static_cast<int>(a.M - t.r0);
+    // wave-uniform: keep the tile in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.r0 = __builtin_amdgcn_readfirstlane(t.r0);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
     return t.rows > 0;
   };
 
@@ -128,39 +152,63 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // (lane & 7) ^ ((row >> 1) & 7) == (lane & 7) ^ ((4 w + lane / 16) & 7).
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);
-  const uint16_t* ap[8];
-  const uint16_t* bp[8];
+  // Row of A for DMA j of the current tile: gathered rows are looked up once
+  // per tile (32-bit indices); all other rows follow from the tile scalars.
+  Tile dt;                       // tile whose rows the DMAs currently fetch
+  uint32_t arow[GATHER ? 8 : 1];
   auto set_rows = [&](const Tile& t) {
+    dt = t;
+    if constexpr (GATHER) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int ri = lrow + 32 * j;
-      const int rr = t.r0 + (ri < t.rows ? ri : t.rows - 1);
-      int64_t src = rr;
-      if constexpr (GATHER) {
-        src = a.gather[rr] / a.gather_div;
+      for (int j = 0; j < 8; ++j) {
+        const int ri = lrow + 32 * j;
+        const int rr = t.r0 + (ri < t.rows ? ri : t.rows - 1);
+        int64_t src = a.gather[rr] / a.gather_div;
         src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
+        arow[j] = static_cast<uint32_t>(src);
       }
-      ap[j] = Ab + src * K + lchunk * 8;
-      int64_t wr;
-      if constexpr (SWIGLU) {
-        const int n = t.n0 + (ri & 127);
-        wr = (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
-      } else {
-        const int n = t.n0 + ri;
-        wr = n < N ? n : N - 1;
-      }
-      bp[j] = Bb + static_cast<int64_t>(t.e) * a.b_stride + wr * K + lchunk * 8;
     }
   };
+  // The per-DMA row arithmetic is recomputed at each use (a few VALU ops
+  // between MFMAs) rather than kept live across the K loop: lrow is made
+  // opaque to the optimiser so that it cannot hoist 16 64-bit addresses.
+  auto opaque_lrow = [&]() {
+    int v = lrow;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto a_row = [&](int j) -> uint64_t {
+    if constexpr (GATHER) {
+      uint32_t v = arow[j];
+      asm volatile("" : "+v"(v));
+      return v;
+    } else {
+      const int ri = opaque_lrow() + 32 * j;
+      return static_cast<uint64_t>(dt.r0 + (ri < dt.rows ? ri : dt.rows - 1));
+    }
+  };
+  auto b_row = [&](int j) -> uint64_t {     // row of the stacked weights [E * rows_per_expert, K]
+    const int ri = opaque_lrow() + 32 * j;
+    if constexpr (SWIGLU) {
+      const int n = dt.n0 + (ri & 127);
+      return static_cast<uint64_t>(dt.e) * (2 * a.I) + (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
+    } else {
+      const int n = dt.n0 + ri;
+      return static_cast<uint64_t>(dt.e) * N + (n < N ? n : N - 1);
+    }
+  };
+  const uint64_t rowbytes = static_cast<uint64_t>(K) * 2;
+  const char* Abytes = reinterpret_cast<const char*>(Ab) + lchunk * 16;
+  const char* Bbytes = reinterpret_cast<const char*>(Bb) + lchunk * 16;
 
   // LDS byte address of stage buffer b for this wave's first DMA
   const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
   const uint32_t sb0 = __builtin_amdgcn_readfirstlane(lds_addr(S0) + wofs);
   const uint32_t sb1 = __builtin_amdgcn_readfirstlane(lds_addr(S1) + wofs);
   auto dma1 = [&](int kc, uint32_t sb, int t) {   // t < 8: A rows 32t.., else B rows 32(t-8)..
-    const int ko = kc * BK;
-    if (t < 8) dma16(ap[t] + ko, sb + t * 4 * 64 * 16);
-    else dma16(bp[t - 8] + ko, sb + BM * 8 * 16 + (t - 8) * 4 * 64 * 16);
+    const uint64_t ko = static_cast<uint64_t>(kc) * BK * 2;
+    if (t < 8) dma16(Abytes + a_row(t) * rowbytes + ko, sb + t * 4 * 64 * 16);
+    else dma16(Bbytes + b_row(t - 8) * rowbytes + ko, sb + BM * 8 * 16 + (t - 8) * 4 * 64 * 16);
   };
 
   f32x16_t acc[4][4];
@@ -171,17 +219,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[j], F.x[i], acc[i][j], 0, 0, 0);
   };
+  // Fragment rows are (multiple of 32) + lane % 32, so their swizzle term
+  // ((row >> 1) & 7) is the same lane constant sl for every fragment: one
+  // byte offset per K16 step and operand, with the row differences as
+  // immediates.  xo[s] / wo[s]: offsets of the first x / w fragment row.
+  const int sl = ((lane & 31) >> 1) & 7;
+  uint32_t xo[4], wo[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int slotv = (2 * st + (lane >> 5)) ^ sl;
+    xo[st] = static_cast<uint32_t>(((wm * 128 + (lane & 31)) * 8 + slotv) * 16);
+    wo[st] = static_cast<uint32_t>((BM * 8 + ((SWIGLU ? wn * 64 : wn * 128) + (lane & 31)) * 8 + slotv) * 16);
+  }
   // fragment t (< 4: x[t], else w[t-4]) of K16 step s (0..3) of the stage in Ss
   auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {
-    const int c = 2 * s + (lane >> 5);
+    const char* base = reinterpret_cast<const char*>(Ss);
     if (t < 4) {
-      F.x[t] = *reinterpret_cast<const bf16x8_t*>(&Ss[swz(wm * 128 + t * 32 + (lane & 31), c)]);
+      F.x[t] = *reinterpret_cast<const bf16x8_t*>(base + xo[s] + t * 32 * 128);
     } else {
       const int j = t - 4;
-      int wrow;
-      if constexpr (SWIGLU) wrow = (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
-      else wrow = wn * 128 + j * 32;
-      F.w[j] = *reinterpret_cast<const bf16x8_t*>(&Ss[BM * 8 + swz(wrow + (lane & 31), c)]);
+      const int rowoff = SWIGLU ? ((j < 2) ? j * 32 : 128 + (j - 2) * 32) : j * 32;
+      F.w[j] = *reinterpret_cast<const bf16x8_t*>(base + wo[s] + rowoff * 128);
     }
   };
 
@@ -263,37 +321,74 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
     }
 
-    // ---- epilogue: lane holds row m, columns 8*grp + 4*(lane>>5) + 0..3 of each 32x32 tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 128 + i * 32 + (lane & 31);
-      if (m >= cur.rows) continue;
-      uint16_t* crow = Cb + static_cast<int64_t>(cur.r0 + m) * N;
+    // ---- epilogue.  The MFMA result leaves each lane with 4 consecutive
+    // columns of one row per 32x32 tile (row i*32 + lane%32, columns
+    // 8 g + 4 (lane/32) + 0..3).  Each wave stages its outputs as bf16 in its
+    // own 16 KB of stage buffer S1 (free here: the next tile's first stage
+    // goes to S0, and S1 is written again only after the next barrier) and
+    // writes them back row-contiguously, 16 bytes per lane, so every store
+    // instruction covers whole 128-byte lines.
+    {
+      uint8_t* stg = reinterpret_cast<uint8_t*>(S1) + wave * 16384;
       if constexpr (SWIGLU) {
+        // 128 rows x 64 h-columns, 128-byte rows, chunk c of row r in slot c ^ ((r>>1)&7)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const int n = cur.n0 + wn * 64 + j * 32 + 8 * grp + 4 * (lane >> 5);
-            if (n >= N) continue;
-            const f32x16_t& gg = acc[i][j];
-            const f32x16_t& uu = acc[i][j + 2];
-            const int b = grp * 4;
-            *reinterpret_cast<uint2*>(crow + n) =
-                pack4_bf16(silu_f(gg[b]) * uu[b], silu_f(gg[b + 1]) * uu[b + 1],
-                           silu_f(gg[b + 2]) * uu[b + 2], silu_f(gg[b + 3]) * uu[b + 3]);
-          }
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+              const int r = i * 32 + (lane & 31);
+              const int c4 = j * 8 + 2 * grp + (lane >> 5);      // 4-column group 0..15
+              const f32x16_t& gg = acc[i][j];
+              const f32x16_t& uu = acc[i][j + 2];
+              const int b = grp * 4;
+              float v[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] = silu_f(acc_rd(gg[b + u])) * acc_rd(uu[b + u]);
+              *reinterpret_cast<uint2*>(stg + r * 128 + (((c4 >> 1) ^ ((r >> 1) & 7)) << 4) + (c4 & 1) * 8) =
+                  pack4_bf16(v[0], v[1], v[2], v[3]);
+              __builtin_amdgcn_sched_barrier(0);   // bounds the registers in flight
+            }
+        const int ncol = cur.n0 + wn * 64;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int idx = q * 64 + lane;
+          const int r = idx >> 3, c = idx & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+          const int m = wm * 128 + r;
+          if (m < cur.rows && ncol < N)
+            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(cur.r0 + m) * N + ncol + c * 8) = v;
+        }
       } else {
+        // two passes of 64 rows x 128 columns, 256-byte rows, chunk c of row r in slot c ^ (r&15)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int p = 0; p < 2; ++p) {
 #pragma unroll
-          for (int grp = 0; grp < 4; ++grp) {
-            const int n = cur.n0 + wn * 128 + j * 32 + 8 * grp + 4 * (lane >> 5);
-            if (n >= N) continue;
-            const f32x16_t& cc = acc[i][j];
-            const int b = grp * 4;
-            *reinterpret_cast<uint2*>(crow + n) = pack4_bf16(cc[b], cc[b + 1], cc[b + 2], cc[b + 3]);
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int grp = 0; grp < 4; ++grp) {
+                const int r = ii * 32 + (lane & 31);
+                const int c4 = j * 8 + 2 * grp + (lane >> 5);    // 4-column group 0..31
+                const f32x16_t& cc = acc[2 * p + ii][j];
+                const int b = grp * 4;
+                *reinterpret_cast<uint2*>(stg + r * 256 + (((c4 >> 1) ^ (r & 15)) << 4) + (c4 & 1) * 8) =
+                    pack4_bf16(acc_rd(cc[b]), acc_rd(cc[b + 1]), acc_rd(cc[b + 2]), acc_rd(cc[b + 3]));
+                __builtin_amdgcn_sched_barrier(0);
+              }
+          const int ncol = cur.n0 + wn * 128;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx >> 4, c = idx & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+            const int m = wm * 128 + p * 64 + r;
+            if (m < cur.rows && ncol + c * 8 < N)
+              *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(cur.r0 + m) * N + ncol + c * 8) = v;
           }
+        }
       }
     }
     if (!more) break;
