@@ -403,6 +403,12 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = T;
   g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
   g.A = x; g.gather = perm; g.gather_div = k;
+  if (bf16 && !moe::gemm_bf16_gather_fits(T, H)) {
+    // x spans more than 2^32 bytes: gather its rows into the (not yet used)
+    // down-projection output buffer, which has the same [M, H] shape
+    MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, 2, w + L.y, s));
+    g.A = w + L.y; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
+  }
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
   g.C = w + L.h; g.N = I; g.K = H;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));

@@ -29,6 +29,21 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
                : "memory", "m0");
 }
 
+// Same with the address split into a wave-uniform base (SGPR pair) and a
+// 32-bit per-lane byte offset, which needs no vector ALU work per DMA.  The
+// base is pinned to scalar registers (readfirstlane is a plain move when it
+// already is scalar), whatever the compiler's divergence analysis concludes.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uintptr_t>(sbase);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const void* s = reinterpret_cast<const void*>(static_cast<uintptr_t>((hi << 32) | lo));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(s), "s"(lds)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const void*)p));

@@ -24,18 +24,22 @@
 // their weights are never read.
 //
 // Per tile: 4 waves in 2x2, each 128x128 outputs = 4x4 MFMA 32x32x16 tiles
-// with fp32 accumulators.  K advances in 64-wide stages through two LDS
-// stage buffers; stage k+1 is fetched straight from L2/HBM into LDS
-// (global_load_lds_dwordx4, no staging registers, whole 128-byte lines per
-// row) while stage k is multiplied, each DMA issued between two MFMAs; the
-// first stage of a workgroup's next tile is issued before the current tile's
-// epilogue, so loads overlap the stores.  Operand fragments are
-// double-buffered across the four K16 steps of a stage.  LDS rows are 128
-// bytes whose 16-byte chunks are XOR-swizzled by row pairs, which keeps the
-// MFMA operand reads free of bank conflicts.  The MFMA
-// takes the weight rows as its A operand and the token rows as B, so each
-// lane ends with 4 consecutive output columns of one row: the epilogue
-// applies silu(g)*u in registers and stores 8-byte bf16 quads.
+// with fp32 accumulators.  K advances in 64-wide stages (whole 128-byte
+// lines per row) through two 64 KB LDS buffers, fetched straight from
+// L2/HBM into LDS (global_load_lds_dwordx4, no staging registers).  The
+// stages of all of a workgroup's tiles form one sequence: one barrier per
+// stage both publishes stage g+1 and frees stage g's buffer, stage g+2 is
+// fetched while the last K16 step of stage g is multiplied, so a DMA has a
+// whole stage of MFMAs to land in, also across tile boundaries and under
+// the epilogue.  DMAs take a scalar base plus a per-lane 32-bit offset set
+// once per tile, so issuing one costs no vector ALU work.  Operand fragments
+// are double-buffered across the four K16 steps, and the first fragments of
+// a stage are read during the previous one.  LDS rows are 128 bytes whose
+// 16-byte chunks are XOR-swizzled by row pairs, which keeps the MFMA operand
+// reads free of bank conflicts.  The MFMA takes the weight rows as its A
+// operand and the token rows as B, so each lane ends with 4 consecutive
+// output columns of one row: the epilogue applies silu(g)*u in registers,
+// stages bf16 rows in LDS and writes whole 128-byte lines.
 #include "moe_internal.h"
 #include "cdna4.h"
 
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // rows of one 64-wide K stage)
   __shared__ uint4 S0[(BM + BN) * 8];
   __shared__ uint4 S1[(BM + BN) * 8];
+  __shared__ uint4 STG[4 * 256];        // epilogue staging, 4 KB per wave
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -132,74 +137,95 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int gsz = (mte - g * G < G) ? mte - g * G : G;
     const int nt = rem / gsz;
     const int mt = g * G + rem % gsz;
-    t.e = e;
-    t.r0 = s_off[e] + mt * BM;
-    t.rows = (s_off[e + 1] - t.r0 < BM) ? s_off[e + 1] - t.r0 : BM;
+    // wave-uniform (L is): keep the tile, and every decision taken on it,
+    // in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.r0 = __builtin_amdgcn_readfirstlane(s_off[e] + mt * BM);
+    const int e_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
+    t.rows = (e_end - t.r0 < BM) ? e_end - t.r0 : BM;
     t.n0 = nt * NOUT;
     if (t.r0 < 0 || t.r0 >= a.M) return false;
     if (t.rows > a.M - t.r0) t.rows = static_cast<int>(a.M - t.r0);
-    // wave-uniform: keep the tile in scalar registers
-    t.e = __builtin_amdgcn_readfirstlane(t.e);
-    t.r0 = __builtin_amdgcn_readfirstlane(t.r0);
-    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
-    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
     return t.rows > 0;
   };
 
-  // Per-lane source rows.  Wave w's j-th DMA of a stage fills LDS rows
-  // 32 j + 8 w .. +7 (8 rows x 8 slots = 64 lanes x 16 bytes); the lane
-  // writes slot lane & 7 of row 32 j + 8 w + lane / 8 and so fetches chunk
+  // DMA addressing.  Wave w's DMA t of a stage fills LDS rows 32 (t & 7) +
+  // 8 w .. +7 of the A part (t < 8) or the B part (t >= 8): 8 rows x 8 slots
+  // = 64 lanes x 16 bytes; the lane writes slot lane & 7 of row
+  // 32 (t & 7) + 8 w + lane / 8 and so fetches chunk
   // (lane & 7) ^ ((row >> 1) & 7) == (lane & 7) ^ ((4 w + lane / 16) & 7).
+  // Each DMA is "wave-uniform base (SGPR pair) + 32-bit lane offset": the
+  // bases of a tile are set once and move by the stage's K offset; the lane
+  // offsets (row within the tile, clamped for tails, times the row pitch,
+  // plus the chunk) are computed once per tile, so issuing a DMA costs no
+  // vector ALU work.  Gathered A rows are looked up when the DMA cursor
+  // enters a tile and converted (permutation entry / k, clamped) at the
+  // first issue after the next barrier, when the loads are known to be done.
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);
-  // Row of A for DMA j of the current tile: gathered rows are looked up once
-  // per tile (32-bit indices); all other rows follow from the tile scalars.
-  Tile dt;                       // tile whose rows the DMAs currently fetch
-  uint32_t arow[GATHER ? 8 : 1];
+  const uint64_t rowbytes = static_cast<uint64_t>(K) * 2;
+  const uint32_t rb32 = static_cast<uint32_t>(rowbytes);
+  const char* Ach = reinterpret_cast<const char*>(Ab);
+  const char* Bch = reinterpret_cast<const char*>(Bb);
+  uint32_t voff[16];
+  const char* dA;                 // A base of the DMA tile (stage 0)
+  const char* dB0;                // B base (swiglu: gate rows)
+  const char* dB1;                // swiglu: up rows
+  int32_t graw[GATHER ? 8 : 1];   // raw permutation entries of the gathered rows
+  bool gpend = false;
   auto set_rows = [&](const Tile& t) {
-    dt = t;
     if constexpr (GATHER) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ri = lrow + 32 * j;
-        const int rr = t.r0 + (ri < t.rows ? ri : t.rows - 1);
-        int64_t src = a.gather[rr] / a.gather_div;
-        src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
-        arow[j] = static_cast<uint32_t>(src);
+        graw[j] = a.gather[t.r0 + (ri < t.rows ? ri : t.rows - 1)];
+      }
+      gpend = true;
+      dA = Ach;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ri = lrow + 32 * j;
+        voff[j] = static_cast<uint32_t>(ri < t.rows ? ri : t.rows - 1) * rb32 + lchunk * 16;
+      }
+      dA = Ach + static_cast<uint64_t>(t.r0) * rowbytes;
+    }
+    if constexpr (SWIGLU) {
+      const int nb = a.I - t.n0;          // rows of each half left from n0
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int rr = (lrow + 32 * j) & 127;
+        voff[8 + j] = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * rb32 + lchunk * 16;
+      }
+      dB0 = Bch + (static_cast<uint64_t>(t.e) * (2 * a.I) + t.n0) * rowbytes;
+      dB1 = dB0 + static_cast<uint64_t>(a.I) * rowbytes;
+    } else {
+      const int nb = N - t.n0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int rr = lrow + 32 * j;
+        voff[8 + j] = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * rb32 + lchunk * 16;
+      }
+      dB0 = Bch + (static_cast<uint64_t>(t.e) * N + t.n0) * rowbytes;
+      dB1 = dB0;
+    }
+  };
+  // gathered row = entry / k by multiply-high (exact for entries < 2^31),
+  // clamped into A; A spans fewer than 2^32 bytes (checked at launch)
+  auto gconv = [&]() {
+    if constexpr (GATHER) {
+      if (gpend) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t v = static_cast<uint32_t>(graw[j] < 0 ? 0 : graw[j]);
+          uint32_t q = a.gather_magic ? (__umulhi(v, a.gather_magic) >> a.gather_shift) : (v >> a.gather_shift);
+          q = q < static_cast<uint32_t>(a.a_rows) ? q : static_cast<uint32_t>(a.a_rows - 1);
+          voff[j] = q * rb32 + lchunk * 16;
+        }
+        gpend = false;
       }
     }
   };
-  // The per-DMA row arithmetic is recomputed at each use (a few VALU ops
-  // between MFMAs) rather than kept live across the K loop: lrow is made
-  // opaque to the optimiser so that it cannot hoist 16 64-bit addresses.
-  auto opaque_lrow = [&]() {
-    int v = lrow;
-    asm volatile("" : "+v"(v));
-    return v;
-  };
-  auto a_row = [&](int j) -> uint64_t {
-    if constexpr (GATHER) {
-      uint32_t v = arow[j];
-      asm volatile("" : "+v"(v));
-      return v;
-    } else {
-      const int ri = opaque_lrow() + 32 * j;
-      return static_cast<uint64_t>(dt.r0 + (ri < dt.rows ? ri : dt.rows - 1));
-    }
-  };
-  auto b_row = [&](int j) -> uint64_t {     // row of the stacked weights [E * rows_per_expert, K]
-    const int ri = opaque_lrow() + 32 * j;
-    if constexpr (SWIGLU) {
-      const int n = dt.n0 + (ri & 127);
-      return static_cast<uint64_t>(dt.e) * (2 * a.I) + (n < a.I ? n : a.I - 1) + (j >= 4 ? a.I : 0);
-    } else {
-      const int n = dt.n0 + ri;
-      return static_cast<uint64_t>(dt.e) * N + (n < N ? n : N - 1);
-    }
-  };
-  const uint64_t rowbytes = static_cast<uint64_t>(K) * 2;
-  const char* Abytes = reinterpret_cast<const char*>(Ab) + lchunk * 16;
-  const char* Bbytes = reinterpret_cast<const char*>(Bb) + lchunk * 16;
 
   // LDS byte address of stage buffer b for this wave's first DMA
   const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
@@ -207,8 +233,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const uint32_t sb1 = __builtin_amdgcn_readfirstlane(lds_addr(S1) + wofs);
   auto dma1 = [&](int kc, uint32_t sb, int t) {   // t < 8: A rows 32t.., else B rows 32(t-8)..
     const uint64_t ko = static_cast<uint64_t>(kc) * BK * 2;
-    if (t < 8) dma16(Abytes + a_row(t) * rowbytes + ko, sb + t * 4 * 64 * 16);
-    else dma16(Bbytes + b_row(t - 8) * rowbytes + ko, sb + BM * 8 * 16 + (t - 8) * 4 * 64 * 16);
+    const char* base = t < 8 ? dA : ((SWIGLU && t >= 12) ? dB1 : dB0);
+    dma16s(base + ko, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
   };
 
   f32x16_t acc[4][4];
@@ -243,156 +269,175 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  // Stage kc sits in buffer kc & 1.  Iteration kc: this lane's DMA of stage
-  // kc has landed, the barrier makes it visible everywhere and retires every
-  // read of stage kc-1, whose buffer then receives stage kc+1.  The fragments
-  // of K16 step s+1 are read while step s is multiplied, and every LDS read
-  // and DMA is issued between two MFMAs, so with one wave per SIMD the matrix
-  // pipe idles only at the barrier and the first fragment read of a stage.
-  Frag Fa, Fb;
-  auto stage = [&](int kc, const uint4* Ss, uint32_t sbn) {
-    wait_vmcnt0();
-    lds_barrier();
-    const bool dma = kc + 1 < nk;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) frag1(Ss, 0, Fa, t);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 0; read step 1, DMA half of stage kc+1
-      mfma1(Fa, t);
-      if (t < 8) frag1(Ss, 1, Fb, t);
-      else if (dma) dma1(kc + 1, sbn, t - 8);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 1; read step 2, DMA the other half
-      mfma1(Fb, t);
-      if (t < 8) frag1(Ss, 2, Fa, t);
-      else if (dma) dma1(kc + 1, sbn, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 2; read step 3
-      mfma1(Fa, t);
-      if (t < 8) frag1(Ss, 3, Fb, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 3
-      mfma1(Fb, t);
-      __builtin_amdgcn_sched_barrier(0);
+  // ---- pipeline.  The stages of all tiles of this workgroup form one
+  // sequence g = 0, 1, ...; stage g sits in buffer g & 1.  Per stage: K16
+  // steps 0..2 are multiplied while the fragments of steps 1..3 are read;
+  // then one barrier, reached after this lane's DMAs of stage g+1 landed and
+  // its reads of stage g completed, both publishes stage g+1 and frees
+  // buffer g & 1.  Step 3 is multiplied while stage g+2 is fetched into that
+  // buffer and the step-0 fragments of stage g+1 are read, so every DMA has
+  // a whole stage of MFMAs to land in and no stage starts with an LDS wait.
+  // The last stage of a tile fetches nothing during step 3: its buffer stages
+  // the tile's outputs, and stage g+2 is fetched right after the epilogue.
+  // The DMA cursor (dkc and the bases above) runs up to two stages ahead of the MFMAs and
+  // decodes tiles on its own; gathered rows of a new tile are loaded one
+  // barrier before their first use.
+  auto next_tile = [&](int L, Tile& t) -> int {
+    for (; L < end; L += nslot)
+      if (decode(L, t)) return L;
+    return end;
+  };
+  Tile ct;                                   // tile whose outputs the MFMAs compute
+  int cL = next_tile(begin + slot, ct);
+  if (cL >= end) return;
+  int dL = cL, dkc = 0;
+  bool dlive = true;
+  set_rows(ct);
+  auto dma_advance = [&]() {
+    if (++dkc == nk) {
+      dkc = 0;
+      Tile t;
+      dL = next_tile(dL + nslot, t);
+      if (dL < end) set_rows(t);
+      else dlive = false;
     }
   };
 
-  Tile cur;
-  int L = begin + slot;
-  bool have = false;
-  for (; L < end; L += nslot)
-    if (decode(L, cur)) { have = true; break; }
-  if (!have) return;
-  set_rows(cur);
+  int ckc = 0;      // K stage of the compute tile being multiplied
+  gconv();
 #pragma unroll
   for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
+  dma_advance();
+  if (dlive) {
+    gconv();
+#pragma unroll
+    for (int t = 0; t < 16; ++t) dma1(dkc, sb1, t);
+    dma_advance();
+  }
+  wait_vmcnt0();
+  lds_barrier();
 
-  while (true) {
+  Frag Fa, Fb;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) frag1(S0, 0, Fa, t);
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero_acc();
 
-    int kc = 0;
-    for (; kc + 2 <= nk; kc += 2) {
-      stage(kc, S0, sb1);
-      stage(kc + 1, S1, sb0);
-    }
-    if (kc < nk) stage(kc, S0, sb1);   // odd number of stages: the last one is in S0
-
-    // next tile of this workgroup; its first stages load during the epilogue
-    Tile nxt;
-    bool more = false;
-    for (L += nslot; L < end; L += nslot)
-      if (decode(L, nxt)) { more = true; break; }
-    lds_barrier();          // every wave is done reading this tile's stage buffers
-    if (more) {
-      set_rows(nxt);
+  // Multiply the stage in buffer par (the other buffer holds the next stage).
+  // Returns whether it was the last stage of its tile.
+  auto stage = [&](int par) -> bool {
+    const uint4* Sc = par ? S1 : S0;
+    const uint4* Sn = par ? S0 : S1;
+    const uint32_t sbc = par ? sb1 : sb0;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
+    for (int t = 0; t < 16; ++t) {     // step 0; read step 1
+      mfma1(Fa, t);
+      if (t < 8) frag1(Sc, 1, Fb, t);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {     // step 1; read step 2
+      mfma1(Fb, t);
+      if (t < 8) frag1(Sc, 2, Fa, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {     // step 2; read step 3
+      mfma1(Fa, t);
+      if (t < 8) frag1(Sc, 3, Fb, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt0();                     // stage g+1 (the only DMAs in flight) landed
+    lds_barrier();                     // ... everywhere, and stage g is no longer read
+    const bool last = ckc == nk - 1;
+    const bool dnow = dlive;
+    if (dnow) gconv();
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch g+2
+      mfma1(Fb, t);
+      if (t < 8) frag1(Sn, 0, Fa, t);  // stale but harmless when g+1 does not exist
+      if (dnow) dma1(dkc, sbc, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (dnow) dma_advance();
+    ckc = last ? 0 : ckc + 1;
+    return last;
+  };
 
-    // ---- epilogue.  The MFMA result leaves each lane with 4 consecutive
-    // columns of one row per 32x32 tile (row i*32 + lane%32, columns
-    // 8 g + 4 (lane/32) + 0..3).  Each wave stages its outputs as bf16 in its
-    // own 16 KB of stage buffer S1 (free here: the next tile's first stage
-    // goes to S0, and S1 is written again only after the next barrier) and
-    // writes them back row-contiguously, 16 bytes per lane, so every store
-    // instruction covers whole 128-byte lines.
+  int par = 0;      // buffer of the stage being multiplied
+  while (true) {
+    bool fin;
+    do {
+      fin = stage(par);
+      par ^= 1;
+    } while (!fin);
+    // MFMA results are read by VALU instructions below: leave the wait
+    // states the last MFMA needs before its accumulators are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // ---- epilogue (the next stages are in flight meanwhile).  The MFMA
+    // result leaves each lane with 4 consecutive columns of one row per 32x32
+    // tile (row i*32 + lane%32, columns 8 g + 4 (lane/32) + 0..3).  A wave
+    // writes its 128 x 64 (swiglu) or 128 x 128 (down) outputs in passes of
+    // 32 rows x 64 columns: the pass is staged as bf16 in the wave's own 4 KB
+    // of LDS (128-byte rows, chunk c of row r in slot c ^ ((r >> 1) & 7)) and
+    // read back row-contiguously, so each store instruction writes whole
+    // 128-byte lines.
     {
-      uint8_t* stg = reinterpret_cast<uint8_t*>(S1) + wave * 16384;
-      if constexpr (SWIGLU) {
-        // 128 rows x 64 h-columns, 128-byte rows, chunk c of row r in slot c ^ ((r>>1)&7)
+      uint8_t* stg = reinterpret_cast<uint8_t*>(STG) + wave * 4096;
+      auto write_back = [&](int row0, int col0) {
+        const int r = lane >> 3, c = lane & 7;    // chunk q*64 + lane: row q*8 + r
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int q = 0; q < 4; ++q) {
+          const int rr = q * 8 + r;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4));
+          const int m = row0 + rr;
+          if (m < ct.rows && col0 < N)
+            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(ct.r0 + m) * N + col0 + c * 8) = v;
+        }
+      };
+      const int r = lane & 31;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int h = 0; h < (SWIGLU ? 1 : 2); ++h) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-              const int r = i * 32 + (lane & 31);
-              const int c4 = j * 8 + 2 * grp + (lane >> 5);      // 4-column group 0..15
-              const f32x16_t& gg = acc[i][j];
-              const f32x16_t& uu = acc[i][j + 2];
+              const int c4 = jj * 8 + 2 * grp + (lane >> 5);     // 4-column group 0..15
               const int b = grp * 4;
               float v[4];
+              if constexpr (SWIGLU) {
+                const f32x16_t& gg = acc[i][jj];
+                const f32x16_t& uu = acc[i][jj + 2];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) v[u] = silu_f(acc_rd(gg[b + u])) * acc_rd(uu[b + u]);
+                for (int u = 0; u < 4; ++u) v[u] = silu_f(acc_rd(gg[b + u])) * acc_rd(uu[b + u]);
+              } else {
+                const f32x16_t& cc = acc[i][2 * h + jj];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = acc_rd(cc[b + u]);
+              }
               *reinterpret_cast<uint2*>(stg + r * 128 + (((c4 >> 1) ^ ((r >> 1) & 7)) << 4) + (c4 & 1) * 8) =
                   pack4_bf16(v[0], v[1], v[2], v[3]);
               __builtin_amdgcn_sched_barrier(0);   // bounds the registers in flight
             }
-        const int ncol = cur.n0 + wn * 64;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int idx = q * 64 + lane;
-          const int r = idx >> 3, c = idx & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-          const int m = wm * 128 + r;
-          if (m < cur.rows && ncol < N)
-            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(cur.r0 + m) * N + ncol + c * 8) = v;
-        }
-      } else {
-        // two passes of 64 rows x 128 columns, 256-byte rows, chunk c of row r in slot c ^ (r&15)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int grp = 0; grp < 4; ++grp) {
-                const int r = ii * 32 + (lane & 31);
-                const int c4 = j * 8 + 2 * grp + (lane >> 5);    // 4-column group 0..31
-                const f32x16_t& cc = acc[2 * p + ii][j];
-                const int b = grp * 4;
-                *reinterpret_cast<uint2*>(stg + r * 256 + (((c4 >> 1) ^ (r & 15)) << 4) + (c4 & 1) * 8) =
-                    pack4_bf16(acc_rd(cc[b]), acc_rd(cc[b + 1]), acc_rd(cc[b + 2]), acc_rd(cc[b + 3]));
-                __builtin_amdgcn_sched_barrier(0);
-              }
-          const int ncol = cur.n0 + wn * 128;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int idx = q * 64 + lane;
-            const int r = idx >> 4, c = idx & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
-            const int m = wm * 128 + p * 64 + r;
-            if (m < cur.rows && ncol + c * 8 < N)
-              *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(cur.r0 + m) * N + ncol + c * 8) = v;
-          }
+          write_back(wm * 128 + i * 32, ct.n0 + (SWIGLU ? wn * 64 : wn * 128 + h * 64));
         }
       }
     }
-    if (!more) break;
-    cur = nxt;
+
+    cL = next_tile(cL + nslot, ct);
+    if (cL >= end) break;
+    zero_acc();
   }
 }
 
@@ -404,8 +449,28 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s) {
-  return a.gather ? launch<true, true>(a, s) : launch<true, false>(a, s);
+bool gemm_bf16_gather_fits(int64_t a_rows, int K) {
+  return static_cast<uint64_t>(a_rows) * static_cast<uint64_t>(K) * 2 <= (uint64_t{1} << 32);
+}
+
+hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
+  if (!a0.gather) return launch<true, false>(a0, s);
+  if (a0.gather_div < 1 || !gemm_bf16_gather_fits(a0.a_rows, a0.K)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  // entry / d for entries in [0, 2^31): d = 2^l is a shift; otherwise, with
+  // l = ceil(log2 d) and m = floor(2^(31+l) / d) + 1 < 2^32, the quotient is
+  // floor(entry * m / 2^(31+l)): the excess entry * (m d - 2^(31+l)) / (d 2^(31+l))
+  // is below 2^-l < 1/d, too small to carry past the next integer.
+  const uint32_t d = static_cast<uint32_t>(a.gather_div);
+  if ((d & (d - 1)) == 0) {
+    a.gather_magic = 0;
+    a.gather_shift = __builtin_ctz(d);
+  } else {
+    const int l = 32 - __builtin_clz(d - 1);
+    a.gather_magic = static_cast<uint32_t>((uint64_t{1} << (31 + l)) / d + 1);
+    a.gather_shift = l - 1;
+  }
+  return launch<true, true>(a, s);
 }
 
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s) {

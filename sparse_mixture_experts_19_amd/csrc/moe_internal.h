@@ -79,6 +79,8 @@ struct GemmArgs {
   const void* A;          // rows: [*,K] (x, x_perm or h)
   const int32_t* gather;  // null: row r of A is r; else row r is gather[r] / gather_div
   int gather_div;
+  uint32_t gather_magic;  // bf16 kernels: entry / gather_div == umulhi(entry, magic) >> shift
+  int gather_shift;       // (magic 0: entry >> shift); set by the launcher
   int64_t a_rows;         // rows of A (gathered row indices are clamped to it)
   int64_t M;              // rows of C (tile rows are clamped to it)
   const void* B;          // stacked weights, expert stride b_stride elements
@@ -91,6 +93,8 @@ struct GemmArgs {
   const int32_t* prefix;  // [E+1] tile prefix for this kernel's BM
   int grid;               // persistent workgroups launched
 };
+// The gathered form (gather != null) needs A to span at most 2^32 bytes.
+bool gemm_bf16_gather_fits(int64_t a_rows, int K);
 hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_swiglu(const GemmArgs& a, hipStream_t s);
