@@ -109,7 +109,15 @@ int need_ptr(const void* p, const char* name, size_t align) {
 }
 
 // ------------------------------------------------------------ workspaces
-size_t gemm_scratch(int E) { return moe::align_up(static_cast<size_t>(E + 1) * 4, 256); }
+// Grouped-GEMM scratch: the tile prefix, then (bf16) the fp32 partial sums
+// of K-split tiles.
+size_t gemm_prefix_bytes(int E) { return moe::align_up(static_cast<size_t>(E + 1) * 4, 256); }
+size_t gemm_scratch(int64_t M, int H, int I, int E, int dtype) {
+  size_t b = gemm_prefix_bytes(E);
+  if (dtype == MOE_DTYPE_BF16)
+    b += static_cast<size_t>(moe::gemm_bf16_pieces(M, H, I, E)) * moe::kGemmBM * moe::kGemmBN * 4;
+  return b;
+}
 
 struct Carver {
   size_t o = 0;
@@ -136,7 +144,7 @@ moe_forward_layout forward_layout(int64_t T, int H, int I, int E, int k, int dty
   const size_t shared_sz = moe::route_scratch_bytes(T, E) > moe::permute_scratch_bytes(M, E)
                                ? moe::route_scratch_bytes(T, E)
                                : moe::permute_scratch_bytes(M, E);
-  L.scratch = c.take(gemm_scratch(E) + shared_sz);
+  L.scratch = c.take(gemm_scratch(static_cast<int64_t>(M), H, I, E, dtype) + shared_sz);
   L.total = c.o;
   return L;
 }
@@ -181,6 +189,8 @@ int run_experts(const void* a_ptr, int64_t a_rows, const int32_t* gather, int ga
   moe::GemmArgs g{};
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = a_rows;
   if (bf16) {
+    g.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(prefix) + gemm_prefix_bytes(E));
+    g.max_pieces = moe::gemm_bf16_pieces(M, H, I, E);
     g.grid = cu >= 8 ? cu / 8 * 8 : 8;
   } else {
     g.grid = cu * 2;
@@ -239,7 +249,7 @@ int moe_workspace_size(int32_t entry, int64_t T, int32_t H, int32_t I, int32_t E
       return ok();
     case MOE_ENTRY_GROUPED_GEMM:
       MOE_CHECK(check_sizes(T, H, I, E, 1, dtype, true));
-      *bytes = gemm_scratch(E);
+      *bytes = gemm_scratch(T, H, I, E, dtype);
       return ok();
     case MOE_ENTRY_COMBINE:
       MOE_CHECK(check_sizes(T, H, 64, k, k, dtype, false));
@@ -324,7 +334,7 @@ int moe_grouped_swiglu_gemm(const void* x_perm, const int32_t* expert_offsets, c
   MOE_CHECK(need_ptr(w2, "w2", 16));
   MOE_CHECK(need_ptr(h, "h", 16));
   MOE_CHECK(need_ptr(y, "y", 16));
-  const size_t need = gemm_scratch(E);
+  const size_t need = gemm_scratch(M, H, I, E, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "grouped gemm needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
@@ -384,8 +394,8 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(w + L.inv_perm);
   int32_t* prefix = reinterpret_cast<int32_t*>(w + L.scratch);
-  char* shared = w + L.scratch + gemm_scratch(E);
   const int64_t M = T * k;
+  char* shared = w + L.scratch + gemm_scratch(M, H, I, E, dtype);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto mark = [&](int i) -> int {
     if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
@@ -402,6 +412,10 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   moe::GemmArgs g{};
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = T;
   g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
+  if (bf16) {
+    g.partials = reinterpret_cast<float*>(w + L.scratch + gemm_prefix_bytes(E));
+    g.max_pieces = moe::gemm_bf16_pieces(M, H, I, E);
+  }
   g.A = x; g.gather = perm; g.gather_div = k;
   if (bf16 && !moe::gemm_bf16_gather_fits(T, H)) {
     // x spans more than 2^32 bytes: gather its rows into the (not yet used)

@@ -85,6 +85,67 @@ struct Tile {
   int e, r0, rows, n0;
 };
 
+// Tile L of a grouped GEMM with NT output-column tiles of nout columns ->
+// (expert, first row, rows, first output column).  pre/off: tile prefix and
+// row offsets per expert.  Inside an expert up to kGroupM m-tiles are walked
+// n-tile-major: the ~32 tiles an XCD runs at once cover every m-tile of a
+// weight panel, so a panel streams from HBM once per group instead of once
+// per m-tile.  False for tiles that malformed offsets would place outside
+// [0, M).  L is wave-uniform, and so is the tile: it is kept, with every
+// decision taken on it, in scalar registers.
+__device__ __forceinline__ bool decode_tile(int L, int NT, int nout, int E, const int* pre,
+                                            const int* off, int64_t M, Tile& t) {
+  const int q = L / NT;
+  int lo = 0, hi = E;            // largest e with pre[e] <= q
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= q) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int local = L - pre[e] * NT;
+  const int mte = pre[e + 1] - pre[e];
+  const int G = mte < kGroupM ? mte : kGroupM;
+  const int g = local / (G * NT);
+  const int rem = local - g * G * NT;
+  const int gsz = (mte - g * G < G) ? mte - g * G : G;
+  const int nt = rem / gsz;
+  const int mt = g * G + rem % gsz;
+  t.e = __builtin_amdgcn_readfirstlane(e);
+  t.r0 = __builtin_amdgcn_readfirstlane(off[e] + mt * BM);
+  const int e_end = __builtin_amdgcn_readfirstlane(off[e + 1]);
+  t.rows = (e_end - t.r0 < BM) ? e_end - t.r0 : BM;
+  t.n0 = nt * nout;
+  if (t.r0 < 0 || t.r0 >= M) return false;
+  if (t.rows > M - t.r0) t.rows = static_cast<int>(M - t.r0);
+  return t.rows > 0;
+}
+
+// Work split of a grouped GEMM over G persistent workgroups.  The first
+// `full` tiles (a multiple of G) are computed whole, full / G per workgroup.
+// The remaining rem < G tiles would leave most workgroups idle for a whole
+// tile; when G allows, each is cut along K into `ways` pieces of at least
+// kMinPiece stages (shorter pieces cost more in partial sums than they save)
+// that run on different workgroups and leave fp32 partial sums, which the
+// fixup kernel adds in piece order (deterministic) and finishes with the
+// epilogue.
+constexpr int kMinPiece = 16;
+struct Split {
+  int full, rem, ways;
+};
+__device__ __forceinline__ Split split_work(int total, int G, int nk, int max_pieces) {
+  Split sp;
+  sp.full = total / G * G;
+  sp.rem = total - sp.full;
+  sp.ways = 1;
+  if (sp.rem > 0) {
+    int w = G / sp.rem;
+    w = w < nk / kMinPiece ? w : nk / kMinPiece;
+    w = w < max_pieces / sp.rem ? w : max_pieces / sp.rem;
+    if (w >= 2) sp.ways = w;
+  }
+  return sp;
+}
+
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // two stage buffers as distinct arrays (each holds the A rows then the B
@@ -108,45 +169,52 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int nk = K / BK;
 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int begin = xcd * chunk;
-  const int end = (begin + chunk < total) ? begin + chunk : total;
+  const Split sp = split_work(total, gridDim.x, nk, a.max_pieces);
+  const int nf = sp.full / gridDim.x;          // whole tiles of this workgroup
+  const int xbegin = xcd * (sp.full >> 3);     // its XCD's range of whole tiles
 
   const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
   const uint16_t* Bb = static_cast<const uint16_t*>(a.B);
   uint16_t* Cb = static_cast<uint16_t*>(a.C);
 
-  // tile L -> (expert, first row, rows, first output column); false for
-  // tiles that malformed offsets would place outside [0, M)
-  auto decode = [&](int L, Tile& t) -> bool {
-    const int q = L / NT;
-    int lo = 0, hi = E;            // largest e with s_pre[e] <= q
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pre[mid] <= q) lo = mid; else hi = mid;
+  // Work item i of this workgroup: its whole tiles (XCD-aware walk), then
+  // one remainder tile or one K piece of one.  Returns 0 past the end, 2 for
+  // an item that malformed offsets make empty (skipped), else 1.
+  struct Item {
+    Tile t;
+    int k0, k1, pslot;      // K stages [k0, k1); partial-sum slot or -1
+  };
+  auto item = [&](int i, Item& it) -> int {
+    int L;
+    it.k0 = 0;
+    it.k1 = nk;
+    it.pslot = -1;
+    if (i < nf) {
+      L = xbegin + slot + i * nslot;
+    } else if (i == nf) {
+      const int b = blockIdx.x;
+      if (sp.ways > 1) {
+        if (b >= sp.rem * sp.ways) return 0;
+        L = sp.full + b / sp.ways;
+        const int p = b % sp.ways;
+        it.k0 = p * nk / sp.ways;
+        it.k1 = (p + 1) * nk / sp.ways;
+        it.pslot = b;
+      } else {
+        if (b >= sp.rem) return 0;
+        L = sp.full + b;
+      }
+    } else {
+      return 0;
     }
-    const int e = lo;
-    const int local = L - s_pre[e] * NT;
-    const int mte = s_pre[e + 1] - s_pre[e];
-    // up to kGroupM m-tiles of the expert walked n-tile-major: the ~32 tiles
-    // an XCD runs at once cover every m-tile of a weight panel, so a panel
-    // streams from HBM once per group instead of once per m-tile
-    const int G = mte < kGroupM ? mte : kGroupM;
-    const int g = local / (G * NT);
-    const int rem = local - g * G * NT;
-    const int gsz = (mte - g * G < G) ? mte - g * G : G;
-    const int nt = rem / gsz;
-    const int mt = g * G + rem % gsz;
-    // wave-uniform (L is): keep the tile, and every decision taken on it,
-    // in scalar registers
-    t.e = __builtin_amdgcn_readfirstlane(e);
-    t.r0 = __builtin_amdgcn_readfirstlane(s_off[e] + mt * BM);
-    const int e_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
-    t.rows = (e_end - t.r0 < BM) ? e_end - t.r0 : BM;
-    t.n0 = nt * NOUT;
-    if (t.r0 < 0 || t.r0 >= a.M) return false;
-    if (t.rows > a.M - t.r0) t.rows = static_cast<int>(a.M - t.r0);
-    return t.rows > 0;
+    return decode_tile(L, NT, NOUT, E, s_pre, s_off, a.M, it.t) ? 1 : 2;
+  };
+  auto next_item = [&](int i, Item& it) -> int {   // index of the first item >= i, or -1
+    for (;; ++i) {
+      const int r = item(i, it);
+      if (r == 1) return i;
+      if (r == 0) return -1;
+    }
   };
 
   // DMA addressing.  Wave w's DMA t of a stage fills LDS rows 32 (t & 7) +
@@ -282,31 +350,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // The DMA cursor (dkc and the bases above) runs up to two stages ahead of the MFMAs and
   // decodes tiles on its own; gathered rows of a new tile are loaded one
   // barrier before their first use.
-  auto next_tile = [&](int L, Tile& t) -> int {
-    for (; L < end; L += nslot)
-      if (decode(L, t)) return L;
-    return end;
-  };
-  Tile ct;                                   // tile whose outputs the MFMAs compute
-  int cL = next_tile(begin + slot, ct);
-  if (cL >= end) return;
-  int dL = cL, dkc = 0;
+  Item ci;                                   // item whose outputs the MFMAs compute
+  int cidx = next_item(0, ci);
+  if (cidx < 0) return;
+  Item di = ci;                              // item the DMAs fetch
+  int didx = cidx, dkc = ci.k0;
   bool dlive = true;
-  set_rows(ct);
+  set_rows(ci.t);
   auto dma_advance = [&]() {
-    if (++dkc == nk) {
-      dkc = 0;
-      Tile t;
-      dL = next_tile(dL + nslot, t);
-      if (dL < end) set_rows(t);
-      else dlive = false;
+    if (++dkc == di.k1) {
+      didx = next_item(didx + 1, di);
+      if (didx >= 0) {
+        dkc = di.k0;
+        set_rows(di.t);
+      } else {
+        dlive = false;
+      }
     }
   };
 
-  int ckc = 0;      // K stage of the compute tile being multiplied
+  int ckc = ci.k0;  // K stage being multiplied
   gconv();
 #pragma unroll
-  for (int t = 0; t < 16; ++t) dma1(0, sb0, t);
+  for (int t = 0; t < 16; ++t) dma1(dkc, sb0, t);
   dma_advance();
   if (dlive) {
     gconv();
@@ -357,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
     wait_vmcnt0();                     // stage g+1 (the only DMAs in flight) landed
     lds_barrier();                     // ... everywhere, and stage g is no longer read
-    const bool last = ckc == nk - 1;
+    const bool last = ckc == ci.k1 - 1;
     const bool dnow = dlive;
     if (dnow) gconv();
 #pragma unroll
@@ -368,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (dnow) dma_advance();
-    ckc = last ? 0 : ckc + 1;
+    if (!last) ++ckc;
     return last;
   };
 
@@ -383,6 +449,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     // states the last MFMA needs before its accumulators are read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
+    if (ci.pslot >= 0) {
+      // ---- K piece: raw fp32 sums into its partial slot, [256 token rows]
+      // x [256 weight rows of the tile] (swiglu: 128 gate rows, then 128 up)
+      float* P = a.partials + static_cast<int64_t>(ci.pslot) * (BM * BN);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int row = wm * 128 + i * 32 + (lane & 31);
+            const int wrow = (SWIGLU ? (j < 2 ? wn * 64 + 32 * j : 128 + wn * 64 + 32 * (j - 2))
+                                     : wn * 128 + 32 * j) +
+                             8 * grp + 4 * (lane >> 5);
+            float4 v;
+            v.x = acc_rd(acc[i][j][4 * grp]);
+            v.y = acc_rd(acc[i][j][4 * grp + 1]);
+            v.z = acc_rd(acc[i][j][4 * grp + 2]);
+            v.w = acc_rd(acc[i][j][4 * grp + 3]);
+            *reinterpret_cast<float4*>(P + row * BN + wrow) = v;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+    } else
     // ---- epilogue (the next stages are in flight meanwhile).  The MFMA
     // result leaves each lane with 4 consecutive columns of one row per 32x32
     // tile (row i*32 + lane%32, columns 8 g + 4 (lane/32) + 0..3).  A wave
@@ -400,8 +489,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           const int rr = q * 8 + r;
           const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4));
           const int m = row0 + rr;
-          if (m < ct.rows && col0 < N)
-            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(ct.r0 + m) * N + col0 + c * 8) = v;
+          if (m < ci.t.rows && col0 < N)
+            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(ci.t.r0 + m) * N + col0 + c * 8) = v;
         }
       };
       const int r = lane & 31;
@@ -430,24 +519,89 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
                   pack4_bf16(v[0], v[1], v[2], v[3]);
               __builtin_amdgcn_sched_barrier(0);   // bounds the registers in flight
             }
-          write_back(wm * 128 + i * 32, ct.n0 + (SWIGLU ? wn * 64 : wn * 128 + h * 64));
+          write_back(wm * 128 + i * 32, ci.t.n0 + (SWIGLU ? wn * 64 : wn * 128 + h * 64));
         }
       }
     }
 
-    cL = next_tile(cL + nslot, ct);
-    if (cL >= end) break;
+    cidx = next_item(cidx + 1, ci);
+    if (cidx < 0) break;
+    ckc = ci.k0;
     zero_acc();
+  }
+}
+
+// Finish the K-split remainder tiles: sum each tile's partial slots in piece
+// order, apply the epilogue (swiglu: silu(gate) * up) and store bf16 rows.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_bf16_fixup_kernel(GemmArgs a) {
+  constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+  const int NT = (a.N + NOUT - 1) / NOUT;
+  const int total = a.prefix[a.E] * NT;
+  const Split sp = split_work(total, a.grid, a.K / BK, a.max_pieces);
+  if (sp.ways < 2) return;
+  constexpr int CPR = NOUT / 8;                  // 8-column groups per output row
+  const int64_t work = static_cast<int64_t>(sp.rem) * BM * CPR;
+  uint16_t* C = static_cast<uint16_t*>(a.C);
+  for (int64_t idx = blockIdx.x * 256LL + threadIdx.x; idx < work; idx += gridDim.x * 256LL) {
+    const int q = static_cast<int>(idx / (BM * CPR));
+    const int row = static_cast<int>(idx / CPR % BM);
+    const int c8 = static_cast<int>(idx % CPR);
+    Tile t;
+    if (!decode_tile(sp.full + q, NT, NOUT, a.E, a.prefix, a.offsets, a.M, t)) continue;
+    if (row >= t.rows || t.n0 + c8 * 8 >= a.N) continue;
+    float v[8], up[8];             // swiglu: v = gate sums; down: the outputs
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = up[u] = 0.f;
+    for (int p = 0; p < sp.ways; ++p) {
+      const float* P = a.partials + static_cast<int64_t>(q * sp.ways + p) * (BM * BN) + row * BN;
+      const float4 x0 = *reinterpret_cast<const float4*>(P + c8 * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(P + c8 * 8 + 4);
+      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+      if constexpr (SWIGLU) {
+        const float4 u0 = *reinterpret_cast<const float4*>(P + 128 + c8 * 8);
+        const float4 u1 = *reinterpret_cast<const float4*>(P + 128 + c8 * 8 + 4);
+        up[0] += u0.x; up[1] += u0.y; up[2] += u0.z; up[3] += u0.w;
+        up[4] += u1.x; up[5] += u1.y; up[6] += u1.z; up[7] += u1.w;
+      }
+    }
+    if constexpr (SWIGLU) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
+    }
+    uint4 o;
+    const uint2 lo = pack4_bf16(v[0], v[1], v[2], v[3]);
+    const uint2 hi = pack4_bf16(v[4], v[5], v[6], v[7]);
+    o.x = lo.x; o.y = lo.y; o.z = hi.x; o.w = hi.y;
+    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(t.r0 + row) * a.N + t.n0 + c8 * 8) = o;
   }
 }
 
 template <bool SWIGLU, bool GATHER>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_pieces < 2 || a.K / BK < 2 * kMinPiece) return e;
+  hipLaunchKernelGGL((gemm_bf16_fixup_kernel<SWIGLU>), dim3(512), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int gemm_bf16_pieces(int64_t M, int H, int I, int E) {
+  // a K split never makes more pieces than tiles x (K stages / kMinPiece) of
+  // either GEMM, and none when a tile cannot be cut in two
+  const int64_t mt = (M + BM - 1) / BM + E;           // m-tiles, upper bound
+  auto most = [&](int64_t nt, int nk) -> int64_t {
+    const int w = nk / kMinPiece;
+    return w >= 2 ? mt * nt * w : 0;
+  };
+  const int64_t up = most((I + BN / 2 - 1) / (BN / 2), H / BK);
+  const int64_t down = most((H + BN - 1) / BN, I / BK);
+  const int64_t m = up > down ? up : down;
+  return static_cast<int>(m < kGemmPieces ? m : kGemmPieces);
+}
 
 bool gemm_bf16_gather_fits(int64_t a_rows, int K) {
   return static_cast<uint64_t>(a_rows) * static_cast<uint64_t>(K) * 2 <= (uint64_t{1} << 32);

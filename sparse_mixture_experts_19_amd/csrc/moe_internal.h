@@ -17,6 +17,7 @@ constexpr int kPermChunk = 1024;       // assignments per permutation workgroup
 constexpr int kGemmBM = 256;           // bf16 grouped GEMM: rows per tile
 constexpr int kGemmBN = 256;           // bf16 grouped GEMM: weight rows per tile
 constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage
+constexpr int kGemmPieces = 256;       // bf16 grouped GEMM: most K-split partial tiles
 constexpr int kF32BM = 64;             // fp32 grouped GEMM tile
 constexpr int kF32BN = 64;
 constexpr int kF32BK = 16;
@@ -91,8 +92,12 @@ struct GemmArgs {
   int E;
   const int32_t* offsets; // [E+1]
   const int32_t* prefix;  // [E+1] tile prefix for this kernel's BM
-  int grid;               // persistent workgroups launched
+  int grid;               // persistent workgroups launched (bf16: a multiple of 8)
+  float* partials;        // bf16: fp32 partial sums of K-split tiles, max_pieces x BM x BN
+  int max_pieces;         // capacity of partials in tiles (0: tiles are never split)
 };
+// Partial-sum slots the bf16 GEMMs of an [M rows, H, I, E] expert MLP can use.
+int gemm_bf16_pieces(int64_t M, int H, int I, int E);
 // The gathered form (gather != null) needs A to span at most 2^32 bytes.
 bool gemm_bf16_gather_fits(int64_t a_rows, int K);
 hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);

@@ -34,6 +34,8 @@ CASES = [
     ([256, 256], 128, 128),               # exact tiles
     ([1000], 512, 256),                   # one expert, several m-tiles
     ([37] * 9, 192, 64),                  # many small experts
+    ([300, 0, 45, 600], 2048, 192),       # long K of gate/up: tiles cut along K
+    ([130, 700, 0], 320, 3072),           # long K of down, N tail: tiles cut along K
 ]
 
 

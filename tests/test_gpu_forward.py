@@ -48,6 +48,14 @@ SMALL = {
     "e1k1": ("coarse_bf16", dict(T=333, H=128, I=128, E=1, k=1)),
     "k_eq_e": ("coarse_bf16", dict(T=257, H=128, I=192, E=4, k=4)),
     "f32_ragged": ("tiny_f32", dict(T=203, H=192, I=320, E=6, k=3, renormalize=True)),
+    # long K with few tiles: the bf16 GEMMs cut tiles along K into pieces whose
+    # fp32 partial sums a fixup pass adds (gate/up: H = 2048; down: I = 4096)
+    "ksplit_up": ("coarse_bf16", dict(T=300, H=2048, I=256)),
+    "ksplit_down": ("coarse_bf16", dict(T=300, H=256, I=4096)),
+    # gathered rows are permutation entry / k: k that are not powers of two
+    "k3_bf16": ("fine_bf16", dict(T=301, H=256, I=192, E=16, k=3)),
+    "k6_bf16": ("fine_bf16", dict(T=150, H=256, I=128, E=12, k=6, renormalize=False)),
+    "k7_bf16": ("vfine_bf16", dict(T=129, H=128, I=256, E=32, k=7)),
 }
 
 
