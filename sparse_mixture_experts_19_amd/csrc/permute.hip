@@ -12,9 +12,10 @@
 //   inv[f]     = r with perm[r] == f
 // Three passes, all deterministic and free of order-deciding atomics:
 //   1. per-chunk expert histograms (LDS integer counters),
-//   2. one workgroup turns them into per-(chunk, expert) row bases,
-//   3. each chunk ranks its elements in order (wave match + LDS prefix) and
-//      writes perm / inv.
+//   2. one workgroup per expert scans its chunk counts into chunk-local row
+//      bases and the expert's count,
+//   3. each chunk derives the expert offsets from the counts, ranks its
+//      elements in order (wave match + LDS prefix) and writes perm / inv.
 #include "moe_internal.h"
 
 namespace moe {
@@ -37,43 +38,56 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(PermuteArgs a) {
   if (tid < a.E) a.block_hist[static_cast<int64_t>(blockIdx.x) * a.E + tid] = hist[tid];
 }
 
+// Exclusive scan of a 256-entry workgroup vector in LDS; returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int add = tid >= d ? buf[tid - d] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int incl = buf[tid], total = buf[255];
+  __syncthreads();
+  buf[tid] = incl - v;
+  return total;
+}
+
+// One workgroup per expert: the expert's chunk counts become chunk-local row
+// bases (exclusive prefix over chunks, in chunk order); counts[e] = total.
 __global__ __launch_bounds__(256) void perm_scan_kernel(PermuteArgs a, int nblocks) {
-  __shared__ int tot[kMaxE];
-  __shared__ int off[kMaxE + 1];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < a.E) {
-    for (int b = 0; b < nblocks; ++b) {
-      int* p = a.block_hist + static_cast<int64_t>(b) * a.E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
-    }
-    tot[e] = run;
-    a.counts[e] = run;
+  __shared__ int buf[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblocks; b0 += 256) {
+    const int b = b0 + tid;
+    int* p = a.block_hist + static_cast<int64_t>(b) * a.E + e;
+    const int v = b < nblocks ? *p : 0;
+    const int total = block_exclusive_scan(v, buf);
+    if (b < nblocks) *p = carry + buf[tid];
+    carry += total;
+    __syncthreads();
   }
-  __syncthreads();
-  if (e == 0) {
-    int s = 0;
-    for (int i = 0; i < a.E; ++i) { off[i] = s; s += tot[i]; }
-    off[a.E] = s;
-  }
-  __syncthreads();
-  // E may equal the workgroup size (256): the last offset is written separately
-  if (e < a.E) a.offsets[e] = off[e];
-  if (e == 0) a.offsets[a.E] = off[a.E];
-  if (e < a.E) {
-    const int base = off[e];
-    for (int b = 0; b < nblocks; ++b) a.block_hist[static_cast<int64_t>(b) * a.E + e] += base;
-  }
+  if (tid == 0) a.counts[e] = carry;
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a) {
   __shared__ int base[kMaxE];
   __shared__ int wc[4][kMaxE];
+  __shared__ int buf[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
-  if (tid < E) base[tid] = a.block_hist[static_cast<int64_t>(blockIdx.x) * E + tid];
+  // expert offsets = exclusive prefix of the counts (every workgroup derives
+  // them; the first one also writes them out)
+  const int cnt = tid < E ? a.counts[tid] : 0;
+  const int all = block_exclusive_scan(cnt, buf);
+  if (blockIdx.x == 0) {
+    if (tid < E) a.offsets[tid] = buf[tid];
+    if (tid == 0) a.offsets[E] = all;
+  }
+  if (tid < E) base[tid] = buf[tid] + a.block_hist[static_cast<int64_t>(blockIdx.x) * E + tid];
   for (int i = tid; i < 4 * kMaxE; i += 256) (&wc[0][0])[i] = 0;
   __syncthreads();
 
@@ -156,7 +170,7 @@ size_t permute_scratch_bytes(int64_t M, int E) {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int nb = static_cast<int>((a.M + CH - 1) / CH);
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, a, nb);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(a.E), dim3(256), 0, s, a, nb);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
