@@ -141,22 +141,23 @@ moe_forward_layout forward_layout(int64_t T, int H, int I, int E, int k, int dty
   L.inv_perm = c.take(M * 4);
   L.h = c.take(M * I * eb);
   L.y = c.take(M * H * eb);
-  const size_t shared_sz = moe::route_scratch_bytes(T, E) > moe::permute_scratch_bytes(M, E)
-                               ? moe::route_scratch_bytes(T, E)
-                               : moe::permute_scratch_bytes(M, E);
+  const size_t rs = moe::route_scratch_bytes(T, H, E, dtype == MOE_DTYPE_BF16);
+  const size_t shared_sz = rs > moe::permute_scratch_bytes(M, E) ? rs : moe::permute_scratch_bytes(M, E);
   L.scratch = c.take(gemm_scratch(static_cast<int64_t>(M), H, I, E, dtype) + shared_sz);
   L.total = c.o;
   return L;
 }
 
 // Router scratch carved from `base`; returns the bytes used.
-size_t carve_route(char* base, int64_t T, int E, moe::RouteArgs& a) {
+size_t carve_route(char* base, int64_t T, int H, int E, bool bf16, moe::RouteArgs& a) {
   Carver c;
+  const size_t ks = static_cast<size_t>(moe::route_ksplit(T, H, E, bf16));
+  a.ksplit = static_cast<int>(ks);
   a.flag = reinterpret_cast<int32_t*>(base + c.take(static_cast<size_t>(T) * 4));
   a.meta = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 16));
-  a.logits = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * E * 4));
-  a.xnorm2 = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 4));
-  a.wnorm2 = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(E) * 4));
+  a.logits = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(T) * E * 4));
+  a.xnorm2 = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(T) * 4));
+  a.wnorm2 = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(E) * 4));
   return c.o;
 }
 
@@ -166,9 +167,10 @@ int run_route(const void* x, const void* w_router, const float* bias, int64_t T,
   moe::RouteArgs a{};
   a.x = x; a.w = w_router; a.bias = bias; a.T = T; a.H = H; a.E = E; a.k = k; a.renorm = renorm;
   a.ids = ids; a.weights = weights;
-  if (carve_route(scratch, T, E, a) > moe::route_scratch_bytes(T, E))
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  if (carve_route(scratch, T, H, E, bf16, a) > moe::route_scratch_bytes(T, H, E, bf16))
     return fail(MOE_ERR_WORKSPACE, "internal: router scratch layout exceeds its size");
-  MOE_HIP(moe::launch_route(a, dtype == MOE_DTYPE_BF16, s));
+  MOE_HIP(moe::launch_route(a, bf16, s));
   return MOE_OK;
 }
 
@@ -241,7 +243,7 @@ int moe_workspace_size(int32_t entry, int64_t T, int32_t H, int32_t I, int32_t E
   switch (entry) {
     case MOE_ENTRY_ROUTE:
       MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
-      *bytes = moe::route_scratch_bytes(T, E);
+      *bytes = moe::route_scratch_bytes(T, H, E, dtype == MOE_DTYPE_BF16);
       return ok();
     case MOE_ENTRY_PERMUTE:
       MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
@@ -282,7 +284,7 @@ int moe_route(const void* x, const void* w_router, const float* router_bias, int
   if (router_bias) MOE_CHECK(need_ptr(router_bias, "router_bias", 4));
   MOE_CHECK(need_ptr(topk_ids, "topk_ids", 4));
   MOE_CHECK(need_ptr(topk_weights, "topk_weights", 4));
-  const size_t need = moe::route_scratch_bytes(T, E);
+  const size_t need = moe::route_scratch_bytes(T, H, E, dtype == MOE_DTYPE_BF16);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, workspace_bytes);
   MOE_CHECK(need_ptr(workspace, "workspace", 16));

@@ -48,11 +48,15 @@ struct RouteArgs {
   float* weights;         // [T,k]
   int32_t* flag;          // [T]     1 = needs the float64 re-rank
   float* meta;            // [T,4]   max, sum, delta, unused
-  float* logits;          // [T,E]   fp32 logits (bf16 path: of every token)
-  float* xnorm2;          // [T]     ||x_t||^2 (bf16 path)
-  float* wnorm2;          // [E]     ||W_e||^2 (bf16 path)
+  float* logits;          // [ksplit,T,E] fp32 logits (bf16 path: partial sums over K ranges
+                          //              of every token; slot 0 then holds flagged tokens' totals)
+  float* xnorm2;          // [ksplit,T]   ||x_t||^2 (bf16 path, partial over K ranges)
+  float* wnorm2;          // [ksplit,E]   ||W_e||^2 (bf16 path, partial over K ranges)
+  int ksplit;             // K ranges of the bf16 logits kernel (1 for fp32)
 };
-size_t route_scratch_bytes(int64_t T, int E);
+// K ranges the bf16 router splits H into so that its grid fills the chip.
+int route_ksplit(int64_t T, int H, int E, bool bf16);
+size_t route_scratch_bytes(int64_t T, int H, int E, bool bf16);
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
 
 // ------------------------------------------------- permutation (permute.hip)
