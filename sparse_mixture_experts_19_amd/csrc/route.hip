@@ -25,6 +25,7 @@
 #include "cdna4.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -245,8 +246,30 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(RouteArgs a) {
 #pragma unroll
   for (int n = 0; n < NE; ++n) wsq[n] = 0.f;
 
-  // router-row norms: only the first token block stores them
-  const bool wnorms = blockIdx.x == 0 && wave == 0;
+  // router-row norms: only wave 0 of the first token block stores them (a
+  // wave-uniform choice, taken once per stage outside the MFMA sequence)
+  const bool wnorms = blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(wave) == 0;
+  auto multiply = [&](const uint4* Rs, f32x16_t* part, auto with_w) {
+    // all fragments of the stage first, so their LDS latencies overlap
+    bf16x8_t bx[4], aw[4][NE];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      bx[s] = *reinterpret_cast<const bf16x8_t*>(&Rs[swz128(wave * 32 + (lane & 31), c)]);
+#pragma unroll
+      for (int n = 0; n < NE; ++n)
+        aw[s][n] = *reinterpret_cast<const bf16x8_t*>(&Rs[LT * 8 + swz128(n * 32 + (lane & 31), c)]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      xsq = sumsq8_dot(bx[s], xsq);
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        if constexpr (decltype(with_w)::value) wsq[n] += sumsq8(aw[s][n]);
+        part[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[s][n], bx[s], part[n], 0, 0, 0);
+      }
+    }
+  };
   issue(0);
   if (1 < nk) issue(1);
   if (2 < nk) issue(2);
@@ -264,19 +287,8 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(RouteArgs a) {
     for (int n = 0; n < NE; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[n][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(&Rs[swz128(wave * 32 + (lane & 31), c)]);
-      xsq = sumsq8_dot(bx, xsq);
-#pragma unroll
-      for (int n = 0; n < NE; ++n) {
-        const bf16x8_t aw =
-            *reinterpret_cast<const bf16x8_t*>(&Rs[LT * 8 + swz128(n * 32 + (lane & 31), c)]);
-        if (wnorms) wsq[n] += sumsq8(aw);
-        part[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx, part[n], 0, 0, 0);
-      }
-    }
+    if (wnorms) multiply(Rs, part, std::true_type{});
+    else multiply(Rs, part, std::false_type{});
 #pragma unroll
     for (int n = 0; n < NE; ++n) acc[n] += part[n];
   }
