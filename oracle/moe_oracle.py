@@ -24,7 +24,9 @@ reason in the design notes of the repository):
     phase 4), and is optionally renormalised over the k selected experts;
   * the expert MLP is SwiGLU: W2 @ (silu(Wg @ x) * (Wu @ x)), with W13[e]
     holding the gate rows Wg first and the up rows Wu after them;
-  * the permutation is stable over the flat assignment index f = t*k + j.
+  * the permutation is stable over the flat assignment index f = t*k + j;
+  * the shared expert (optional) is a dense SwiGLU expert over every token
+    whose output is added with weight 1 to the routed sum.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (brute force, closed forms, library routines,
@@ -229,6 +231,37 @@ def forward(x, w_router, bias, w13, w2, k: int, renormalize: bool) -> Dict[str, 
     out = combine(Y, inv, w, T, k)
     return dict(out=out, ids=ids, weights=w, logits=l, probs=p, counts=counts,
                 offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
+
+
+# ---------------------------------------------------------------------------
+# Shared expert.
+# ---------------------------------------------------------------------------
+
+def shared_expert(x, ws13, ws2) -> np.ndarray:
+    """The shared expert: one SwiGLU MLP applied to every token, weight 1.
+
+    [Hunyuan page] §二.1 routes tokens through a shared-expert pool besides the
+    gated experts and gives no formula for it.  Reading taken: a dense expert
+    of the same SwiGLU form as the routed ones (gate rows then up rows in
+    ws13 [2Is,H], down weight ws2 [H,Is], its own intermediate size Is) whose
+    output is added, unweighted, to the routed sum.
+    """
+    return expert_mlp(x, ws13, ws2)
+
+
+def forward_shared(x, w_router, bias, w13, w2, ws13, ws2, k: int,
+                   renormalize: bool) -> Dict[str, np.ndarray]:
+    """MoE block with a shared expert: out = sum_j w[t,j] Y_j + S(x_t).
+
+    The routed part is ``forward``; S is ``shared_expert``.  Returns every
+    intermediate of ``forward`` plus S and the routed-only output.
+    """
+    res = forward(x, w_router, bias, w13, w2, k, renormalize)
+    S = shared_expert(x, ws13, ws2)
+    res["out_routed"] = res["out"]
+    res["S"] = S
+    res["out"] = res["out"] + S
+    return res
 
 
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],

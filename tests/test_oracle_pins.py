@@ -332,6 +332,27 @@ def pin_combine_direct():
     assert np.array_equal(out, want)
 
 
+def pin_shared_expert():
+    from scipy.special import expit
+    x, wr, b, w13, w2 = _rand_case(T=9, H=5, E=4, k=2, I=3, seed=31)
+    for renorm in (False, True):
+        base = O.forward(x, wr, b, w13, w2, 2, renorm)
+        # a zero shared down projection leaves the routed output untouched
+        zero = O.forward_shared(x, wr, b, w13, w2, np.ones((8, 5)), np.zeros((5, 4)), 2, renorm)
+        assert np.array_equal(zero["out"], base["out"])
+        # gate = 2 x, up = x, down = identity: S(x) = silu(2x) * x = 2 x^2 sigmoid(2x),
+        # added with weight 1 whatever the routing weights are
+        ws13 = np.vstack([2.0 * np.eye(5), np.eye(5)])
+        sh = O.forward_shared(x, wr, b, w13, w2, ws13, np.eye(5), 2, renorm)
+        assert np.allclose(sh["out"] - base["out"], 2.0 * x ** 2 * expit(2.0 * x), rtol=1e-12, atol=1e-14)
+        # the shared contribution is linear in its down weights
+        r = np.random.default_rng(32)
+        a13, a2 = r.standard_normal((6, 5)), r.standard_normal((5, 3))
+        one = O.forward_shared(x, wr, b, w13, w2, a13, a2, 2, renorm)["out"] - base["out"]
+        three = O.forward_shared(x, wr, b, w13, w2, a13, 3.0 * a2, 2, renorm)["out"] - base["out"]
+        assert np.allclose(three, 3.0 * one, rtol=1e-12, atol=1e-13)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
 
 
@@ -415,6 +436,18 @@ def _mut_combine_unweighted(Y, inv, w, T, k):
     return _orig_combine(Y, inv, np.ones_like(np.asarray(w, float)), T, k)
 
 
+_orig_shared = O.shared_expert
+
+
+def _mut_shared_gate_up_swapped(x, ws13, ws2):
+    I = np.asarray(ws13).shape[0] // 2
+    return _orig_shared(x, np.concatenate([ws13[I:], ws13[:I]], axis=0), ws2)
+
+
+def _mut_shared_omitted(x, ws13, ws2):
+    return np.zeros((np.asarray(x).shape[0], np.asarray(ws2).shape[0]))
+
+
 def _mut_silu_sign(z):
     z = np.asarray(z, float)
     return z / (1.0 + np.exp(z))
@@ -432,6 +465,8 @@ MUTATIONS = {
     "perm used for inv_perm in combine": ("combine", _mut_combine_perm_for_inv),
     "routing weight dropped": ("combine", _mut_combine_unweighted),
     "silu sign flipped": ("silu", _mut_silu_sign),
+    "shared expert gate and up swapped": ("shared_expert", _mut_shared_gate_up_swapped),
+    "shared expert omitted": ("shared_expert", _mut_shared_omitted),
 }
 
 
