@@ -45,9 +45,10 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic(wl, counts):
+def algorithmic(wl, counts, Is: int = 0):
     """Algorithmic flops / bytes per launch of every stage (real rows only;
-    only the weights of experts that own rows are counted)."""
+    only the weights of experts that own rows are counted).  Is: intermediate
+    size of the shared expert (0: none)."""
     b = 2 if wl.dtype == "bf16" else 4
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     M = T * k
@@ -59,7 +60,10 @@ def algorithmic(wl, counts):
     st["gemm_gate_up_swiglu"] = dict(flops=4 * M * H * I,
                                      bytes=2 * active * I * H * b + M * H * b + M * I * b + 4 * M)
     st["gemm_down"] = dict(flops=2 * M * I * H, bytes=active * H * I * b + M * I * b + M * H * b)
-    st["combine"] = dict(bytes=M * H * b + T * H * b + 8 * M, flops=0)
+    st["combine"] = dict(bytes=M * H * b + T * H * b + 8 * M + (T * H * b if Is else 0), flops=0)
+    if Is:
+        st["shared_expert"] = dict(flops=6 * T * H * Is,
+                                   bytes=3 * Is * H * b + T * H * b + 2 * T * Is * b + T * H * b)
     return st
 
 
@@ -68,8 +72,9 @@ def padding_waste(counts, bm=BM):
     return 1.0 - sum(counts) / (tiles * bm) if tiles else 0.0
 
 
-def cpu_baseline(inp, sample_tokens: int):
-    """Time the oracle as it stands on the first ``sample_tokens`` tokens."""
+def cpu_baseline(inp, sample_tokens: int, shared=None):
+    """Time the oracle as it stands on the first ``sample_tokens`` tokens
+    (with ``shared`` = (ws13, ws2) float32 arrays: the block with a shared expert)."""
     import numpy as np
     from oracle import moe_oracle as O
     try:
@@ -83,12 +88,16 @@ def cpu_baseline(inp, sample_tokens: int):
     x = inp.f32("x")[:S]
     wr, w13, w2 = inp.f32("w_router"), inp.f32("w13"), inp.f32("w2")
     t0 = time.perf_counter()
-    res = O.forward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize)
+    if shared is None:
+        res = O.forward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize)
+    else:
+        res = O.forward_shared(x, wr, inp.bias, w13, w2, shared[0], shared[1], wl.k, wl.renormalize)
     dt = time.perf_counter() - t0
     assert np.isfinite(res["out"]).all()
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {wl.T} tokens of {wl.name}, float64 numpy oracle "
-                      f"(route+permute+experts+combine), {dt:.1f} s"}
+                      f"(route+permute+experts{'+shared expert' if shared is not None else ''}"
+                      f"+combine), {dt:.1f} s"}
 
 
 def main():
@@ -103,6 +112,8 @@ def main():
     ap.add_argument("--report", default=None, help="also append the JSON record to this file")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB MiB (scales HBM byte counters)")
+    ap.add_argument("--shared-intermediate", type=int, default=0, metavar="IS",
+                    help="add a shared expert of intermediate size IS (moe_forward_shared)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -144,10 +155,17 @@ def main():
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     dt_code = B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
     out = torch.empty((wl.T, wl.H), dtype=x.dtype, device=dev)
-    ws = torch.empty(B.workspace_size(B.ENTRY_FORWARD, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code),
-                     dtype=torch.uint8, device=dev)
-    nst = len(B.PROFILE_STAGES)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.PROFILE_EVENTS)]
+    Is = args.shared_intermediate
+    if Is:
+        hs13, hs2 = W.make_shared_weights(wl, Is)
+        ws13, ws2 = up(hs13), up(hs2)
+        nbytes = B.shared_layout(wl.T, wl.H, wl.I, Is, wl.E, wl.k, dt_code).total
+        stages, n_ev = B.PROFILE_STAGES_SHARED, B.PROFILE_EVENTS_SHARED
+    else:
+        nbytes = B.workspace_size(B.ENTRY_FORWARD, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
+        stages, n_ev = B.PROFILE_STAGES, B.PROFILE_EVENTS
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
            for _ in range(max(args.steps, 1))]
     for row in evs:
         for e in row:
@@ -155,8 +173,12 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
-        B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
-                               evs[i % len(evs)])
+        if Is:
+            B.moe_forward_shared(x, wr, bias, w13, w2, ws13, ws2, wl.k, wl.renormalize, out, ws,
+                                 events=evs[i % len(evs)])
+        else:
+            B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
+                                   evs[i % len(evs)])
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -170,16 +192,16 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    stage_ms = {s: 0.0 for s in B.PROFILE_STAGES}
+    stage_ms = {s: 0.0 for s in stages}
     for i in range(args.steps):
-        for j, s in enumerate(B.PROFILE_STAGES):
+        for j, s in enumerate(stages):
             stage_ms[s] += evs[i][j].elapsed_time(evs[i][j + 1]) / args.steps
     mid = B.forward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
     counts = mid["counts"].cpu().numpy().tolist()
 
-    alg = algorithmic(wl, counts)
+    alg = algorithmic(wl, counts, Is)
     detail = {}
-    for s in B.PROFILE_STAGES:
+    for s in stages:
         t = stage_ms[s] * 1e-3
         d = {"ms": round(stage_ms[s], 5)}
         if alg[s]["bytes"]:
@@ -193,7 +215,7 @@ def main():
     grouped_tflops = g_flops / g_t / 1e12
 
     # dominant kernel roofline
-    dom = max(B.PROFILE_STAGES, key=lambda s: stage_ms[s])
+    dom = max(stages, key=lambda s: stage_ms[s])
     a = alg[dom]
     tdom = stage_ms[dom] * 1e-3
     ai = a["flops"] / a["bytes"] if a["bytes"] else 0.0
@@ -230,8 +252,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
-        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
-                   "top_k": wl.k, "intermediate": wl.I, "renormalize": wl.renormalize,
+        "config": {"workload": wl.name + (f"+shared{Is}" if Is else ""), "tokens": wl.T,
+                   "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
+                   "shared_intermediate": Is, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},
         "grouped_gemm": {"TFLOP/s": round(grouped_tflops, 1),
                          "frac_of_peak": round(grouped_tflops / peak, 4),
@@ -243,7 +266,11 @@ def main():
         sample = args.cpu_sample or {"tiny_f32": 512, "coarse_bf16": 4096, "fine_bf16": 4096,
                                      "vfine_bf16": 4096, "skewed_bf16": 8192}.get(wl.name, 1024)
         log(f"[bench] CPU oracle baseline on {sample} tokens")
-        rec["cpu_baseline"] = cpu_baseline(inp, sample)
+        sh = None
+        if Is:
+            cv = (lambda a: W.bf16_bits_to_f32(a)) if wl.dtype == "bf16" else (lambda a: a)
+            sh = (cv(hs13), cv(hs2))
+        rec["cpu_baseline"] = cpu_baseline(inp, sample, sh)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.report:

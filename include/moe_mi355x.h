@@ -218,6 +218,64 @@ int moe_forward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E,
                                  moe_forward_layout* layout);
 
 /*
+ * moe_forward_shared -- moe_forward plus a shared expert.  [Hunyuan page]
+ * §二.1 routes tokens through a shared-expert pool besides the gated experts
+ * without giving its formula; the reading implemented here is a dense expert
+ * of the routed experts' SwiGLU form applied to every token and added with
+ * weight 1:
+ *   out[t] = sum_{j<k} w[t,j] * Y_{t,j} + S(x_t),
+ *   S(x)   = ws2 (silu(ws13[0:Is] x) * (ws13[Is:2Is] x)).
+ * S is computed by the same grouped-GEMM kernels as one dense group, stored
+ * as dtype like Y, and added after the k routed slots in the same fp32 sum,
+ * rounded once.
+ *
+ *   ws13 [2*Is,H] dtype, ws2 [H,Is] dtype, device, 16-byte aligned; Is a
+ *   multiple of 64, at most 65536.  Other arguments as moe_forward.
+ *   workspace  moe_forward_shared_layout(...).total bytes, device.  The
+ *              routed intermediates sit at the offsets of layout.routed, the
+ *              shared expert's h and output at h_shared / y_shared.
+ */
+int moe_forward_shared(const void* x, const void* w_router,
+                       const float* router_bias, const void* w13,
+                       const void* w2, const void* ws13, const void* ws2,
+                       int64_t T, int32_t H, int32_t I, int32_t Is, int32_t E,
+                       int32_t k, int32_t dtype, int32_t renormalize,
+                       void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * moe_forward_shared_profiled -- moe_forward_shared recording caller-created
+ * HIP events around its stages (as moe_forward_profiled), n_events ==
+ * MOE_PROFILE_EVENTS_SHARED: stages 0..4 as moe_forward_profiled, then
+ *   5 shared expert (gate/up and down GEMMs over every token)
+ *   6 combine (routed slots plus the shared output)
+ */
+#define MOE_PROFILE_EVENTS_SHARED 8
+int moe_forward_shared_profiled(const void* x, const void* w_router,
+                                const float* router_bias, const void* w13,
+                                const void* w2, const void* ws13,
+                                const void* ws2, int64_t T, int32_t H,
+                                int32_t I, int32_t Is, int32_t E, int32_t k,
+                                int32_t dtype, int32_t renormalize, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* const* events, int32_t n_events,
+                                void* stream);
+
+/* Byte offsets inside the moe_forward_shared workspace. */
+typedef struct moe_shared_layout {
+    moe_forward_layout routed;  /* routed intermediates, as in moe_forward */
+    size_t h_shared;            /* [T,Is] dtype */
+    size_t y_shared;            /* [T,H] dtype: S(x) */
+    size_t scratch;             /* internal */
+    size_t total;               /* workspace bytes moe_forward_shared needs */
+} moe_shared_layout;
+
+/* Host-only.  Fills *layout; same validation as moe_forward_shared's sizes. */
+int moe_forward_shared_layout(int64_t T, int32_t H, int32_t I, int32_t Is,
+                              int32_t E, int32_t k, int32_t dtype,
+                              moe_shared_layout* layout);
+
+/*
  * Host-only.  Workspace bytes needed by `entry` (a moe_entry) for these
  * sizes, written to *bytes (host pointer).  For MOE_ENTRY_GROUPED_GEMM pass
  * T = M and k = 1.  Sizes that the entry ignores may be given as 1.

@@ -34,6 +34,11 @@ class ForwardLayout(ctypes.Structure):
         "h", "y", "scratch", "total")]
 
 
+class SharedLayout(ctypes.Structure):
+    _fields_ = [("routed", ForwardLayout)] + [(n, ctypes.c_size_t) for n in (
+        "h_shared", "y_shared", "scratch", "total")]
+
+
 _SIGS = {
     "moe_route": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
     "moe_permute": [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
@@ -41,6 +46,9 @@ _SIGS = {
     "moe_combine": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _vp, _vp],
     "moe_forward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
     "moe_forward_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_forward_shared": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
+    "moe_forward_shared_profiled": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_forward_shared_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(SharedLayout)],
     "moe_workspace_size": [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_forward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_status_string": [_c_i32],
@@ -229,6 +237,56 @@ def moe_forward_profiled(x, w_router, router_bias, w13, w2, k: int, renormalize:
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       handles, PROFILE_EVENTS, _stream(dev)))
     return out
+
+
+def shared_layout(T: int, H: int, I: int, Is: int, E: int, k: int, dtype: int) -> SharedLayout:
+    L = SharedLayout()
+    _check(lib().moe_forward_shared_layout(T, H, I, Is, E, k, dtype, ctypes.byref(L)))
+    return L
+
+
+PROFILE_EVENTS_SHARED = 8
+PROFILE_STAGES_SHARED = ("route", "permute", "schedule", "gemm_gate_up_swiglu", "gemm_down",
+                         "shared_expert", "combine")
+
+
+def moe_forward_shared(x, w_router, router_bias, w13, w2, ws13, ws2, k: int, renormalize: bool,
+                       out=None, workspace=None, events=None):
+    """The MoE block with a shared expert (ws13 [2Is,H], ws2 [H,Is]) added to every token.
+    Returns (out, workspace); with ``events`` (8 timing events) the stages are recorded
+    as PROFILE_STAGES_SHARED."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    Is = ws13.shape[0] // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    ws = _workspace(shared_layout(T, H, I, Is, E, k, dt).total, dev, workspace)
+    args = [_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2), _ptr(ws13), _ptr(ws2),
+            T, H, I, Is, E, k, dt, int(bool(renormalize)), _ptr(out), _ptr(ws),
+            ws.numel() * ws.element_size()]
+    if events is None:
+        _check(lib().moe_forward_shared(*args, _stream(dev)))
+    else:
+        if len(events) != PROFILE_EVENTS_SHARED:
+            raise ValueError(f"need {PROFILE_EVENTS_SHARED} events")
+        handles = (ctypes.c_void_p * PROFILE_EVENTS_SHARED)(*[ev.cuda_event for ev in events])
+        _check(lib().moe_forward_shared_profiled(*args, handles, PROFILE_EVENTS_SHARED, _stream(dev)))
+    return out, ws
+
+
+def shared_intermediates(ws: torch.Tensor, T: int, H: int, I: int, Is: int, E: int, k: int,
+                         dtype: int):
+    """forward_intermediates plus the shared expert's h_shared [T,Is] and y_shared [T,H]."""
+    S = shared_layout(T, H, I, Is, E, k, dtype)
+    eb = 2 if dtype == MOE_DTYPE_BF16 else 4
+    tdt = _torch_dtype(dtype)
+    mid = forward_intermediates(ws, T, H, I, E, k, dtype)
+    mid["h_shared"] = ws[S.h_shared:S.h_shared + T * Is * eb].view(tdt).view(T, Is)
+    mid["y_shared"] = ws[S.y_shared:S.y_shared + T * H * eb].view(tdt).view(T, H)
+    return mid
 
 
 def forward_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int, dtype: int):

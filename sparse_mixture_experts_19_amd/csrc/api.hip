@@ -148,6 +148,22 @@ moe_forward_layout forward_layout(int64_t T, int H, int I, int E, int k, int dty
   return L;
 }
 
+// The moe_forward layout, then the shared expert's h [T,Is], output [T,H]
+// and its own GEMM scratch: dense offsets {0, T} (256 bytes), then the tile
+// prefix and partial sums of a one-group grouped GEMM.
+moe_shared_layout shared_layout(int64_t T, int H, int I, int Is, int E, int k, int dtype) {
+  moe_shared_layout S;
+  S.routed = forward_layout(T, H, I, E, k, dtype);
+  const size_t eb = elem_bytes(dtype);
+  Carver c;
+  c.o = S.routed.total;
+  S.h_shared = c.take(static_cast<size_t>(T) * Is * eb);
+  S.y_shared = c.take(static_cast<size_t>(T) * H * eb);
+  S.scratch = c.take(256 + gemm_scratch(T, H, Is, 1, dtype));
+  S.total = c.o;
+  return S;
+}
+
 // Router scratch carved from `base`; returns the bytes used.
 size_t carve_route(char* base, int64_t T, int H, int E, bool bf16, moe::RouteArgs& a) {
   Carver c;
@@ -222,7 +238,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 100; }
+int moe_version(void) { return 101; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -369,8 +385,16 @@ namespace {
 int forward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
                  const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                  int32_t dtype, int32_t renormalize, void* out, void* workspace,
-                 size_t workspace_bytes, void* const* events, hipStream_t s) {
+                 size_t workspace_bytes, void* const* events, hipStream_t s,
+                 const void* ws13 = nullptr, const void* ws2 = nullptr, int32_t Is = 0) {
+  const bool with_shared = ws13 != nullptr || ws2 != nullptr || Is != 0;
   MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  if (with_shared) {
+    MOE_CHECK(check_sizes(T, H, Is, 1, 1, dtype, true));
+    if (T == 0) return ok();
+    MOE_CHECK(need_ptr(ws13, "ws13", 16));
+    MOE_CHECK(need_ptr(ws2, "ws2", 16));
+  }
   if (T == 0) return ok();
   MOE_CHECK(need_ptr(x, "x", 16));
   MOE_CHECK(need_ptr(w_router, "w_router", 16));
@@ -378,13 +402,16 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   MOE_CHECK(need_ptr(w13, "w13", 16));
   MOE_CHECK(need_ptr(w2, "w2", 16));
   MOE_CHECK(need_ptr(out, "out", 16));
-  const moe_forward_layout L = forward_layout(T, H, I, E, k, dtype);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", L.total,
+  const moe_shared_layout SL = shared_layout(T, H, I, with_shared ? Is : 64, E, k, dtype);
+  const moe_forward_layout& L = SL.routed;
+  const size_t need = with_shared ? SL.total : L.total;
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
   MOE_CHECK(need_ptr(workspace, "workspace", 256));
+  const int n_events = with_shared ? MOE_PROFILE_EVENTS_SHARED : MOE_PROFILE_EVENTS;
   if (events)
-    for (int i = 0; i < MOE_PROFILE_EVENTS; ++i)
+    for (int i = 0; i < n_events; ++i)
       if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
   int cu = 0;
   MOE_CHECK(current_device(nullptr, &cu));
@@ -434,8 +461,34 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   g.C = w + L.y; g.N = H; g.K = I;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
   MOE_CHECK(mark(5));
-  MOE_HIP(moe::launch_combine(w + L.y, inv, wts, T, H, k, bf16, out, s));
-  MOE_CHECK(mark(6));
+  const void* ys = nullptr;
+  if (with_shared) {
+    // the shared expert: one dense group of all T rows of x through the same
+    // grouped-GEMM kernels
+    char* ss = w + SL.scratch;
+    int32_t* soff = reinterpret_cast<int32_t*>(ss);
+    int32_t* spre = reinterpret_cast<int32_t*>(ss + 256);
+    MOE_HIP(moe::launch_dense_offsets(soff, T, s));
+    MOE_HIP(moe::launch_tile_schedule(soff, 1, bf16 ? moe::kGemmBM : moe::kF32BM, T, spre, s));
+    moe::GemmArgs d{};
+    d.E = 1; d.offsets = soff; d.prefix = spre; d.I = Is; d.M = T; d.a_rows = T; d.grid = g.grid;
+    if (bf16) {
+      d.partials = reinterpret_cast<float*>(ss + 256 + gemm_prefix_bytes(1));
+      d.max_pieces = moe::gemm_bf16_pieces(T, H, Is, 1);
+    }
+    d.A = x; d.gather = nullptr; d.gather_div = 1;
+    d.B = ws13; d.b_stride = static_cast<int64_t>(2) * Is * H;
+    d.C = w + SL.h_shared; d.N = Is; d.K = H;
+    MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(d, s) : moe::launch_gemm_f32_swiglu(d, s));
+    d.A = w + SL.h_shared;
+    d.B = ws2; d.b_stride = static_cast<int64_t>(H) * Is;
+    d.C = w + SL.y_shared; d.N = H; d.K = Is;
+    MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(d, s) : moe::launch_gemm_f32_down(d, s));
+    ys = w + SL.y_shared;
+    MOE_CHECK(mark(6));
+  }
+  MOE_HIP(moe::launch_combine(w + L.y, inv, wts, T, H, k, bf16, out, s, ys));
+  MOE_CHECK(mark(with_shared ? 7 : 6));
   return ok();
 }
 
@@ -461,6 +514,41 @@ int moe_forward_profiled(const void* x, const void* w_router, const float* route
                 MOE_PROFILE_EVENTS);
   return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
                       workspace, workspace_bytes, events, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_shared(const void* x, const void* w_router, const float* router_bias,
+                       const void* w13, const void* w2, const void* ws13, const void* ws2,
+                       int64_t T, int32_t H, int32_t I, int32_t Is, int32_t E, int32_t k,
+                       int32_t dtype, int32_t renormalize, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!ws13 || !ws2) return fail(MOE_ERR_INVALID_ARG, "ws13 and ws2 must be set");
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream), ws13,
+                      ws2, Is);
+}
+
+int moe_forward_shared_profiled(const void* x, const void* w_router, const float* router_bias,
+                                const void* w13, const void* w2, const void* ws13,
+                                const void* ws2, int64_t T, int32_t H, int32_t I, int32_t Is,
+                                int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* const* events, int32_t n_events, void* stream) {
+  if (!ws13 || !ws2) return fail(MOE_ERR_INVALID_ARG, "ws13 and ws2 must be set");
+  if (!events || n_events != MOE_PROFILE_EVENTS_SHARED)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_SHARED (%d) handles",
+                MOE_PROFILE_EVENTS_SHARED);
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream), ws13,
+                      ws2, Is);
+}
+
+int moe_forward_shared_layout(int64_t T, int32_t H, int32_t I, int32_t Is, int32_t E, int32_t k,
+                              int32_t dtype, moe_shared_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  MOE_CHECK(check_sizes(T, H, Is, 1, 1, dtype, true));
+  *layout = shared_layout(T, H, I, Is, E, k, dtype);
+  return ok();
 }
 
 }  // extern "C"

@@ -75,6 +75,9 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
                               int elem_bytes, void* x_perm, hipStream_t s);
 
+// offsets[0] = 0, offsets[1] = M: one dense group of M rows.
+hipError_t launch_dense_offsets(int32_t* offsets, int64_t M, hipStream_t s);
+
 // Tile schedule of the grouped GEMMs: prefix[e] = sum_{e'<e} ceil(count_e'/bm).
 hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int64_t M,
                                 int32_t* prefix, hipStream_t s);
@@ -111,7 +114,7 @@ hipError_t launch_gemm_f32_down(const GemmArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ combine (combine.hip)
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t T, int H,
-                          int k, bool bf16, void* out, hipStream_t s);
+                          int k, bool bf16, void* out, hipStream_t s, const void* ys = nullptr);
 
 // ------------------------------------------------------------ device query
 int device_cu_count();

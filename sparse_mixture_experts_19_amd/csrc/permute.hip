@@ -142,6 +142,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   }
 }
 
+__global__ void dense_offsets_kernel(int32_t* offsets, int64_t M) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = static_cast<int32_t>(M);
+  }
+}
+
 __global__ __launch_bounds__(256) void tile_schedule_kernel(const int32_t* offsets, int E, int bm,
                                                             int64_t M, int32_t* prefix) {
   __shared__ int mt[kMaxE];
@@ -186,6 +193,11 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int
   hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
                      static_cast<const uint4*>(x), perm, M, M / k, chunks, k,
                      static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_offsets(int32_t* offsets, int64_t M, hipStream_t s) {
+  hipLaunchKernelGGL(dense_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, M);
   return hipGetLastError();
 }
 

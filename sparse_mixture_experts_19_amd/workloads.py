@@ -41,6 +41,8 @@ TENSOR_X = 0
 TENSOR_WR = 1
 TENSOR_W13 = 2
 TENSOR_W2 = 3
+TENSOR_WS13 = 4       # shared expert (optional)
+TENSOR_WS2 = 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -189,6 +191,16 @@ def make_inputs(wl: Workload, threads: Optional[int] = None,
     else:
         raise ValueError(f"unknown bias recipe {wl.bias!r}")
     return Inputs(wl, x, w_router, bias, w13, w2)
+
+
+def make_shared_weights(wl: Workload, Is: int):
+    """Weights of a shared expert with intermediate size Is for ``wl``: ws13
+    [2Is,H] (gate rows then up rows, scale 1/sqrt(H)) and ws2 [H,Is] (scale
+    1/sqrt(Is)), same recipe as the routed experts, own tensor ids."""
+    H = wl.H
+    ws13 = _finish(_draw(wl.seed, wl.config_id, TENSOR_WS13, 0, (2 * Is, H), 1.0 / math.sqrt(H)), wl.dtype)
+    ws2 = _finish(_draw(wl.seed, wl.config_id, TENSOR_WS2, 0, (H, Is), 1.0 / math.sqrt(Is)), wl.dtype)
+    return ws13, ws2
 
 
 def random_small(T: int, H: int, E: int, k: int, I: int, dtype: str, seed: int,

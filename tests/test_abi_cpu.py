@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 100
+    assert L.moe_version() == 101
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -125,6 +125,32 @@ def test_other_entries_argument_errors():
     size = ctypes.c_size_t(0)
     assert L.moe_workspace_size(9, 8, 64, 64, 4, 2, 1, ctypes.byref(size)) == B.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size(0, 8, 64, 64, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_shared_expert_layout_and_argument_errors():
+    T, H, I, Is, E, k = 4096, 4096, 14336, 5632, 8, 2
+    S = B.shared_layout(T, H, I, Is, E, k, B.MOE_DTYPE_BF16)
+    R = B.forward_layout(T, H, I, E, k, B.MOE_DTYPE_BF16)
+    # the routed part is laid out exactly as moe_forward's, the shared regions follow it
+    for f, _ in B.ForwardLayout._fields_:
+        assert getattr(S.routed, f) == getattr(R, f), f
+    offs = [R.total, S.h_shared, S.y_shared, S.scratch, S.total]
+    assert S.h_shared >= R.total and all(o % 256 == 0 for o in offs[1:])
+    assert S.y_shared - S.h_shared >= T * Is * 2 and S.scratch - S.y_shared >= T * H * 2
+    L = B.lib()
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("wr", FAKE), ("b", None), ("w13", FAKE), ("w2", FAKE), ("ws13", FAKE),
+        ("ws2", FAKE), ("T", 8), ("H", 64), ("I", 128), ("Is", 128), ("E", 4), ("k", 2),
+        ("dt", 1), ("ren", 0), ("out", FAKE), ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert L.moe_forward_shared(*args(ws13=None)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_shared(*args(ws2=FAKE + 4)) == B.MOE_ERR_INVALID_ARG   # misaligned
+    assert L.moe_forward_shared(*args(Is=100)) == B.MOE_ERR_UNSUPPORTED          # Is % 64
+    assert L.moe_forward_shared(*args(Is=0)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_shared(*args(wsb=1024)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward_shared(*args(T=0, x=None, out=None, ws=None, wsb=0)) == B.MOE_OK
+    lay = B.SharedLayout()
+    assert L.moe_forward_shared_layout(8, 64, 128, 96, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_shared_layout(8, 64, 128, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
