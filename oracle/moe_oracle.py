@@ -12,6 +12,7 @@ is exact in float64 and each dot product carries only float64 summation error.
 Page legend (titles of the pages the steps are taken from):
   [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
   [Hunyuan page]   "混合专家架构大模型Hunyuan-Large：原理剖析与实现机制"
+  [SonicMoE page]  "SonicMoE与传统MoE架构对比：Token舍入技术如何实现训练效率跃升"
 
 Readings taken where the pages leave a step open (each is listed with its
 reason in the design notes of the repository):
@@ -26,7 +27,8 @@ reason in the design notes of the repository):
     holding the gate rows Wg first and the up rows Wu after them;
   * the permutation is stable over the flat assignment index f = t*k + j;
   * the shared expert (optional) is a dense SwiGLU expert over every token
-    whose output is added with weight 1 to the routed sum.
+    whose output is added with weight 1 to the routed sum;
+  * token rounding (optional) follows the integer rule in ``token_round``.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (brute force, closed forms, library routines,
@@ -262,6 +264,111 @@ def forward_shared(x, w_router, bias, w13, w2, ws13, ws2, k: int,
     res["S"] = S
     res["out"] = res["out"] + S
     return res
+
+
+# ---------------------------------------------------------------------------
+# Token rounding (routing variant).
+# ---------------------------------------------------------------------------
+
+def _round_pool(ids, E: int, B: int):
+    """Kept row counts floor(c_e/B)*B and the pooled flat indices (flat order)."""
+    counts, offsets, perm, inv = permute(ids, E)
+    keep = (counts // B) * B
+    pooled = np.zeros(np.asarray(ids).size, dtype=bool)
+    for e in range(E):
+        pooled[perm[offsets[e] + keep[e]:offsets[e + 1]]] = True
+    return keep, [int(f) for f in np.nonzero(pooled)[0]]
+
+
+def _round_order(load):
+    """Experts in the order a pooled tile is offered to them: load, then id."""
+    return sorted(range(len(load)), key=lambda q: (load[q], q))
+
+
+def _round_eligible(cur, t: int, j: int, e: int) -> bool:
+    """Slot j of token t may move to e if no other slot of t holds e."""
+    return all(cur[t, jj] != e for jj in range(cur.shape[1]) if jj != j)
+
+
+def _round_weights(probs, ids, renormalize: bool):
+    """Weight of each slot: the token's softmax probability of its expert."""
+    w = _f64(probs)[np.arange(ids.shape[0])[:, None], ids]
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+def token_round(ids, probs, E: int, B: int, renormalize: bool):
+    """Token rounding: re-route assignments so expert row counts are tile multiples.
+
+    [SonicMoE page] 核心差异 §3: each expert's assignment count is rounded
+    down to a multiple of the tile size and the remaining tokens are given to
+    the least-loaded experts, which removes the tile padding of the grouped
+    GEMM.  The page's listing is garbled (``tokens // expert_capacity``); the
+    rule taken here, with every decision on integers:
+
+    1. Expert e keeps the first floor(c_e / B) * B rows of its segment of the
+       stable expert-sorted permutation (assignments in flat order f = t*k+j);
+       the rest of its rows go to a pool.
+    2. The pool, in flat order, is handed out in tiles of B: the tile goes to
+       the expert with the lowest load (kept rows plus rows received so far,
+       ties to the lowest id) that can take at least one pooled assignment,
+       and takes the next pooled assignments, in order, whose token is not
+       routed to that expert by another slot; at most one slot of a token per
+       tile (taking a slot makes the token's other slots ineligible).  A tile
+       is shorter than B only when fewer eligible assignments are left.
+    3. A moved assignment keeps its slot j; its weight is the token's softmax
+       probability of the new expert, renormalised over the token's k weights
+       when the workload renormalises (unmoved slots keep the same formula).
+
+    ids [T,k] int, probs [T,E] float64 (softmax over all experts).  Returns
+    (new ids [T,k] int32, new weights [T,k] float64, moved [T,k] bool).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    keep, pool = _round_pool(ids, E, B)
+    load = keep.astype(np.int64).copy()
+    cur = ids.astype(np.int32).copy()
+    taken = [False] * len(pool)
+    left = len(pool)
+    while left:
+        for e in _round_order(load):
+            got, seen = 0, set()
+            for i, f in enumerate(pool):
+                if taken[i]:
+                    continue
+                t, j = divmod(f, k)
+                if t in seen or not _round_eligible(cur, t, j, e):
+                    continue
+                cur[t, j] = e
+                taken[i] = True
+                seen.add(t)
+                got += 1
+                if got == B:
+                    break
+            if got:
+                load[e] += got
+                left -= got
+                break
+        else:
+            raise RuntimeError("no expert can take a pooled assignment")   # needs k >= E
+    return cur, _round_weights(probs, cur, renormalize), cur != ids
+
+
+def forward_rounded(x, w_router, bias, w13, w2, k: int, renormalize: bool,
+                    B: int) -> Dict[str, np.ndarray]:
+    """MoE block with token rounding (``token_round``, tile B) between routing
+    and the permutation.  Returns the output and every intermediate."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    ids0, w0, l, p = route(x, w_router, bias, k, renormalize)
+    ids, w, moved = token_round(ids0, p, E, B, renormalize)
+    counts, offsets, perm, inv = permute(ids, E)
+    Y = experts(x, perm, offsets, w13, w2, k)
+    out = combine(Y, inv, w, T, k)
+    return dict(out=out, ids=ids, weights=w, moved=moved, ids_topk=ids0, weights_topk=w0,
+                logits=l, probs=p, counts=counts, offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
 
 
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],

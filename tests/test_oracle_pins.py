@@ -353,6 +353,140 @@ def pin_shared_expert():
         assert np.allclose(three, 3.0 * one, rtol=1e-12, atol=1e-13)
 
 
+# --------------------------------------------------------------------------
+# Token rounding ([SonicMoE page] 核心差异 §3; the integer rule in the
+# oracle's token_round docstring)
+# --------------------------------------------------------------------------
+
+def _route_case(T, E, k, seed, H=8):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((T, H))
+    w = r.standard_normal((E, H)) / 3
+    ids, wts, l, p = O.route(x, w, None, k, False)
+    return ids, p
+
+
+def _rank_in_expert(ids):
+    """rank[t, j]: how many earlier assignments (flat order) share the expert."""
+    seen = {}
+    rank = np.zeros(ids.shape, dtype=np.int64)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            rank[t, j] = seen.get(e, 0)
+            seen[e] = rank[t, j] + 1
+    return rank
+
+
+def pin_token_round_hand_example():
+    """Worked by hand: T=6, E=3, k=2, B=3.  Counts are 4,4,4, so each expert
+    keeps 3 and pools its last assignment in flat order: (t4,j0)->0,
+    (t5,j0)->2, (t5,j1)->1.  Tile 1 (all loads 3, lowest id) goes to expert 0
+    and takes (t4,j0) (back to 0) and (t5,j0) (2 -> 0); (t5,j1) is the same
+    token's second slot, so the pool runs out for this tile at 2 rows.  Tile
+    2 goes to expert 1 (load 3 < 5) and takes (t5,j1), whose expert stays 1."""
+    ids = np.array([[0, 1], [0, 2], [0, 1], [1, 2], [0, 2], [2, 1]])
+    p = np.full((6, 3), 1.0 / 3.0)
+    p[5] = [0.5, 0.2, 0.3]
+    new, w, moved = O.token_round(ids, p, 3, 3, False)
+    want = ids.copy()
+    want[5, 0] = 0
+    assert np.array_equal(new, want)
+    assert moved.sum() == 1 and moved[5, 0]
+    assert np.allclose(w[5], [0.5, 0.2]) and np.allclose(w[:5], 1.0 / 3.0)
+    _, wr, _ = O.token_round(ids, p, 3, 3, True)
+    assert np.allclose(wr[5], [0.5 / 0.7, 0.2 / 0.7])
+
+
+def pin_token_round_k1_closed_form():
+    """k = 1 has no eligibility limit: the pool (flat order) is cut into
+    consecutive blocks of B, and block i goes to the i-th choice of the
+    water-filling (least kept-plus-received rows, lowest id), so the padded
+    tile count becomes exactly ceil(T / B)."""
+    for T, E, B, seed in [(97, 5, 8, 1), (300, 7, 16, 2), (64, 3, 64, 3), (50, 6, 7, 4)]:
+        ids, p = _route_case(T, E, 1, seed)
+        flat = ids[:, 0]
+        counts = np.array([(flat == e).sum() for e in range(E)])
+        keep = counts // B * B
+        rank = _rank_in_expert(ids)[:, 0]
+        pool = [t for t in range(T) if rank[t] >= keep[flat[t]]]
+        load = list(keep)
+        owners = []
+        left = len(pool)
+        while left > 0:
+            e = min(range(E), key=lambda q: (load[q], q))
+            n = min(B, left)
+            owners.append(e)
+            load[e] += n
+            left -= n
+        want = flat.copy()
+        for i, t in enumerate(pool):
+            want[t] = owners[i // B]
+        new, w, moved = O.token_round(ids, p, E, B, False)
+        assert np.array_equal(new[:, 0], want), (T, E, B)
+        c2 = np.bincount(new[:, 0], minlength=E)
+        assert np.ceil(c2 / B).sum() == -(-T // B)
+        assert np.allclose(w[:, 0], p[np.arange(T), new[:, 0]])
+
+
+def pin_token_round_wide_tile():
+    """B > T: every count is below B, so everything is pooled and all loads
+    start at 0.  Expert 0 then takes one slot of every token, expert 1 the
+    next, ...: each token ends with exactly the experts {0, ..., k-1}."""
+    for T, E, k, seed in [(9, 5, 2, 5), (20, 8, 3, 6), (6, 4, 4, 7)]:
+        ids, p = _route_case(T, E, k, seed)
+        new, w, moved = O.token_round(ids, p, E, T + 1, True)
+        for t in range(T):
+            assert sorted(new[t]) == list(range(k))
+        assert np.allclose(w.sum(axis=1), 1.0)
+
+
+def pin_token_round_invariants():
+    """Random cases: no token holds an expert twice; the kept rows (the first
+    floor(c_e/B)*B of each expert in flat order) never move; only pooled rows
+    move; weights are the probabilities of the final experts; nothing moves
+    when B = 1, when every count is already a multiple of B, or when k = E."""
+    for T, E, k, B, seed, renorm in [(200, 8, 2, 16, 8, False), (150, 16, 4, 8, 9, True),
+                                      (300, 32, 8, 12, 10, True), (80, 6, 3, 5, 11, False)]:
+        ids, p = _route_case(T, E, k, seed)
+        new, w, moved = O.token_round(ids, p, E, B, renorm)
+        counts = np.bincount(ids.ravel(), minlength=E)
+        keep = counts // B * B
+        rank = _rank_in_expert(ids)
+        kept = rank < keep[ids]
+        assert np.array_equal(new[kept], ids[kept])
+        assert np.array_equal(moved, new != ids) and not moved[kept].any()
+        assert moved.any()
+        for t in range(T):
+            assert len(set(new[t].tolist())) == k
+        want = p[np.arange(T)[:, None], new]
+        if renorm:
+            want = want / want.sum(axis=1, keepdims=True)
+        assert np.allclose(w, want, rtol=1e-14, atol=0)
+        assert np.bincount(new.ravel(), minlength=E).sum() == T * k
+    ids, p = _route_case(60, 8, 2, 12)
+    for B in (1,):
+        new, w, moved = O.token_round(ids, p, 8, B, False)
+        assert not moved.any() and np.array_equal(new, ids)
+    # every count a multiple of 4: tokens cycle through pairs (e, e+1 mod 8)
+    ids = np.array([[t % 8, (t + 1) % 8] for t in range(32)])
+    new, w, moved = O.token_round(ids, np.full((32, 8), 0.125), 8, 4, False)
+    assert not moved.any()
+    ids, p = _route_case(40, 4, 4, 13)
+    new, w, moved = O.token_round(ids, p, 4, 3, False)
+    assert not moved.any()
+
+
+def pin_forward_rounded_composition():
+    """The rounded block is the plain block run on the rounded routing."""
+    x, w, b, w13, w2 = _rand_case(T=30, H=6, E=5, k=2, I=3, seed=31)
+    r = O.forward_rounded(x, w, b, w13, w2, 2, True, 4)
+    c = np.bincount(r["ids"].ravel(), minlength=5)
+    assert np.array_equal(c, r["counts"])
+    ref = _brute_dense(x, r["ids"], r["weights"], w13, w2)
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
 
 
@@ -453,6 +587,38 @@ def _mut_silu_sign(z):
     return z / (1.0 + np.exp(z))
 
 
+_orig_round_pool = O._round_pool
+_orig_round_order = O._round_order
+_orig_round_weights = O._round_weights
+
+
+def _mut_round_pool_reversed(ids, E, B):
+    keep, pool = _orig_round_pool(ids, E, B)
+    return keep, pool[::-1]
+
+
+def _mut_round_pool_ceil(ids, E, B):
+    keep, pool = _orig_round_pool(ids, E, B)
+    c = np.bincount(np.asarray(ids).ravel(), minlength=E)
+    return -(-c // B) * B, []
+
+
+def _mut_round_most_loaded(load):
+    return _orig_round_order(load)[::-1]
+
+
+def _mut_round_ties_high(load):
+    return sorted(range(len(load)), key=lambda q: (load[q], -q))
+
+
+def _mut_round_any_slot(cur, t, j, e):
+    return True
+
+
+def _mut_round_weights_not_renormalised(probs, ids, renormalize):
+    return _orig_round_weights(probs, ids, False)
+
+
 MUTATIONS = {
     "topk ties to the highest index": ("topk_ids", _mut_topk_ties_high),
     "topk slots ascending": ("topk_ids", _mut_topk_ascending_slots),
@@ -467,6 +633,12 @@ MUTATIONS = {
     "silu sign flipped": ("silu", _mut_silu_sign),
     "shared expert gate and up swapped": ("shared_expert", _mut_shared_gate_up_swapped),
     "shared expert omitted": ("shared_expert", _mut_shared_omitted),
+    "rounding pool in reverse order": ("_round_pool", _mut_round_pool_reversed),
+    "rounding keeps rounded-up counts": ("_round_pool", _mut_round_pool_ceil),
+    "rounding tile to the most-loaded expert": ("_round_order", _mut_round_most_loaded),
+    "rounding ties to the highest id": ("_round_order", _mut_round_ties_high),
+    "rounding ignores the token's other slots": ("_round_eligible", _mut_round_any_slot),
+    "rounded weights not renormalised": ("_round_weights", _mut_round_weights_not_renormalised),
 }
 
 
