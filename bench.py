@@ -61,6 +61,10 @@ def algorithmic(wl, counts, Is: int = 0):
                                      bytes=2 * active * I * H * b + M * H * b + M * I * b + 4 * M)
     st["gemm_down"] = dict(flops=2 * M * I * H, bytes=active * H * I * b + M * I * b + M * H * b)
     st["combine"] = dict(bytes=M * H * b + T * H * b + 8 * M + (T * H * b if Is else 0), flops=0)
+    # token rounding: permutation of the routed ids (12 B per assignment), the
+    # pooled-slot pass (8 B read per assignment, 9 B written per token) and the
+    # new ids / weights pass (4 B read per assignment)
+    st["token_round"] = dict(bytes=24 * M + 9 * T, flops=0)
     if Is:
         st["shared_expert"] = dict(flops=6 * T * H * Is,
                                    bytes=3 * Is * H * b + T * H * b + 2 * T * Is * b + T * H * b)
@@ -72,9 +76,10 @@ def padding_waste(counts, bm=BM):
     return 1.0 - sum(counts) / (tiles * bm) if tiles else 0.0
 
 
-def cpu_baseline(inp, sample_tokens: int, shared=None):
+def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0):
     """Time the oracle as it stands on the first ``sample_tokens`` tokens
-    (with ``shared`` = (ws13, ws2) float32 arrays: the block with a shared expert)."""
+    (with ``shared`` = (ws13, ws2) float32 arrays: the block with a shared expert;
+    with ``round_tile``: the block with token rounding over those tokens)."""
     import numpy as np
     from oracle import moe_oracle as O
     try:
@@ -88,7 +93,9 @@ def cpu_baseline(inp, sample_tokens: int, shared=None):
     x = inp.f32("x")[:S]
     wr, w13, w2 = inp.f32("w_router"), inp.f32("w13"), inp.f32("w2")
     t0 = time.perf_counter()
-    if shared is None:
+    if round_tile:
+        res = O.forward_rounded(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize, round_tile)
+    elif shared is None:
         res = O.forward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize)
     else:
         res = O.forward_shared(x, wr, inp.bias, w13, w2, shared[0], shared[1], wl.k, wl.renormalize)
@@ -96,7 +103,8 @@ def cpu_baseline(inp, sample_tokens: int, shared=None):
     assert np.isfinite(res["out"]).all()
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {wl.T} tokens of {wl.name}, float64 numpy oracle "
-                      f"(route+permute+experts{'+shared expert' if shared is not None else ''}"
+                      f"(route{'+token rounding' if round_tile else ''}+permute+experts"
+                      f"{'+shared expert' if shared is not None else ''}"
                       f"+combine), {dt:.1f} s"}
 
 
@@ -114,6 +122,10 @@ def main():
                     help="only run device-to-device copies of MB MiB (scales HBM byte counters)")
     ap.add_argument("--shared-intermediate", type=int, default=0, metavar="IS",
                     help="add a shared expert of intermediate size IS (moe_forward_shared)")
+    ap.add_argument("--round", action="store_true",
+                    help="token rounding to the grouped GEMM's row tile (moe_forward_rounded)")
+    ap.add_argument("--round-tile", type=int, default=0, metavar="B",
+                    help="token rounding to B rows (moe_forward_rounded)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -156,7 +168,14 @@ def main():
     dt_code = B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
     out = torch.empty((wl.T, wl.H), dtype=x.dtype, device=dev)
     Is = args.shared_intermediate
-    if Is:
+    RB = args.round_tile or (B.gemm_tile_rows(dt_code) if args.round else 0)
+    if RB and Is:
+        print("bench.py: --round and --shared-intermediate do not combine", file=sys.stderr)
+        sys.exit(2)
+    if RB:
+        nbytes = B.rounded_layout(wl.T, wl.H, wl.I, wl.E, wl.k, dt_code).total
+        stages, n_ev = B.PROFILE_STAGES_ROUNDED, B.PROFILE_EVENTS_ROUNDED
+    elif Is:
         hs13, hs2 = W.make_shared_weights(wl, Is)
         ws13, ws2 = up(hs13), up(hs2)
         nbytes = B.shared_layout(wl.T, wl.H, wl.I, Is, wl.E, wl.k, dt_code).total
@@ -173,7 +192,10 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
-        if Is:
+        if RB:
+            B.moe_forward_rounded(x, wr, bias, w13, w2, wl.k, wl.renormalize, RB, out, ws,
+                                  events=evs[i % len(evs)])
+        elif Is:
             B.moe_forward_shared(x, wr, bias, w13, w2, ws13, ws2, wl.k, wl.renormalize, out, ws,
                                  events=evs[i % len(evs)])
         else:
@@ -252,9 +274,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
-        "config": {"workload": wl.name + (f"+shared{Is}" if Is else ""), "tokens": wl.T,
+        "config": {"workload": wl.name + (f"+shared{Is}" if Is else "") +
+                   (f"+round{RB}" if RB else ""), "tokens": wl.T,
                    "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
-                   "shared_intermediate": Is, "renormalize": wl.renormalize,
+                   "shared_intermediate": Is, "round_tile": RB, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},
         "grouped_gemm": {"TFLOP/s": round(grouped_tflops, 1),
                          "frac_of_peak": round(grouped_tflops / peak, 4),
@@ -270,7 +293,7 @@ def main():
         if Is:
             cv = (lambda a: W.bf16_bits_to_f32(a)) if wl.dtype == "bf16" else (lambda a: a)
             sh = (cv(hs13), cv(hs2))
-        rec["cpu_baseline"] = cpu_baseline(inp, sample, sh)
+        rec["cpu_baseline"] = cpu_baseline(inp, sample, sh, RB)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.report:

@@ -276,6 +276,75 @@ int moe_forward_shared_layout(int64_t T, int32_t H, int32_t I, int32_t Is,
                               moe_shared_layout* layout);
 
 /*
+ * moe_forward_rounded -- moe_forward with token rounding between the router
+ * and the permutation.  [SonicMoE page] 核心差异 §3 rounds each expert's row
+ * count down to a multiple of the GEMM row tile and gives the remaining
+ * tokens to the least-loaded experts, so the grouped GEMM pads no tile.  The
+ * rule implemented (all integer decisions, B = tile_rows):
+ *   1. expert e keeps the first floor(c_e/B)*B of its assignments in flat
+ *      order f = t*k + j; the others are pooled;
+ *   2. the pool is handed out in rounds: a round with P pooled assignments
+ *      left opens ceil(P/B) tiles of B rows and first picks their owners by
+ *      water-filling (lowest row count, kept plus B per tile already planned,
+ *      ties to the lowest id, skipping experts one of whose tiles came out
+ *      empty); then, tile by tile, a tile takes up to B pooled assignments in
+ *      flat order whose token holds its owner in no other slot, at most one
+ *      slot per token (a token's first untaken pooled slot, or the slot that
+ *      already holds the owner).  What a round leaves goes to the next one;
+ *   3. a moved slot keeps its position j; its weight is the token's softmax
+ *      probability of the new expert (renormalised over the token's k
+ *      weights when renormalize != 0).  Unmoved tokens keep their weights.
+ * No token ever holds an expert twice (needs k <= E, which is a limit anyway).
+ *
+ *   tile_rows  B >= 1; moe_gemm_tile_rows(dtype) is the row tile of this
+ *              library's grouped GEMM, the value that removes its padding.
+ *   workspace  moe_forward_rounded_layout(...).total bytes, device.
+ * The workspace intermediates are those of moe_forward for the rounded
+ * routing: topk_ids / topk_weights hold the rounded ids and weights, and the
+ * counts, offsets and permutation are those of the rounded ids.  Other
+ * arguments and results as moe_forward.  The tile hand-out is sequential by
+ * nature and runs in one workgroup (its tiles pipelined across 16 waves); its
+ * cost grows with the number of tiles handed out and the pool tokens each
+ * tile walks.
+ */
+int moe_forward_rounded(const void* x, const void* w_router,
+                        const float* router_bias, const void* w13,
+                        const void* w2, int64_t T, int32_t H, int32_t I,
+                        int32_t E, int32_t k, int32_t dtype,
+                        int32_t renormalize, int32_t tile_rows, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward_rounded_profiled -- moe_forward_rounded recording caller-created
+ * HIP events around its stages (as moe_forward_profiled), n_events ==
+ * MOE_PROFILE_EVENTS_ROUNDED:
+ *   0 router (also keeps every token's logits, softmax max and sum)
+ *   1 token rounding (permutation of the routed ids, pooled slots, tile
+ *     hand-out, new weights)
+ *   2 permutation of the rounded ids
+ *   3..6 tile schedule, gate/up GEMM, down GEMM, combine
+ */
+#define MOE_PROFILE_EVENTS_ROUNDED 8
+int moe_forward_rounded_profiled(const void* x, const void* w_router,
+                                 const float* router_bias, const void* w13,
+                                 const void* w2, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k,
+                                 int32_t dtype, int32_t renormalize,
+                                 int32_t tile_rows, void* out, void* workspace,
+                                 size_t workspace_bytes, void* const* events,
+                                 int32_t n_events, void* stream);
+
+/* Host-only.  Fills *layout (same fields as moe_forward's; a larger scratch
+ * and total); same validation as moe_forward's sizes. */
+int moe_forward_rounded_layout(int64_t T, int32_t H, int32_t I, int32_t E,
+                               int32_t k, int32_t dtype,
+                               moe_forward_layout* layout);
+
+/* Host-only.  Rows per tile of the grouped GEMM for dtype (bf16: 256, fp32:
+ * 64); 0 for an unknown dtype (moe_last_error() then says so). */
+int moe_gemm_tile_rows(int32_t dtype);
+
+/*
  * Host-only.  Workspace bytes needed by `entry` (a moe_entry) for these
  * sizes, written to *bytes (host pointer).  For MOE_ENTRY_GROUPED_GEMM pass
  * T = M and k = 1.  Sizes that the entry ignores may be given as 1.

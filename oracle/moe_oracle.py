@@ -310,13 +310,16 @@ def token_round(ids, probs, E: int, B: int, renormalize: bool):
     1. Expert e keeps the first floor(c_e / B) * B rows of its segment of the
        stable expert-sorted permutation (assignments in flat order f = t*k+j);
        the rest of its rows go to a pool.
-    2. The pool, in flat order, is handed out in tiles of B: the tile goes to
-       the expert with the lowest load (kept rows plus rows received so far,
-       ties to the lowest id) that can take at least one pooled assignment,
-       and takes the next pooled assignments, in order, whose token is not
-       routed to that expert by another slot; at most one slot of a token per
-       tile (taking a slot makes the token's other slots ineligible).  A tile
-       is shorter than B only when fewer eligible assignments are left.
+    2. The pool is handed out in rounds.  A round with P pooled assignments
+       left opens n = ceil(P / B) tiles of B rows and first decides the owner
+       of every tile by water-filling: tile by tile, the expert with the
+       lowest load (rows kept plus B per tile granted so far in the round;
+       ties to the lowest id) among those that have not come out empty.
+       Then, tile by tile in order, a tile takes up to B of the pooled
+       assignments, in flat order, whose token holds the owner in no other
+       slot, at most one slot per token.  A tile that takes nothing marks its
+       owner as unable to take; whatever a round leaves goes to the next
+       round, with the loads actually reached.
     3. A moved assignment keeps its slot j; its weight is the token's softmax
        probability of the new expert, renormalised over the token's k weights
        when the workload renormalises (unmoved slots keep the same formula).
@@ -328,13 +331,24 @@ def token_round(ids, probs, E: int, B: int, renormalize: bool):
     T, k = ids.shape
     keep, pool = _round_pool(ids, E, B)
     load = keep.astype(np.int64).copy()
+    unable = np.zeros(E, dtype=bool)
     cur = ids.astype(np.int32).copy()
     taken = [False] * len(pool)
     left = len(pool)
     while left:
-        for e in _round_order(load):
+        plan = load.copy()
+        owners = []
+        for _ in range(-(-left // B)):
+            order = [e for e in _round_order(plan) if not unable[e]]
+            if not order:
+                raise RuntimeError("no expert can take a pooled assignment")   # needs k >= E
+            owners.append(order[0])
+            plan[order[0]] += B
+        for e in owners:
             got, seen = 0, set()
             for i, f in enumerate(pool):
+                if got == B:
+                    break
                 if taken[i]:
                     continue
                 t, j = divmod(f, k)
@@ -344,14 +358,10 @@ def token_round(ids, probs, E: int, B: int, renormalize: bool):
                 taken[i] = True
                 seen.add(t)
                 got += 1
-                if got == B:
-                    break
-            if got:
-                load[e] += got
-                left -= got
-                break
-        else:
-            raise RuntimeError("no expert can take a pooled assignment")   # needs k >= E
+            load[e] += got
+            left -= got
+            if got == 0:
+                unable[e] = True
     return cur, _round_weights(probs, cur, renormalize), cur != ids
 
 

@@ -49,6 +49,10 @@ _SIGS = {
     "moe_forward_shared": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
     "moe_forward_shared_profiled": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
     "moe_forward_shared_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(SharedLayout)],
+    "moe_forward_rounded": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
+    "moe_forward_rounded_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_forward_rounded_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
+    "moe_gemm_tile_rows": [_c_i32],
     "moe_workspace_size": [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_forward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_status_string": [_c_i32],
@@ -287,6 +291,53 @@ def shared_intermediates(ws: torch.Tensor, T: int, H: int, I: int, Is: int, E: i
     mid["h_shared"] = ws[S.h_shared:S.h_shared + T * Is * eb].view(tdt).view(T, Is)
     mid["y_shared"] = ws[S.y_shared:S.y_shared + T * H * eb].view(tdt).view(T, H)
     return mid
+
+
+def rounded_layout(T: int, H: int, I: int, E: int, k: int, dtype: int) -> ForwardLayout:
+    L = ForwardLayout()
+    _check(lib().moe_forward_rounded_layout(T, H, I, E, k, dtype, ctypes.byref(L)))
+    return L
+
+
+def gemm_tile_rows(dtype: int) -> int:
+    """Rows per tile of the grouped GEMM (the token-rounding tile that removes its padding)."""
+    n = lib().moe_gemm_tile_rows(dtype)
+    if n <= 0:
+        _check(MOE_ERR_UNSUPPORTED)
+    return n
+
+
+PROFILE_EVENTS_ROUNDED = 8
+PROFILE_STAGES_ROUNDED = ("route", "token_round", "permute", "schedule", "gemm_gate_up_swiglu",
+                          "gemm_down", "combine")
+
+
+def moe_forward_rounded(x, w_router, router_bias, w13, w2, k: int, renormalize: bool,
+                        tile_rows: Optional[int] = None, out=None, workspace=None, events=None):
+    """The MoE block with token rounding to ``tile_rows`` rows (default: the grouped
+    GEMM's row tile).  Returns (out, workspace); the workspace holds the rounded
+    routing at the moe_forward offsets (``forward_intermediates``).  With ``events``
+    (8 timing events) the stages are recorded as PROFILE_STAGES_ROUNDED."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    B = gemm_tile_rows(dt) if tile_rows is None else int(tile_rows)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    ws = _workspace(rounded_layout(T, H, I, E, k, dt).total, dev, workspace)
+    args = [_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2), T, H, I, E, k, dt,
+            int(bool(renormalize)), B, _ptr(out), _ptr(ws), ws.numel() * ws.element_size()]
+    if events is None:
+        _check(lib().moe_forward_rounded(*args, _stream(dev)))
+    else:
+        if len(events) != PROFILE_EVENTS_ROUNDED:
+            raise ValueError(f"need {PROFILE_EVENTS_ROUNDED} events")
+        handles = (ctypes.c_void_p * PROFILE_EVENTS_ROUNDED)(*[ev.cuda_event for ev in events])
+        _check(lib().moe_forward_rounded_profiled(*args, handles, PROFILE_EVENTS_ROUNDED,
+                                                  _stream(dev)))
+    return out, ws
 
 
 def forward_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int, dtype: int):

@@ -164,6 +164,22 @@ moe_shared_layout shared_layout(int64_t T, int H, int I, int Is, int E, int k, i
   return S;
 }
 
+// The moe_forward layout with a scratch region that holds the router's,
+// the permutation's and the token rounding's scratch side by side: the
+// rounding reads the router's logits after the first permutation ran.
+moe_forward_layout rounded_layout(int64_t T, int H, int I, int E, int k, int dtype) {
+  moe_forward_layout L = forward_layout(T, H, I, E, k, dtype);
+  const int64_t M = T * k;
+  Carver c;
+  c.o = L.scratch;
+  c.take(gemm_scratch(M, H, I, E, dtype));
+  c.take(moe::route_scratch_bytes(T, H, E, dtype == MOE_DTYPE_BF16));
+  c.take(moe::permute_scratch_bytes(M, E));
+  c.take(moe::round_scratch_bytes(T));
+  L.total = c.o;
+  return L;
+}
+
 // Router scratch carved from `base`; returns the bytes used.
 size_t carve_route(char* base, int64_t T, int H, int E, bool bf16, moe::RouteArgs& a) {
   Carver c;
@@ -179,14 +195,15 @@ size_t carve_route(char* base, int64_t T, int H, int E, bool bf16, moe::RouteArg
 
 int run_route(const void* x, const void* w_router, const float* bias, int64_t T, int H, int E,
               int k, int dtype, int renorm, int32_t* ids, float* weights, char* scratch,
-              hipStream_t s) {
+              hipStream_t s, moe::RouteArgs* out_args = nullptr) {
   moe::RouteArgs a{};
   a.x = x; a.w = w_router; a.bias = bias; a.T = T; a.H = H; a.E = E; a.k = k; a.renorm = renorm;
-  a.ids = ids; a.weights = weights;
+  a.ids = ids; a.weights = weights; a.keep_all = out_args != nullptr;
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   if (carve_route(scratch, T, H, E, bf16, a) > moe::route_scratch_bytes(T, H, E, bf16))
     return fail(MOE_ERR_WORKSPACE, "internal: router scratch layout exceeds its size");
   MOE_HIP(moe::launch_route(a, bf16, s));
+  if (out_args) *out_args = a;
   return MOE_OK;
 }
 
@@ -238,7 +255,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 101; }
+int moe_version(void) { return 102; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -382,12 +399,29 @@ int moe_combine(const void* y, const int32_t* inv_perm, const float* topk_weight
 
 namespace {
 
+// Optional parts of the block: a shared expert (ws13, ws2, Is) or token
+// rounding to round_tile rows (0: off).
+struct Options {
+  const void* ws13 = nullptr;
+  const void* ws2 = nullptr;
+  int32_t Is = 0;
+  int32_t round_tile = 0;
+};
+
 int forward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
                  const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                  int32_t dtype, int32_t renormalize, void* out, void* workspace,
                  size_t workspace_bytes, void* const* events, hipStream_t s,
-                 const void* ws13 = nullptr, const void* ws2 = nullptr, int32_t Is = 0) {
+                 const Options& opt = Options()) {
+  const void* ws13 = opt.ws13;
+  const void* ws2 = opt.ws2;
+  const int32_t Is = opt.Is;
   const bool with_shared = ws13 != nullptr || ws2 != nullptr || Is != 0;
+  const bool rounded = opt.round_tile != 0;
+  if (rounded && opt.round_tile < 1)
+    return fail(MOE_ERR_INVALID_ARG, "tile_rows must be >= 1 (got %d)", opt.round_tile);
+  if (rounded && with_shared)
+    return fail(MOE_ERR_UNSUPPORTED, "token rounding with a shared expert is not supported");
   MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
   if (with_shared) {
     MOE_CHECK(check_sizes(T, H, Is, 1, 1, dtype, true));
@@ -403,13 +437,15 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   MOE_CHECK(need_ptr(w2, "w2", 16));
   MOE_CHECK(need_ptr(out, "out", 16));
   const moe_shared_layout SL = shared_layout(T, H, I, with_shared ? Is : 64, E, k, dtype);
-  const moe_forward_layout& L = SL.routed;
+  const moe_forward_layout L = rounded ? rounded_layout(T, H, I, E, k, dtype) : SL.routed;
   const size_t need = with_shared ? SL.total : L.total;
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
   MOE_CHECK(need_ptr(workspace, "workspace", 256));
-  const int n_events = with_shared ? MOE_PROFILE_EVENTS_SHARED : MOE_PROFILE_EVENTS;
+  const int n_events = with_shared ? MOE_PROFILE_EVENTS_SHARED
+                       : rounded   ? MOE_PROFILE_EVENTS_ROUNDED
+                                   : MOE_PROFILE_EVENTS;
   if (events)
     for (int i = 0; i < n_events; ++i)
       if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
@@ -426,18 +462,42 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   const int64_t M = T * k;
   char* shared = w + L.scratch + gemm_scratch(M, H, I, E, dtype);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
-  auto mark = [&](int i) -> int {
-    if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[i]), s));
+  int next_event = 0;
+  auto mark = [&]() -> int {
+    if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[next_event]), s));
+    ++next_event;
     return MOE_OK;
   };
 
-  MOE_CHECK(mark(0));
-  MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared, s));
-  MOE_CHECK(mark(1));
-  MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
-  MOE_CHECK(mark(2));
+  MOE_CHECK(mark());
+  if (rounded) {
+    // router scratch, permutation scratch and rounding scratch side by side
+    Carver c;
+    char* rs = shared + c.take(moe::route_scratch_bytes(T, H, E, bf16));
+    char* ps = shared + c.take(moe::permute_scratch_bytes(M, E));
+    char* xs = shared + c.take(moe::round_scratch_bytes(T));
+    moe::RouteArgs ra{};
+    MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, rs, s,
+                        &ra));
+    MOE_CHECK(mark());
+    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, ps, s));
+    moe::RoundArgs r{};
+    r.ids = ids; r.weights = wts; r.logits = ra.logits; r.meta = ra.meta;
+    r.counts = counts; r.offsets = offsets; r.inv = inv;
+    r.T = T; r.E = E; r.k = k; r.B = opt.round_tile; r.renorm = renormalize;
+    moe::carve_round(xs, r);
+    MOE_HIP(moe::launch_token_round(r, s));
+    MOE_CHECK(mark());
+    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, ps, s));
+  } else {
+    MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared,
+                        s));
+    MOE_CHECK(mark());
+    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
+  }
+  MOE_CHECK(mark());
   MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, M, prefix, s));
-  MOE_CHECK(mark(3));
+  MOE_CHECK(mark());
   moe::GemmArgs g{};
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = T;
   g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
@@ -455,12 +515,12 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
   g.C = w + L.h; g.N = I; g.K = H;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
-  MOE_CHECK(mark(4));
+  MOE_CHECK(mark());
   g.A = w + L.h; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
   g.C = w + L.y; g.N = H; g.K = I;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
-  MOE_CHECK(mark(5));
+  MOE_CHECK(mark());
   const void* ys = nullptr;
   if (with_shared) {
     // the shared expert: one dense group of all T rows of x through the same
@@ -485,10 +545,13 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
     d.C = w + SL.y_shared; d.N = H; d.K = Is;
     MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(d, s) : moe::launch_gemm_f32_down(d, s));
     ys = w + SL.y_shared;
-    MOE_CHECK(mark(6));
+    MOE_CHECK(mark());
   }
   MOE_HIP(moe::launch_combine(w + L.y, inv, wts, T, H, k, bf16, out, s, ys));
-  MOE_CHECK(mark(with_shared ? 7 : 6));
+  MOE_CHECK(mark());
+  if (next_event != n_events)
+    return fail(MOE_ERR_UNSUPPORTED, "internal: %d stage events recorded, %d expected", next_event,
+                n_events);
   return ok();
 }
 
@@ -522,9 +585,10 @@ int moe_forward_shared(const void* x, const void* w_router, const float* router_
                        int32_t dtype, int32_t renormalize, void* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (!ws13 || !ws2) return fail(MOE_ERR_INVALID_ARG, "ws13 and ws2 must be set");
+  Options o;
+  o.ws13 = ws13; o.ws2 = ws2; o.Is = Is;
   return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
-                      workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream), ws13,
-                      ws2, Is);
+                      workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream), o);
 }
 
 int moe_forward_shared_profiled(const void* x, const void* w_router, const float* router_bias,
@@ -537,9 +601,10 @@ int moe_forward_shared_profiled(const void* x, const void* w_router, const float
   if (!events || n_events != MOE_PROFILE_EVENTS_SHARED)
     return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_SHARED (%d) handles",
                 MOE_PROFILE_EVENTS_SHARED);
+  Options o;
+  o.ws13 = ws13; o.ws2 = ws2; o.Is = Is;
   return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
-                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream), ws13,
-                      ws2, Is);
+                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream), o);
 }
 
 int moe_forward_shared_layout(int64_t T, int32_t H, int32_t I, int32_t Is, int32_t E, int32_t k,
@@ -549,6 +614,49 @@ int moe_forward_shared_layout(int64_t T, int32_t H, int32_t I, int32_t Is, int32
   MOE_CHECK(check_sizes(T, H, Is, 1, 1, dtype, true));
   *layout = shared_layout(T, H, I, Is, E, k, dtype);
   return ok();
+}
+
+int moe_forward_rounded(const void* x, const void* w_router, const float* router_bias,
+                        const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
+                        int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
+                        int32_t tile_rows, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (tile_rows < 1) return fail(MOE_ERR_INVALID_ARG, "tile_rows must be >= 1 (got %d)", tile_rows);
+  Options o;
+  o.round_tile = tile_rows;
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream), o);
+}
+
+int moe_forward_rounded_profiled(const void* x, const void* w_router, const float* router_bias,
+                                 const void* w13, const void* w2, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k, int32_t dtype,
+                                 int32_t renormalize, int32_t tile_rows, void* out,
+                                 void* workspace, size_t workspace_bytes, void* const* events,
+                                 int32_t n_events, void* stream) {
+  if (tile_rows < 1) return fail(MOE_ERR_INVALID_ARG, "tile_rows must be >= 1 (got %d)", tile_rows);
+  if (!events || n_events != MOE_PROFILE_EVENTS_ROUNDED)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_ROUNDED (%d) handles",
+                MOE_PROFILE_EVENTS_ROUNDED);
+  Options o;
+  o.round_tile = tile_rows;
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream), o);
+}
+
+int moe_forward_rounded_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                               int32_t dtype, moe_forward_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  *layout = rounded_layout(T, H, I, E, k, dtype);
+  return ok();
+}
+
+int moe_gemm_tile_rows(int32_t dtype) {
+  if (dtype == MOE_DTYPE_BF16) return moe::kGemmBM;
+  if (dtype == MOE_DTYPE_F32) return moe::kF32BM;
+  fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  return 0;
 }
 
 }  // extern "C"

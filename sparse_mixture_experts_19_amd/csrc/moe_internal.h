@@ -53,6 +53,7 @@ struct RouteArgs {
   float* xnorm2;          // [ksplit,T]   ||x_t||^2 (bf16 path, partial over K ranges)
   float* wnorm2;          // [ksplit,E]   ||W_e||^2 (bf16 path, partial over K ranges)
   int ksplit;             // K ranges of the bf16 logits kernel (1 for fp32)
+  int keep_all;           // 1: meta and total logits are written for every token
 };
 // K ranges the bf16 router splits H into so that its grid fills the chip.
 int route_ksplit(int64_t T, int H, int E, bool bf16);
@@ -111,6 +112,28 @@ hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_down(const GemmArgs& a, hipStream_t s);
+
+// --------------------------------------------------- token rounding (round.hip)
+struct RoundArgs {
+  int32_t* ids;           // [T,k] in: routed ids; out: rounded ids
+  float* weights;         // [T,k] out: weights of tokens whose experts changed
+  const float* logits;    // [T,E] fp32 total logits (bias included) of every token
+  const float* meta;      // [T,4] softmax max and sum of every token
+  const int32_t* counts;  // [E]   of the routed ids
+  const int32_t* offsets; // [E+1]
+  const int32_t* inv;     // [T*k] inverse of the routed ids' stable permutation
+  int64_t T;
+  int E, k, B, renorm;
+  uint8_t* mask;          // [T] scratch: pooled slots of each token
+  uint64_t* packed;       // [T] scratch: the token's ids, one byte per slot
+  int32_t* pool_tok;      // [T] scratch: tokens with a pooled slot, in order
+  uint64_t* gsid;         // [T] scratch: hand-out state when it does not fit in LDS
+  uint8_t* gmask;         // [T]
+};
+size_t round_scratch_bytes(int64_t T);
+// Carves the scratch arrays of `a` from `base` (round_scratch_bytes(T) bytes).
+void carve_round(char* base, RoundArgs& a);
+hipError_t launch_token_round(const RoundArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ combine (combine.hip)
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t T, int H,

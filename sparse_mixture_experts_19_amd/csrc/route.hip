@@ -134,7 +134,7 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
     a.weights[t * k + sub] = a.renorm ? pj / ps : pj;
   }
   if (sub == 0) a.flag[t] = flag ? 1 : 0;
-  if (flag) {
+  if (flag || a.keep_all) {
     if (sub == 0) {
       a.meta[t * 4 + 0] = mx;
       a.meta[t * 4 + 1] = s;

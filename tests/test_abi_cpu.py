@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 101
+    assert L.moe_version() == 102
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -151,6 +151,38 @@ def test_shared_expert_layout_and_argument_errors():
     lay = B.SharedLayout()
     assert L.moe_forward_shared_layout(8, 64, 128, 96, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_forward_shared_layout(8, 64, 128, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_rounded_layout_and_argument_errors():
+    T, H, I, E, k = 16384, 2048, 768, 128, 8
+    R = B.forward_layout(T, H, I, E, k, B.MOE_DTYPE_BF16)
+    Q = B.rounded_layout(T, H, I, E, k, B.MOE_DTYPE_BF16)
+    # same intermediates at the same offsets, a larger scratch region
+    for f, _ in B.ForwardLayout._fields_:
+        if f != "total":
+            assert getattr(Q, f) == getattr(R, f), f
+    assert Q.total > R.total and Q.total % 256 == 0
+    assert B.gemm_tile_rows(B.MOE_DTYPE_BF16) == 256 and B.gemm_tile_rows(B.MOE_DTYPE_F32) == 64
+    L = B.lib()
+    assert L.moe_gemm_tile_rows(7) == 0 and len(L.moe_last_error()) > 0
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("wr", FAKE), ("b", None), ("w13", FAKE), ("w2", FAKE), ("T", 8), ("H", 64),
+        ("I", 128), ("E", 4), ("k", 2), ("dt", 1), ("ren", 0), ("B", 256), ("out", FAKE),
+        ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert L.moe_forward_rounded(*args(B=0)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_rounded(*args(B=-5)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_rounded(*args(k=5)) == B.MOE_ERR_INVALID_ARG            # k > E
+    assert L.moe_forward_rounded(*args(w13=None)) == B.MOE_ERR_INVALID_ARG
+    # the rounded path needs more workspace than moe_forward's
+    small = B.forward_layout(8, 64, 128, 4, 2, B.MOE_DTYPE_BF16).total
+    assert L.moe_forward_rounded(*args(wsb=small)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward_rounded(*args(T=0, x=None, out=None, ws=None, wsb=0)) == B.MOE_OK
+    assert L.moe_forward_rounded_profiled(*args()[:-1], None, 0, None) == B.MOE_ERR_INVALID_ARG
+    ev = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert L.moe_forward_rounded_profiled(*args()[:-1], ev, 7, None) == B.MOE_ERR_INVALID_ARG
+    lay = B.ForwardLayout()
+    assert L.moe_forward_rounded_layout(8, 64, 100, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_rounded_layout(8, 64, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")

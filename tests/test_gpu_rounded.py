@@ -1,0 +1,175 @@
+"""GPU parity of moe_forward_rounded (token rounding between the router and
+the permutation) against the float64 oracle: the router's ids bit-exact, the
+rounded ids and the permutation of them bit-exact (every rounding decision is
+an integer one), the rounded weights and the block output within tolerance;
+small shapes in full with small tiles (many tiles handed out), a pool larger
+than the library's LDS state, and the full-size workloads with the GEMM's own
+row tile on sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_19_amd import binding as B
+from sparse_mixture_experts_19_amd import workloads as W
+from moe_test_utils import (TOL_OUT, TOL_WEIGHTS, compare_ids, host_f64, log, row_rel_err,
+                            sample_tokens, upload)
+
+pytestmark = pytest.mark.gpu
+
+# Pool tokens (tokens with a pooled slot) whose hand-out state the library
+# keeps in LDS; larger pools keep it in the workspace.
+LDS_POOL_TOKENS = 14336
+
+
+def _dt(wl):
+    return B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
+
+
+def _run(inp, tile, d=None):
+    wl = inp.wl
+    d = d or upload(inp)
+    out, ws = B.moe_forward_rounded(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                                    wl.renormalize, tile)
+    ids0, _ = B.moe_route(d["x"], d["w_router"], d["bias"], wl.k, wl.renormalize)
+    torch.cuda.synchronize()
+    mid = B.forward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k, _dt(wl))
+    mid = {n: (v.cpu() if n not in ("h", "y") else v) for n, v in mid.items()}
+    return out, mid, ids0.cpu().numpy(), d
+
+
+def _check_rounding(mid, ids0_gpu, ids0, l, p, E, tile, renorm):
+    """Router ids exact; rounded ids, counts, offsets, perm, inv exact; weights
+    within TOL_WEIGHTS.  Returns the oracle's rounded ids and weights."""
+    assert not compare_ids(ids0_gpu, ids0, l), "float64 ties in the routing"
+    new, nw, moved = O.token_round(ids0, p, E, tile, renorm)
+    got = mid["ids"].numpy()
+    bad = np.nonzero((got != new).any(axis=1))[0]
+    assert bad.size == 0, (f"{bad.size} tokens differ, first {bad[:5].tolist()}: "
+                           f"{got[bad[:3]].tolist()} vs {new[bad[:3]].tolist()}")
+    ew = np.abs(mid["weights"].numpy() - nw).max()
+    assert ew <= TOL_WEIGHTS, ew
+    oc, oo, op, oi = O.permute(new, E)
+    assert np.array_equal(mid["counts"].numpy(), oc)
+    assert np.array_equal(mid["offsets"].numpy(), oo)
+    assert np.array_equal(mid["perm"].numpy(), op)
+    assert np.array_equal(mid["inv_perm"].numpy(), oi)
+    c0 = np.bincount(ids0.ravel(), minlength=E)
+    log(f"  moved {int(moved.sum())} of {moved.size}; padded tiles "
+        f"{int(np.ceil(c0 / tile).sum())} -> {int(np.ceil(oc / tile).sum())}")
+    return new, nw, oo, op
+
+
+CASES = {
+    # base workload, size changes, rounding tile
+    "coarse_t32": ("coarse_bf16", dict(T=300, H=256, I=512), 32),
+    "fine_t16": ("fine_bf16", dict(T=400, H=256, I=256), 16),
+    "fine_t256": ("fine_bf16", dict(T=700, H=256, I=128), 256),
+    "vfine_t8": ("vfine_bf16", dict(T=200, H=512, I=256), 8),
+    "skewed_t64": ("skewed_bf16", dict(T=900, H=256, I=192), 64),
+    "f32_ragged_t16": ("tiny_f32", dict(T=203, H=192, I=320, E=6, k=3, renormalize=True), 16),
+    "f32_t64": ("tiny_f32", dict(T=512), 64),
+    "one_token": ("fine_bf16", dict(T=1, H=128, I=128), 256),
+    "k_eq_e": ("coarse_bf16", dict(T=257, H=128, I=192, E=4, k=4), 16),
+    "tile_above_T": ("coarse_bf16", dict(T=100, H=128, I=128, E=8, k=3), 101),
+    "k7_t24": ("vfine_bf16", dict(T=129, H=128, I=256, E=32, k=7), 24),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_rounded_small_full_compare(case):
+    base, ch, tile = CASES[case]
+    wl = W.scaled(W.WORKLOADS[base], **ch)
+    log(f"rounded small {case}: {wl} tile={tile}")
+    inp = W.make_inputs(wl)
+    out, mid, ids0_gpu, _ = _run(inp, tile)
+    x, wr = inp.f32("x"), inp.f32("w_router")
+    ids0, _, l, p = O.route(x, wr, inp.bias, wl.k, wl.renormalize)
+    _check_rounding(mid, ids0_gpu, ids0, l, p, wl.E, tile, wl.renormalize)
+    ref = O.forward_rounded(x, wr, inp.bias, inp.f32("w13"), inp.f32("w2"), wl.k,
+                            wl.renormalize, tile)
+    ey = row_rel_err(host_f64(mid["y"]), ref["Y"])
+    eo = row_rel_err(host_f64(out), ref["out"])
+    log(f"  y err {ey:.3e}  out err {eo:.3e}")
+    assert ey <= TOL_OUT[wl.dtype] and eo <= TOL_OUT[wl.dtype]
+
+
+def test_rounded_tile_one_equals_forward():
+    """B = 1 pools nothing: ids, weights, permutation and output equal moe_forward's."""
+    wl = W.scaled(W.WORKLOADS["skewed_bf16"], T=700, H=256, I=256)
+    inp = W.make_inputs(wl)
+    out_r, mid_r, _, d = _run(inp, 1)
+    out_f, ws_f = B.moe_forward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                                wl.renormalize)
+    torch.cuda.synchronize()
+    mid_f = B.forward_intermediates(ws_f, wl.T, wl.H, wl.I, wl.E, wl.k, B.MOE_DTYPE_BF16)
+    for n in ("ids", "weights", "counts", "offsets", "perm", "inv_perm"):
+        assert torch.equal(mid_r[n], mid_f[n].cpu()), n
+    assert torch.equal(out_r.view(torch.int16), out_f.view(torch.int16))
+
+
+def test_rounded_deterministic_and_events():
+    wl = W.scaled(W.WORKLOADS["fine_bf16"], T=1500, H=256, I=256)
+    inp = W.make_inputs(wl)
+    o1, m1, _, d = _run(inp, 64)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(B.PROFILE_EVENTS_ROUNDED)]
+    for e in ev:
+        e.record()          # creates the HIP event behind the torch object
+    torch.cuda.synchronize()
+    o2, ws2 = B.moe_forward_rounded(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                                    wl.renormalize, 64, events=ev)
+    torch.cuda.synchronize()
+    m2 = B.forward_intermediates(ws2, wl.T, wl.H, wl.I, wl.E, wl.k, B.MOE_DTYPE_BF16)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for n in ("ids", "weights", "perm", "inv_perm", "offsets"):
+        assert torch.equal(m1[n], m2[n].cpu()), n
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    log("  stage ms " + " ".join(f"{s}={t:.3f}" for s, t in zip(B.PROFILE_STAGES_ROUNDED, times)))
+    assert all(t >= 0 for t in times)
+
+
+def test_rounded_pool_beyond_lds_state():
+    """More pool tokens than the LDS state holds: the hand-out keeps its state
+    in the workspace.  Every rounding decision is still compared exactly."""
+    wl = W.scaled(W.WORKLOADS["vfine_bf16"], T=20000, H=128, I=64)
+    tile = 512
+    inp = W.make_inputs(wl)
+    log(f"rounded large pool: {wl} tile={tile}")
+    out, mid, ids0_gpu, _ = _run(inp, tile)
+    x, wr = inp.f32("x"), inp.f32("w_router")
+    ids0, w0, l, p = O.route(x, wr, inp.bias, wl.k, wl.renormalize)
+    keep, pool = O._round_pool(ids0, wl.E, tile)
+    n_tok = len({f // wl.k for f in pool})
+    log(f"  pool: {len(pool)} assignments over {n_tok} tokens")
+    assert n_tok > LDS_POOL_TOKENS
+    new, nw, oo, op = _check_rounding(mid, ids0_gpu, ids0, l, p, wl.E, tile, wl.renormalize)
+    toks = sample_tokens(wl.T, new, oo, op, wl.k, cap=128)
+    want = O.forward_tokens(inp.x, new[toks], nw[toks], inp.w13, inp.w2, toks,
+                            to_f32=W.bf16_bits_to_f32)
+    err = row_rel_err(host_f64(out[torch.tensor(toks, device=out.device)]), want)
+    log(f"  sampled out err {err:.3e}")
+    assert err <= TOL_OUT["bf16"]
+
+
+@pytest.mark.parametrize("name", ["coarse_bf16", "fine_bf16", "vfine_bf16", "skewed_bf16"])
+def test_rounded_full_size(name):
+    """Full-size workloads, rounding to the grouped GEMM's row tile (the launch
+    configuration the benchmark times with --round)."""
+    wl = W.WORKLOADS[name]
+    tile = B.gemm_tile_rows(_dt(wl))
+    log(f"rounded full {name}: generating")
+    inp = W.make_inputs(wl)
+    log("  gpu forward")
+    out, mid, ids0_gpu, d = _run(inp, tile)
+    del d
+    log("  oracle routing and rounding")
+    ids0, _, l, p = O.route(inp.f32("x"), inp.f32("w_router"), inp.bias, wl.k, wl.renormalize)
+    new, nw, oo, op = _check_rounding(mid, ids0_gpu, ids0, l, p, wl.E, tile, wl.renormalize)
+    del l, p
+    toks = sample_tokens(wl.T, new, oo, op, wl.k, cap=160)
+    log(f"  oracle on {len(toks)} sampled tokens")
+    want = O.forward_tokens(inp.x, new[toks], nw[toks], inp.w13, inp.w2, toks,
+                            to_f32=W.bf16_bits_to_f32)
+    err = row_rel_err(host_f64(out[torch.tensor(toks, device=out.device)]), want)
+    log(f"  sampled out err {err:.3e}")
+    assert err <= TOL_OUT["bf16"]
