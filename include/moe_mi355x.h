@@ -162,7 +162,9 @@ int moe_combine(const void* y, const int32_t* inv_perm,
 /*
  * moe_forward -- the whole block: route, permute, grouped SwiGLU, combine.
  * The grouped GEMM reads the rows of x through the permutation directly (no
- * x_perm copy).  Every intermediate is left in the workspace at the offsets
+ * x_perm copy), and its down projection writes each output row straight back
+ * to token order (row perm[r]), so the combine reads every token's k rows
+ * contiguously.  Every intermediate is left in the workspace at the offsets
  * moe_forward_workspace_layout() reports, so each step can be inspected.
  *
  *   x [T,H], w_router [E,H], router_bias [E] fp32 or NULL, w13 [E,2I,H],
@@ -207,7 +209,9 @@ typedef struct moe_forward_layout {
     size_t perm;            /* [T*k] int32 */
     size_t inv_perm;        /* [T*k] int32 */
     size_t h;               /* [T*k,I] dtype */
-    size_t y;               /* [T*k,H] dtype */
+    size_t y;               /* [T*k,H] dtype, token order: row t*k+j is slot (t,j)'s
+                               expert output (the down GEMM writes row r of the
+                               expert-sorted order to row perm[r]) */
     size_t scratch;         /* internal */
     size_t total;           /* == moe_workspace_size(MOE_ENTRY_FORWARD, ...) */
 } moe_forward_layout;

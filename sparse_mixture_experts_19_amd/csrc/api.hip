@@ -516,9 +516,10 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   g.C = w + L.h; g.N = I; g.K = H;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
   MOE_CHECK(mark());
+  // y rows go straight to token order (row t*k+j), so the combine streams them
   g.A = w + L.h; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
-  g.C = w + L.y; g.N = H; g.K = I;
+  g.C = w + L.y; g.N = H; g.K = I; g.scatter = perm;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_down(g, s) : moe::launch_gemm_f32_down(g, s));
   MOE_CHECK(mark());
   const void* ys = nullptr;
@@ -547,7 +548,7 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
     ys = w + SL.y_shared;
     MOE_CHECK(mark());
   }
-  MOE_HIP(moe::launch_combine(w + L.y, inv, wts, T, H, k, bf16, out, s, ys));
+  MOE_HIP(moe::launch_combine(w + L.y, nullptr, wts, T, H, k, bf16, out, s, ys));
   MOE_CHECK(mark());
   if (next_event != n_events)
     return fail(MOE_ERR_UNSUPPORTED, "internal: %d stage events recorded, %d expected", next_event,

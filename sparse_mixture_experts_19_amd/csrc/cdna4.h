@@ -44,6 +44,27 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// 4-byte-per-lane variant (global_load_lds_dword): lane i's 4 bytes land at
+// LDS byte address lds + 4 i.
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uintptr_t>(sbase);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const void* s = reinterpret_cast<const void*>(static_cast<uintptr_t>((hi << 32) | lo));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(s), "s"(lds)
+               : "memory", "m0");
+}
+
+// Same with a base already in scalar registers (wave-uniform by construction).
+__device__ __forceinline__ void dma16p(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const void*)p));

@@ -7,7 +7,9 @@
 // outputs of [Qwen3-MoE page] §1 (phase 4) and the scatter back to token
 // order of §2.2.  Each thread owns one 16-byte chunk of one output row, so the
 // k rows are gathered with 128-bit loads, summed in fp32 in slot order and
-// rounded once -- no atomics, bitwise deterministic.  With a shared expert
+// rounded once -- no atomics, bitwise deterministic.  The fused forward has
+// its down GEMM write y already in token order (row t*k+j), passes no inv,
+// and the k rows of a token are then read contiguously.  With a shared expert
 // (moe_forward_shared) its output row is added last, with weight 1.
 #include "moe_internal.h"
 
@@ -30,8 +32,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
     for (int j = 0; j < k; ++j) {
-      int64_t r = inv[t * k + j];
-      r = r < 0 ? 0 : (r >= T * k ? T * k - 1 : r);   // malformed inv_perm stays in bounds
+      int64_t r = t * k + j;
+      if (inv) {
+        r = inv[r];
+        r = r < 0 ? 0 : (r >= T * k ? T * k - 1 : r);   // malformed inv_perm stays in bounds
+      }
       const float wj = w[t * k + j];
       const uint4 q = y[r * chunks + c];
       if constexpr (BF16) {

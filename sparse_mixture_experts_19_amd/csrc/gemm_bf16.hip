@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ uint4 S0[(BM + BN) * 8];
   __shared__ uint4 S1[(BM + BN) * 8];
   __shared__ uint4 STG[4 * 256];        // epilogue staging, 4 KB per wave
+  __shared__ int32_t SROW[2 * 256];     // scattered output rows, by tile parity
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -304,6 +305,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const char* base = t < 8 ? dA : ((SWIGLU && t >= 12) ? dB1 : dB0);
     dma16s(base + ko, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
   };
+  // The three global bases of stage kc, pinned to scalar registers once, so
+  // that each DMA of the stage is one M0 write and the load.
+  struct StageBase {
+    const char *a, *b0, *b1;
+  };
+  auto stage_base = [&](int kc) -> StageBase {
+    const uint64_t ko = static_cast<uint64_t>(kc) * BK * 2;
+    auto pin = [](const char* p) {
+      const uint64_t v = reinterpret_cast<uintptr_t>(p);
+      const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+      const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+      return reinterpret_cast<const char*>(static_cast<uintptr_t>((hi << 32) | lo));
+    };
+    return StageBase{pin(dA + ko), pin(dB0 + ko), pin(SWIGLU ? dB1 + ko : dB0 + ko)};
+  };
+  auto dma_pre = [&](const StageBase& g, uint32_t sb, int t) {
+    const char* base = t < 8 ? g.a : ((SWIGLU && t >= 12) ? g.b1 : g.b0);
+    dma16p(base, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
+  };
 
   f32x16_t acc[4][4];
   struct Frag {
@@ -353,6 +373,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   Item ci;                                   // item whose outputs the MFMAs compute
   int cidx = next_item(0, ci);
   if (cidx < 0) return;
+  // Scattered C rows (down GEMM of the fused forward): the tile's 256
+  // scatter entries are fetched into LDS by one 4-byte DMA per wave when the
+  // tile starts (row 64 w + lane, clamped into the tile), in the buffer of the
+  // tile's parity; the first stage's wait and barrier retire them long before
+  // the epilogue reads them.
+  const bool scat = !SWIGLU && a.scatter != nullptr;
+  int spar = 0;                       // SROW buffer of the tile being multiplied
+  auto load_srows = [&](const Tile& t) {
+    if constexpr (!SWIGLU) {
+      if (scat) {
+        const int m = 64 * wave + lane;
+        const uint32_t off = static_cast<uint32_t>(m < t.rows ? m : t.rows - 1) * 4u;
+        dma4s(a.scatter + t.r0, off, __builtin_amdgcn_readfirstlane(lds_addr(SROW) + spar * 1024 + wave * 256));
+      }
+    }
+  };
+  load_srows(ci.t);
   Item di = ci;                              // item the DMAs fetch
   int didx = cidx, dkc = ci.k0;
   bool dlive = true;
@@ -424,16 +461,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     wait_vmcnt0();                     // stage g+1 (the only DMAs in flight) landed
     lds_barrier();                     // ... everywhere, and stage g is no longer read
     const bool last = ckc == ci.k1 - 1;
-    const bool dnow = dlive;
-    if (dnow) gconv();
+    if (dlive) gconv();
+    // One branch-free step 3.  With nothing left to fetch the DMAs re-read
+    // stage 0 of the last tile into the buffer just freed (valid memory,
+    // never read again); the kernel waits for them before it ends.
+    const StageBase gb = stage_base(dlive ? dkc : 0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch g+2
       mfma1(Fb, t);
       if (t < 8) frag1(Sn, 0, Fa, t);  // stale but harmless when g+1 does not exist
-      if (dnow) dma1(dkc, sbc, t);
+      dma_pre(gb, sbc, t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (dnow) dma_advance();
+    if (dlive) dma_advance();
     if (!last) ++ckc;
     return last;
   };
@@ -489,8 +529,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           const int rr = q * 8 + r;
           const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4));
           const int m = row0 + rr;
+          int64_t crow = ci.t.r0 + m;
+          if constexpr (!SWIGLU) {
+            if (scat) crow = SROW[spar * 256 + (m < ci.t.rows ? m : ci.t.rows - 1)];
+          }
           if (m < ci.t.rows && col0 < N)
-            *reinterpret_cast<uint4*>(Cb + static_cast<int64_t>(ci.t.r0 + m) * N + col0 + c * 8) = v;
+            *reinterpret_cast<uint4*>(Cb + crow * N + col0 + c * 8) = v;
         }
       };
       const int r = lane & 31;
@@ -528,7 +572,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     if (cidx < 0) break;
     ckc = ci.k0;
     zero_acc();
+    spar ^= 1;
+    load_srows(ci.t);
   }
+  wait_vmcnt0();                       // the last stages' DMAs landed before the workgroup ends
 }
 
 // Finish the K-split remainder tiles: sum each tile's partial slots in piece
@@ -574,7 +621,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_fixup_kernel(GemmArgs a) {
     const uint2 lo = pack4_bf16(v[0], v[1], v[2], v[3]);
     const uint2 hi = pack4_bf16(v[4], v[5], v[6], v[7]);
     o.x = lo.x; o.y = lo.y; o.z = hi.x; o.w = hi.y;
-    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(t.r0 + row) * a.N + t.n0 + c8 * 8) = o;
+    const int64_t crow = a.scatter ? a.scatter[t.r0 + row] : t.r0 + row;
+    *reinterpret_cast<uint4*>(C + crow * a.N + t.n0 + c8 * 8) = o;
   }
 }
 

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int m = ty * 4 + i;
       if (m >= rows) continue;
-      float* crow = Cb + static_cast<int64_t>(r0 + m) * N;
+      float* crow = Cb + static_cast<int64_t>(a.scatter ? a.scatter[r0 + m] : r0 + m) * N;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + tx * 4 + j;

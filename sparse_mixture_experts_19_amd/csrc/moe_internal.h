@@ -103,6 +103,7 @@ struct GemmArgs {
   int grid;               // persistent workgroups launched (bf16: a multiple of 8)
   float* partials;        // bf16: fp32 partial sums of K-split tiles, max_pieces x BM x BN
   int max_pieces;         // capacity of partials in tiles (0: tiles are never split)
+  const int32_t* scatter; // null: row r of C is row r; else row r is written to row scatter[r]
 };
 // Partial-sum slots the bf16 GEMMs of an [M rows, H, I, E] expert MLP can use.
 int gemm_bf16_pieces(int64_t M, int H, int I, int E);
@@ -136,6 +137,7 @@ void carve_round(char* base, RoundArgs& a);
 hipError_t launch_token_round(const RoundArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ combine (combine.hip)
+// inv != null: slot (t, j) is row inv[t*k+j] of y; inv == null: row t*k+j.
 hipError_t launch_combine(const void* y, const int32_t* inv, const float* w, int64_t T, int H,
                           int k, bool bf16, void* out, hipStream_t s, const void* ys = nullptr);
 
