@@ -28,7 +28,9 @@ reason in the design notes of the repository):
   * the permutation is stable over the flat assignment index f = t*k + j;
   * the shared expert (optional) is a dense SwiGLU expert over every token
     whose output is added with weight 1 to the routed sum;
-  * token rounding (optional) follows the integer rule in ``token_round``.
+  * token rounding (optional) follows the integer rule in ``token_round``;
+  * MXFP8 (optional): expert GEMMs on e4m3 values with E8M0 block scales of
+    32 along the reduction axis (``mx_quantize``), router unquantized.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (brute force, closed forms, library routines,
@@ -379,6 +381,118 @@ def forward_rounded(x, w_router, bias, w13, w2, k: int, renormalize: bool,
     out = combine(Y, inv, w, T, k)
     return dict(out=out, ids=ids, weights=w, moved=moved, ids_topk=ids0, weights_topk=w0,
                 logits=l, probs=p, counts=counts, offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 expert GEMMs (reduced-precision variant).
+# ---------------------------------------------------------------------------
+# [Hunyuan page] §七.1 says FP8 quantization needs the routing to be
+# re-checked; the reading here keeps the router on the unquantized inputs
+# (so its decisions do not move) and runs the expert GEMMs in the OCP MX
+# format MXFP8: e4m3 elements, one E8M0 (power-of-two) scale per 32
+# consecutive values along the reduction axis.
+
+def _e4m3_values() -> np.ndarray:
+    """Value of every e4m3 code 0..255 (OCP FP8 E4M3: bias 7, no infinities,
+    S.1111.111 is NaN), in float64."""
+    v = np.empty(256)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v[c] = np.nan
+        elif e == 0:
+            v[c] = (-1) ** s * 2.0 ** -6 * (m / 8)
+        else:
+            v[c] = (-1) ** s * 2.0 ** (e - 7) * (1 + m / 8)
+    return v
+
+
+E4M3 = _e4m3_values()
+E4M3_MAX = 448.0
+_POS_CODES = np.array([c for c in range(127)])          # 0x00..0x7E: +0 .. +448, increasing
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Nearest e4m3 code to each value (ties to the even code), saturating at
+    +-448; float64 in, uint8 codes out."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    vals = E4M3[_POS_CODES]
+    hi = np.searchsorted(vals, a, side="left")            # first value >= a
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = _POS_CODES[pick]
+    return (code | np.where(np.signbit(y) & (code != 0), 0x80, 0)).astype(np.uint8)
+
+
+def _mx_exponent(amax) -> np.ndarray:
+    """Shared block exponent floor(log2 amax) - 8 (8 = emax of e4m3), clamped
+    to the E8M0 range [-127, 127]; an all-zero block takes -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    ex = np.where(amax > 0, np.floor(np.log2(safe)) - 8, -127)
+    return np.clip(ex, -127, 127)
+
+
+def mx_quantize(v, block: int = 32):
+    """MXFP8 quantization along the last axis (OCP MX v1.0 §6.3): per block of
+    32 values, shared exponent floor(log2 amax) - 8 (8 = emax of e4m3), clamped
+    to the E8M0 range [-127, 127] (an all-zero block takes -127); elements
+    e4m3(v / 2^exp).  Returns (codes uint8 [..., K], scales uint8 [..., K/32]
+    (biased: exp + 127), dequantized float64)."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    b = v.reshape(v.shape[:-1] + (K // block, block))
+    ex = _mx_exponent(np.abs(b).max(axis=-1))
+    scale = np.ldexp(1.0, ex.astype(np.int64))
+    codes = e4m3_encode(b / scale[..., None])
+    deq = E4M3[codes] * scale[..., None]
+    return (codes.reshape(v.shape), (ex + 127).astype(np.uint8),
+            deq.reshape(v.shape))
+
+
+def mx_dequantize(codes, scales, block: int = 32) -> np.ndarray:
+    codes = np.asarray(codes)
+    K = codes.shape[-1]
+    sc = np.ldexp(1.0, np.asarray(scales).astype(np.int64) - 127)
+    return (E4M3[codes].reshape(codes.shape[:-1] + (K // block, block)) * sc[..., None]).reshape(codes.shape)
+
+
+def expert_mlp_mxfp8(xe, w13q_e, w13s_e, w2q_e, w2s_e) -> np.ndarray:
+    """One expert's SwiGLU MLP on MXFP8 operands: its rows of x and its h are
+    quantized along their reduction axes; products and sums in float64."""
+    xd = mx_quantize(xe)[2]
+    w13 = mx_dequantize(w13q_e, w13s_e)
+    I = w13.shape[0] // 2
+    h = silu(xd @ w13[:I].T) * (xd @ w13[I:].T)
+    hd = mx_quantize(h)[2]
+    return hd @ mx_dequantize(w2q_e, w2s_e).T
+
+
+def forward_mxfp8(x, w_router, bias, w13q, w13s, w2q, w2s, k: int,
+                  renormalize: bool) -> Dict[str, np.ndarray]:
+    """The block with MXFP8 expert GEMMs: routing, permutation and combine as
+    in ``forward``; each expert runs ``expert_mlp_mxfp8`` on its rows.
+    w13q [E,2I,H] / w13s [E,2I,H/32] and w2q [E,H,I] / w2s [E,H,I/32] are
+    the quantized expert weights (``mx_quantize`` of bf16/fp32 weights)."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w13q).shape[0]
+    ids, w, l, p = route(x, w_router, bias, k, renormalize)
+    counts, offsets, perm, inv = permute(ids, E)
+    xp = gather_rows(x, perm, k)
+    Y = np.zeros((xp.shape[0], np.asarray(w2q).shape[1]))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            Y[a:b] = expert_mlp_mxfp8(xp[a:b], w13q[e], w13s[e], w2q[e], w2s[e])
+    out = combine(Y, inv, w, T, k)
+    return dict(out=out, ids=ids, weights=w, logits=l, probs=p, counts=counts,
+                offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
 
 
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],

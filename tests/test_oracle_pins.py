@@ -487,6 +487,112 @@ def pin_forward_rounded_composition():
     assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# MXFP8 (OCP FP8 E4M3 elements, OCP MX v1.0 E8M0 block scales of 32)
+# --------------------------------------------------------------------------
+
+def pin_e4m3_table():
+    """Code values fixed by the OCP FP8 E4M3 definition (bias 7, 3 mantissa
+    bits, no infinities, only S.1111.111 is NaN)."""
+    V = O.E4M3
+    assert V[0x38] == 1.0 and V[0x40] == 2.0 and V[0x30] == 0.5
+    assert V[0x7E] == 448.0 and V[0xFE] == -448.0         # largest normal
+    assert V[0x08] == 2.0 ** -6                            # smallest normal
+    assert V[0x01] == 2.0 ** -9 and V[0x07] == 7 * 2.0 ** -9   # subnormals
+    assert np.isnan(V[0x7F]) and np.isnan(V[0xFF])
+    assert np.isnan(V).sum() == 2
+    assert V[0x80] == 0 and np.signbit(V[0x80])
+    finite = V[:0x7F]
+    assert np.all(np.diff(finite) > 0)                     # codes 0..126 increase
+    assert V[0x39] - V[0x38] == 0.125                      # spacing 2^-3 in [1, 2)
+
+
+def pin_e4m3_encode():
+    V = O.E4M3
+    codes = np.arange(0x7F)
+    assert np.array_equal(O.e4m3_encode(V[codes]), codes)          # exact values map to themselves
+    neg = np.arange(0x81, 0xFF)
+    assert np.array_equal(O.e4m3_encode(V[neg]), neg)
+    # ties go to the even code: 1.0625 sits between 1.0 (0x38) and 1.125 (0x39)
+    assert O.e4m3_encode([1.0625])[0] == 0x38
+    assert O.e4m3_encode([1.1875])[0] == 0x3A                      # between 0x39 and 0x3A
+    assert O.e4m3_encode([-1.0625])[0] == 0xB8
+    assert O.e4m3_encode([2.0 ** -10])[0] == 0x00                  # half the smallest subnormal
+    assert O.e4m3_encode([3 * 2.0 ** -11])[0] == 0x01              # 0.75 of it rounds up
+    assert O.e4m3_encode([1.06])[0] == 0x38 and O.e4m3_encode([1.07])[0] == 0x39
+    # saturation at +-448 (no infinities)
+    assert O.e4m3_encode([449.0, 1e9])[0] == 0x7E and O.e4m3_encode([-1e9])[0] == 0xFE
+    assert O.e4m3_encode([464.0])[0] == 0x7E                       # past the 448/480 midpoint
+    r = np.random.default_rng(40).uniform(-500, 500, 2000)
+    d = V[O.e4m3_encode(r)]
+    order = np.argsort(r)
+    assert np.all(np.diff(d[order]) >= 0)                          # monotone
+    inr = np.abs(r) <= 448
+    assert np.all(np.abs(d - r)[inr] <= np.maximum(np.abs(r), 2.0 ** -6)[inr] * 2.0 ** -4 + 1e-300)
+
+
+def pin_mx_quantize():
+    """Block scale 2^(floor(log2 amax) - 8): a block whose largest magnitude
+    is 2^e stores it as 256 = code 0x78; powers of two scale only the
+    exponents; a zero block stays zero; elements within 2^-4 relative."""
+    v = np.zeros((3, 64))
+    v[0, :32] = np.linspace(-1, 1, 32) * 0.75
+    v[0, 5] = 2.0 ** 3                                 # amax of block 0 = 8
+    v[0, 32:] = np.linspace(0.1, 3.0, 32)              # block 1: amax 3
+    v[1, :] = 1e-3 * np.arange(64)
+    codes, sc, deq = O.mx_quantize(v)
+    assert sc[0, 0] == 127 + 3 - 8 and codes[0, 5] == 0x78
+    assert sc[0, 1] == 127 + 1 - 8                     # floor(log2 3) = 1
+    assert np.all(codes[2] == 0) and np.all(deq[2] == 0) and np.all(sc[2] == 0)
+    c2, s2, d2 = O.mx_quantize(v * 2.0 ** 5)
+    assert np.array_equal(c2, codes) and np.array_equal(s2[:2], sc[:2] + 5)
+    assert np.array_equal(d2, deq * 2.0 ** 5)
+    r = np.random.default_rng(41).standard_normal((16, 256))
+    c, s_, d = O.mx_quantize(r)
+    blocks = np.abs(r).reshape(16, 8, 32)
+    scale = np.ldexp(1.0, s_.astype(int) - 127)[..., None]
+    # elements not saturated and above the subnormal range: within 2^-4 relative
+    ok = (blocks / scale <= 448) & (blocks / scale >= 2.0 ** -6)
+    err = np.abs(d - r).reshape(16, 8, 32)
+    assert np.all(err[ok] <= blocks[ok] * 2.0 ** -4)
+    assert np.array_equal(O.mx_dequantize(c, s_), d)
+
+
+def _mx_case(T=40, H=64, E=4, k=2, I=32, seed=50):
+    x, w, b, w13, w2 = _rand_case(T=T, H=H, E=E, k=k, I=I, seed=seed)
+    q13, s13, _ = O.mx_quantize(w13)
+    q2, s2, _ = O.mx_quantize(w2)
+    return x, w, b, w13, w2, q13, s13, q2, s2
+
+
+def pin_forward_mxfp8():
+    """Per-token brute force (each token through its experts alone: blocks
+    run along each row, so batching must not matter); exact power-of-two
+    scaling through W2 and through the up half of W13; and the quantization
+    error against the unquantized block stays at the fp8 level."""
+    x, w, b, w13, w2, q13, s13, q2, s2 = _mx_case()
+    k = 2
+    r = O.forward_mxfp8(x, w, b, q13, s13, q2, s2, k, True)
+    brute = np.zeros_like(r["out"])
+    for t in range(x.shape[0]):
+        for j in range(k):
+            e = int(r["ids"][t, j])
+            brute[t] += r["weights"][t, j] * O.expert_mlp_mxfp8(x[t:t + 1], q13[e], s13[e], q2[e], s2[e])[0]
+    assert np.allclose(r["out"], brute, rtol=1e-12, atol=1e-12)
+    # W2 * 2^3: identical codes, scales + 3, output exactly * 8
+    r8 = O.forward_mxfp8(x, w, b, q13, s13, q2, s2 + 3, k, True)
+    assert np.array_equal(r8["out"], r["out"] * 8)
+    # up half of W13 * 2^-2: h (and its MX scales) exactly / 4
+    I = q13.shape[1] // 2
+    s13u = s13.copy()
+    s13u[:, I:] -= 2
+    ru = O.forward_mxfp8(x, w, b, q13, s13u, q2, s2, k, True)
+    assert np.array_equal(ru["out"], r["out"] / 4)
+    ref = O.forward(x, w, b, w13, w2, k, True)["out"]
+    rel = np.linalg.norm(r["out"] - ref) / np.linalg.norm(ref)   # 4 operands at 3 mantissa bits
+    assert 1e-3 < rel < 0.15, rel
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
 
 
@@ -619,6 +725,35 @@ def _mut_round_weights_not_renormalised(probs, ids, renormalize):
     return _orig_round_weights(probs, ids, False)
 
 
+_orig_e4m3_encode = O.e4m3_encode
+_orig_mx_exponent = O._mx_exponent
+
+
+def _mut_e4m3_ties_up(y):
+    y = np.asarray(y, dtype=np.float64)
+    c = _orig_e4m3_encode(y).astype(np.int64)
+    # nudge exact midpoints away from zero: round half up in magnitude
+    v = O.E4M3[c & 0x7F]
+    nxt = O.E4M3[np.minimum((c & 0x7F) + 1, 0x7E)]
+    mid = np.abs(np.abs(y) - (v + nxt) / 2) < 1e-300
+    c = np.where(mid & ((c & 0x7F) < 0x7E), c + 1, c)
+    return c.astype(np.uint8)
+
+
+def _mut_e4m3_no_saturation(y):
+    c = _orig_e4m3_encode(y)
+    return np.where(np.abs(np.asarray(y, float)) > 448, np.uint8(0x7F), c).astype(np.uint8)
+
+
+def _mut_mx_emax7(amax):
+    return np.clip(_orig_mx_exponent(amax) + 1, -127, 127)
+
+
+def _mut_mx_no_floor(amax):
+    a = np.asarray(amax, float)
+    return np.where(a > 0, np.clip(np.round(np.log2(np.where(a > 0, a, 1))) - 8, -127, 127), -127)
+
+
 MUTATIONS = {
     "topk ties to the highest index": ("topk_ids", _mut_topk_ties_high),
     "topk slots ascending": ("topk_ids", _mut_topk_ascending_slots),
@@ -639,6 +774,10 @@ MUTATIONS = {
     "rounding ties to the highest id": ("_round_order", _mut_round_ties_high),
     "rounding ignores the token's other slots": ("_round_eligible", _mut_round_any_slot),
     "rounded weights not renormalised": ("_round_weights", _mut_round_weights_not_renormalised),
+    "e4m3 ties away from zero": ("e4m3_encode", _mut_e4m3_ties_up),
+    "e4m3 overflow to NaN": ("e4m3_encode", _mut_e4m3_no_saturation),
+    "MX scale exponent one too large": ("_mx_exponent", _mut_mx_emax7),
+    "MX scale exponent rounded": ("_mx_exponent", _mut_mx_no_floor),
 }
 
 
