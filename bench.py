@@ -29,7 +29,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 BM = 256                       # rows per grouped-GEMM tile (bf16 kernels)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-GEMM_SOURCES = ["sparse_mixture_experts_19_amd/csrc/gemm_bf16.hip",
+GEMM_SOURCES = ["sparse_mixture_experts_19_amd/csrc/gemm_mfma.hip",
                 "sparse_mixture_experts_19_amd/csrc/moe_internal.h"]
 
 

@@ -349,6 +349,98 @@ int moe_forward_rounded_layout(int64_t T, int32_t H, int32_t I, int32_t E,
 int moe_gemm_tile_rows(int32_t dtype);
 
 /*
+ * MXFP8 expert GEMMs
+ * ------------------
+ * [Hunyuan page] §七.1 runs the experts in FP8 and asks for the routing to be
+ * checked again under quantization.  Here the router stays on the bf16
+ * inputs (its decisions are those of moe_forward) and the two expert GEMMs
+ * run on MXFP8 operands, the OCP Microscaling v1.0 format: along the
+ * reduction axis of each row, a block of 32 consecutive values shares one
+ * E8M0 scale 2^e with e = floor(log2 amax) - 8 (8 = largest exponent of
+ * e4m3), clamped to [-127, 127] (-127 for a block of zeros), and each value
+ * is stored as the e4m3 code (bias 7, largest magnitude 448, no infinities)
+ * nearest to value / 2^e, ties to the even code, saturating at +-448; a
+ * value that rounds to zero gets the code of +0.  Scales are stored as the
+ * biased exponent e + 127, one uint8 per block.
+ */
+
+/*
+ * moe_mx_quantize -- MXFP8 codes and scales of a [rows, cols] matrix along
+ * its rows (the format above).
+ *   src     [rows, cols] dtype (bf16 or fp32), device, 16-byte aligned.
+ *   cols    a multiple of 32; rows >= 0 (0: no-op).
+ *   codes   [rows, cols] uint8, device, output, 16-byte aligned.
+ *   scales  [rows, cols/32] uint8, device, output.
+ * The expert weights of moe_forward_mxfp8 are w13 viewed as [E*2I, H] and
+ * w2 as [E*H, I], each quantized along its input dimension.
+ */
+int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, int32_t dtype,
+                    uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_forward_mxfp8 -- the block of moe_forward with MXFP8 expert GEMMs:
+ * routing and permutation as moe_forward (dtype must be MOE_DTYPE_BF16);
+ * x quantized along H; per expert, h = silu(x Wg^T) * (x Wu^T) from the
+ * block-scaled MFMA (products of the dequantized values, fp32 sums),
+ * quantized along I; y = h W2^T (fp32 sums) rounded to bf16; the weighted
+ * combine as moe_forward.
+ *   w13q [E,2I,H] uint8 codes, w13s [E,2I,H/32] uint8 scales;
+ *   w2q [E,H,I] uint8 codes, w2s [E,H,I/32] uint8 scales (moe_mx_quantize
+ *   of the expert weights); codes 16-byte aligned.
+ *   H and I multiples of 128; T*H <= 2^32.
+ *   workspace  moe_forward_mxfp8_layout(...).total bytes, device, 256-byte
+ *              aligned; afterwards it holds the intermediates at the layout's
+ *              offsets (y in token order: row t*k+j).
+ * Other arguments, limits and results as moe_forward.
+ */
+int moe_forward_mxfp8(const void* x, const void* w_router,
+                      const float* router_bias, const uint8_t* w13q,
+                      const uint8_t* w13s, const uint8_t* w2q,
+                      const uint8_t* w2s, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t k, int32_t dtype,
+                      int32_t renormalize, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward_mxfp8_profiled -- moe_forward_mxfp8 recording caller-created
+ * HIP events around its stages (as moe_forward_profiled), n_events ==
+ * MOE_PROFILE_EVENTS_MXFP8: 0 router, 1 permutation, 2 quantization of x,
+ * 3 tile schedule, 4 gate/up GEMM (with the quantization of h), 5 down GEMM,
+ * 6 combine.
+ */
+#define MOE_PROFILE_EVENTS_MXFP8 8
+int moe_forward_mxfp8_profiled(const void* x, const void* w_router,
+                               const float* router_bias, const uint8_t* w13q,
+                               const uint8_t* w13s, const uint8_t* w2q,
+                               const uint8_t* w2s, int64_t T, int32_t H,
+                               int32_t I, int32_t E, int32_t k, int32_t dtype,
+                               int32_t renormalize, void* out, void* workspace,
+                               size_t workspace_bytes, void* const* events,
+                               int32_t n_events, void* stream);
+
+/* Byte offsets of the moe_forward_mxfp8 workspace regions (M = T*k). */
+typedef struct moe_mxfp8_layout {
+    size_t topk_ids;       /* [T,k] int32 */
+    size_t topk_weights;   /* [T,k] fp32 */
+    size_t expert_counts;  /* [E] int32 */
+    size_t expert_offsets; /* [E+1] int32 */
+    size_t perm;           /* [M] int32 */
+    size_t inv_perm;       /* [M] int32 */
+    size_t x_codes;        /* [T,H] uint8: x quantized along H */
+    size_t x_scales;       /* [T,H/32] uint8 */
+    size_t h_codes;        /* [M,I] uint8: h of the expert-sorted rows */
+    size_t h_scales;       /* [M,I/32] uint8 */
+    size_t y;              /* [M,H] bf16: expert outputs, row t*k+j */
+    size_t scratch;        /* kernel scratch */
+    size_t total;          /* bytes of the whole workspace */
+} moe_mxfp8_layout;
+
+/* Host-only.  Fills *layout; validates the sizes as moe_forward_mxfp8. */
+int moe_forward_mxfp8_layout(int64_t T, int32_t H, int32_t I, int32_t E,
+                             int32_t k, int32_t dtype,
+                             moe_mxfp8_layout* layout);
+
+/*
  * Host-only.  Workspace bytes needed by `entry` (a moe_entry) for these
  * sizes, written to *bytes (host pointer).  For MOE_ENTRY_GROUPED_GEMM pass
  * T = M and k = 1.  Sizes that the entry ignores may be given as 1.

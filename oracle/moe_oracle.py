@@ -462,14 +462,21 @@ def mx_dequantize(codes, scales, block: int = 32) -> np.ndarray:
     return (E4M3[codes].reshape(codes.shape[:-1] + (K // block, block)) * sc[..., None]).reshape(codes.shape)
 
 
-def expert_mlp_mxfp8(xe, w13q_e, w13s_e, w2q_e, w2s_e) -> np.ndarray:
-    """One expert's SwiGLU MLP on MXFP8 operands: its rows of x and its h are
-    quantized along their reduction axes; products and sums in float64."""
+def expert_h_mxfp8(xe, w13q_e, w13s_e):
+    """One expert's h = silu(x Wg^T) * (x Wu^T) on MXFP8 operands (its rows of
+    x quantized along H; products and sums in float64), quantized along I:
+    (codes, scales, dequantized) as ``mx_quantize``, then h itself."""
     xd = mx_quantize(xe)[2]
     w13 = mx_dequantize(w13q_e, w13s_e)
     I = w13.shape[0] // 2
     h = silu(xd @ w13[:I].T) * (xd @ w13[I:].T)
-    hd = mx_quantize(h)[2]
+    return mx_quantize(h) + (h,)
+
+
+def expert_mlp_mxfp8(xe, w13q_e, w13s_e, w2q_e, w2s_e) -> np.ndarray:
+    """One expert's SwiGLU MLP on MXFP8 operands: its rows of x and its h are
+    quantized along their reduction axes; products and sums in float64."""
+    hd = expert_h_mxfp8(xe, w13q_e, w13s_e)[2]
     return hd @ mx_dequantize(w2q_e, w2s_e).T
 
 
@@ -478,21 +485,29 @@ def forward_mxfp8(x, w_router, bias, w13q, w13s, w2q, w2s, k: int,
     """The block with MXFP8 expert GEMMs: routing, permutation and combine as
     in ``forward``; each expert runs ``expert_mlp_mxfp8`` on its rows.
     w13q [E,2I,H] / w13s [E,2I,H/32] and w2q [E,H,I] / w2s [E,H,I/32] are
-    the quantized expert weights (``mx_quantize`` of bf16/fp32 weights)."""
+    the quantized expert weights (``mx_quantize`` of bf16/fp32 weights).
+    Hq / Hs are the codes and scales of h and H is h before quantization,
+    row r for permuted row r."""
     x = np.asarray(x)
     T = x.shape[0]
-    E = np.asarray(w13q).shape[0]
+    E, I2 = np.asarray(w13q).shape[:2]
+    I = I2 // 2
     ids, w, l, p = route(x, w_router, bias, k, renormalize)
     counts, offsets, perm, inv = permute(ids, E)
     xp = gather_rows(x, perm, k)
-    Y = np.zeros((xp.shape[0], np.asarray(w2q).shape[1]))
+    M = xp.shape[0]
+    Y = np.zeros((M, np.asarray(w2q).shape[1]))
+    Hq = np.zeros((M, I), dtype=np.uint8)
+    Hs = np.zeros((M, I // 32), dtype=np.uint8)
+    Hf = np.zeros((M, I))
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
-            Y[a:b] = expert_mlp_mxfp8(xp[a:b], w13q[e], w13s[e], w2q[e], w2s[e])
+            Hq[a:b], Hs[a:b], hd, Hf[a:b] = expert_h_mxfp8(xp[a:b], w13q[e], w13s[e])
+            Y[a:b] = hd @ mx_dequantize(w2q[e], w2s[e]).T
     out = combine(Y, inv, w, T, k)
     return dict(out=out, ids=ids, weights=w, logits=l, probs=p, counts=counts,
-                offsets=offsets, perm=perm, inv_perm=inv, Y=Y)
+                offsets=offsets, perm=perm, inv_perm=inv, Y=Y, Hq=Hq, Hs=Hs, H=Hf)
 
 
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],

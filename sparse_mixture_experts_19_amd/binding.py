@@ -39,6 +39,12 @@ class SharedLayout(ctypes.Structure):
         "h_shared", "y_shared", "scratch", "total")]
 
 
+class Mxfp8Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "topk_ids", "topk_weights", "expert_counts", "expert_offsets", "perm", "inv_perm",
+        "x_codes", "x_scales", "h_codes", "h_scales", "y", "scratch", "total")]
+
+
 _SIGS = {
     "moe_route": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
     "moe_permute": [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
@@ -53,6 +59,10 @@ _SIGS = {
     "moe_forward_rounded_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
     "moe_forward_rounded_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_gemm_tile_rows": [_c_i32],
+    "moe_mx_quantize": [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp],
+    "moe_forward_mxfp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
+    "moe_forward_mxfp8_profiled": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_forward_mxfp8_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(Mxfp8Layout)],
     "moe_workspace_size": [_c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_forward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_status_string": [_c_i32],
@@ -359,4 +369,81 @@ def forward_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: i
         inv_perm=view(L.inv_perm, M, torch.int32, 4, (M,)),
         h=view(L.h, M * I, tdt, eb, (M, I)),
         y=view(L.y, M * H, tdt, eb, (M, H)),
+    )
+
+
+def mx_quantize(src, codes=None, scales=None):
+    """MXFP8 codes [..., C] and E8M0 scales [..., C/32] (uint8) of ``src`` (bf16 or
+    fp32, last dimension C a multiple of 32) along its last dimension."""
+    C = src.shape[-1]
+    rows = src.numel() // C if C else 0
+    dev = src.device
+    if codes is None:
+        codes = torch.empty(src.shape, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(tuple(src.shape[:-1]) + (C // 32,), dtype=torch.uint8, device=dev)
+    _check(lib().moe_mx_quantize(_ptr(src), rows, C, _dtype_code(src.dtype), _ptr(codes),
+                                 _ptr(scales), _stream(dev)))
+    return codes, scales
+
+
+def mxfp8_layout(T: int, H: int, I: int, E: int, k: int,
+                 dtype: int = MOE_DTYPE_BF16) -> Mxfp8Layout:
+    L = Mxfp8Layout()
+    _check(lib().moe_forward_mxfp8_layout(T, H, I, E, k, dtype, ctypes.byref(L)))
+    return L
+
+
+PROFILE_EVENTS_MXFP8 = 8
+PROFILE_STAGES_MXFP8 = ("route", "permute", "quantize_x", "schedule", "gemm_gate_up_swiglu",
+                        "gemm_down", "combine")
+
+
+def moe_forward_mxfp8(x, w_router, router_bias, w13q, w13s, w2q, w2s, k: int,
+                      renormalize: bool, out=None, workspace=None, events=None):
+    """The MoE block with MXFP8 expert GEMMs (weights from ``mx_quantize``).
+    Returns (out, workspace); ``mxfp8_intermediates`` reads the workspace.  With
+    ``events`` (8 timing events) the stages are recorded as PROFILE_STAGES_MXFP8."""
+    T, H = x.shape
+    E, I2, _ = w13q.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    ws = _workspace(mxfp8_layout(T, H, I, E, k, dt).total, dev, workspace)
+    args = [_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13q), _ptr(w13s), _ptr(w2q),
+            _ptr(w2s), T, H, I, E, k, dt, int(bool(renormalize)), _ptr(out), _ptr(ws),
+            ws.numel() * ws.element_size()]
+    if events is None:
+        _check(lib().moe_forward_mxfp8(*args, _stream(dev)))
+    else:
+        if len(events) != PROFILE_EVENTS_MXFP8:
+            raise ValueError(f"need {PROFILE_EVENTS_MXFP8} events")
+        handles = (ctypes.c_void_p * PROFILE_EVENTS_MXFP8)(*[ev.cuda_event for ev in events])
+        _check(lib().moe_forward_mxfp8_profiled(*args, handles, PROFILE_EVENTS_MXFP8,
+                                                _stream(dev)))
+    return out, ws
+
+
+def mxfp8_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int):
+    """Typed views of the intermediates moe_forward_mxfp8 leaves in its workspace."""
+    L = mxfp8_layout(T, H, I, E, k)
+    M = T * k
+
+    def view(off, n, dt, esz, shape):
+        return ws[off:off + n * esz].view(dt).view(shape)
+
+    return dict(
+        ids=view(L.topk_ids, M, torch.int32, 4, (T, k)),
+        weights=view(L.topk_weights, M, torch.float32, 4, (T, k)),
+        counts=view(L.expert_counts, E, torch.int32, 4, (E,)),
+        offsets=view(L.expert_offsets, E + 1, torch.int32, 4, (E + 1,)),
+        perm=view(L.perm, M, torch.int32, 4, (M,)),
+        inv_perm=view(L.inv_perm, M, torch.int32, 4, (M,)),
+        x_codes=view(L.x_codes, T * H, torch.uint8, 1, (T, H)),
+        x_scales=view(L.x_scales, T * H // 32, torch.uint8, 1, (T, H // 32)),
+        h_codes=view(L.h_codes, M * I, torch.uint8, 1, (M, I)),
+        h_scales=view(L.h_scales, M * I // 32, torch.uint8, 1, (M, I // 32)),
+        y=view(L.y, M * H, torch.bfloat16, 2, (M, H)),
     )

@@ -115,7 +115,7 @@ size_t gemm_prefix_bytes(int E) { return moe::align_up(static_cast<size_t>(E + 1
 size_t gemm_scratch(int64_t M, int H, int I, int E, int dtype) {
   size_t b = gemm_prefix_bytes(E);
   if (dtype == MOE_DTYPE_BF16)
-    b += static_cast<size_t>(moe::gemm_bf16_pieces(M, H, I, E)) * moe::kGemmBM * moe::kGemmBN * 4;
+    b += static_cast<size_t>(moe::gemm_pieces(M, H, I, E, false)) * moe::kGemmBM * moe::kGemmBN * 4;
   return b;
 }
 
@@ -225,7 +225,7 @@ int run_experts(const void* a_ptr, int64_t a_rows, const int32_t* gather, int ga
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = a_rows;
   if (bf16) {
     g.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(prefix) + gemm_prefix_bytes(E));
-    g.max_pieces = moe::gemm_bf16_pieces(M, H, I, E);
+    g.max_pieces = moe::gemm_pieces(M, H, I, E, false);
     g.grid = cu >= 8 ? cu / 8 * 8 : 8;
   } else {
     g.grid = cu * 2;
@@ -255,7 +255,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 102; }
+int moe_version(void) { return 103; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -503,10 +503,10 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   g.grid = bf16 ? (cu >= 8 ? cu / 8 * 8 : 8) : cu * 2;
   if (bf16) {
     g.partials = reinterpret_cast<float*>(w + L.scratch + gemm_prefix_bytes(E));
-    g.max_pieces = moe::gemm_bf16_pieces(M, H, I, E);
+    g.max_pieces = moe::gemm_pieces(M, H, I, E, false);
   }
   g.A = x; g.gather = perm; g.gather_div = k;
-  if (bf16 && !moe::gemm_bf16_gather_fits(T, H)) {
+  if (bf16 && !moe::gemm_gather_fits(T, H, 2)) {
     // x spans more than 2^32 bytes: gather its rows into the (not yet used)
     // down-projection output buffer, which has the same [M, H] shape
     MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, 2, w + L.y, s));
@@ -535,7 +535,7 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
     d.E = 1; d.offsets = soff; d.prefix = spre; d.I = Is; d.M = T; d.a_rows = T; d.grid = g.grid;
     if (bf16) {
       d.partials = reinterpret_cast<float*>(ss + 256 + gemm_prefix_bytes(1));
-      d.max_pieces = moe::gemm_bf16_pieces(T, H, Is, 1);
+      d.max_pieces = moe::gemm_pieces(T, H, Is, 1, false);
     }
     d.A = x; d.gather = nullptr; d.gather_div = 1;
     d.B = ws13; d.b_stride = static_cast<int64_t>(2) * Is * H;
@@ -650,6 +650,182 @@ int moe_forward_rounded_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32
   if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
   MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
   *layout = rounded_layout(T, H, I, E, k, dtype);
+  return ok();
+}
+
+int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, int32_t dtype, uint8_t* codes,
+                    uint8_t* scales, void* stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (cols <= 0 || cols % moe::kMxBlock)
+    return fail(MOE_ERR_INVALID_ARG, "cols must be a positive multiple of 32 (got %d)", cols);
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (rows * static_cast<int64_t>(cols) / 8 / 256 > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "rows*cols (%lld) too large", (long long)(rows * cols));
+  if (rows == 0) return ok();
+  MOE_CHECK(need_ptr(src, "src", 16));
+  MOE_CHECK(need_ptr(codes, "codes", 16));
+  MOE_CHECK(need_ptr(scales, "scales", 1));
+  MOE_CHECK(current_device(nullptr, nullptr));
+  MOE_HIP(moe::launch_mx_quantize(src, dtype == MOE_DTYPE_BF16, rows, cols, codes, scales,
+                                  static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_mxfp8(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t dtype) {
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  if (dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward_mxfp8 needs dtype MOE_DTYPE_BF16");
+  if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "H (%d) must be a multiple of 128", H);
+  if (I % 128) return fail(MOE_ERR_UNSUPPORTED, "I (%d) must be a multiple of 128", I);
+  if (!moe::gemm_gather_fits(T, H, 1))
+    return fail(MOE_ERR_UNSUPPORTED, "T*H (%lld) exceeds 2^32", (long long)(T * H));
+  return MOE_OK;
+}
+
+moe_mxfp8_layout mxfp8_layout(int64_t T, int H, int I, int E, int k) {
+  const size_t M = static_cast<size_t>(T) * k;
+  Carver c;
+  moe_mxfp8_layout L;
+  L.topk_ids = c.take(M * 4);
+  L.topk_weights = c.take(M * 4);
+  L.expert_counts = c.take(static_cast<size_t>(E) * 4);
+  L.expert_offsets = c.take(static_cast<size_t>(E + 1) * 4);
+  L.perm = c.take(M * 4);
+  L.inv_perm = c.take(M * 4);
+  L.x_codes = c.take(static_cast<size_t>(T) * H);
+  L.x_scales = c.take(static_cast<size_t>(T) * H / 32);
+  L.h_codes = c.take(M * I);
+  L.h_scales = c.take(M * I / 32);
+  L.y = c.take(M * H * 2);
+  const size_t rs = moe::route_scratch_bytes(T, H, E, true);
+  const size_t ps = moe::permute_scratch_bytes(static_cast<int64_t>(M), E);
+  const size_t gs = gemm_prefix_bytes(E) +
+                    static_cast<size_t>(moe::gemm_pieces(static_cast<int64_t>(M), H, I, E, true)) *
+                        moe::kGemmBM * moe::kGemmBN * 4;
+  L.scratch = c.take(gs + (rs > ps ? rs : ps));
+  L.total = c.o;
+  return L;
+}
+
+int forward_mxfp8_impl(const void* x, const void* w_router, const float* router_bias,
+                       const uint8_t* w13q, const uint8_t* w13s, const uint8_t* w2q,
+                       const uint8_t* w2s, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                       int32_t dtype, int32_t renormalize, void* out, void* workspace,
+                       size_t workspace_bytes, void* const* events, hipStream_t s) {
+  MOE_CHECK(check_mxfp8(T, H, I, E, k, dtype));
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(x, "x", 16));
+  MOE_CHECK(need_ptr(w_router, "w_router", 16));
+  if (router_bias) MOE_CHECK(need_ptr(router_bias, "router_bias", 4));
+  MOE_CHECK(need_ptr(w13q, "w13q", 16));
+  MOE_CHECK(need_ptr(w13s, "w13s", 4));
+  MOE_CHECK(need_ptr(w2q, "w2q", 16));
+  MOE_CHECK(need_ptr(w2s, "w2s", 4));
+  MOE_CHECK(need_ptr(out, "out", 16));
+  const moe_mxfp8_layout L = mxfp8_layout(T, H, I, E, k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", L.total,
+                workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 256));
+  if (events)
+    for (int i = 0; i < MOE_PROFILE_EVENTS_MXFP8; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  int cu = 0;
+  MOE_CHECK(current_device(nullptr, &cu));
+  char* w = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(w + L.topk_ids);
+  float* wts = reinterpret_cast<float*>(w + L.topk_weights);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + L.expert_counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.expert_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(w + L.inv_perm);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.x_codes);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(w + L.x_scales);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.scratch);
+  const int64_t M = T * k;
+  const int pieces = moe::gemm_pieces(M, H, I, E, true);
+  char* shared = w + L.scratch + gemm_prefix_bytes(E) +
+                 static_cast<size_t>(pieces) * moe::kGemmBM * moe::kGemmBN * 4;
+  int next_event = 0;
+  auto mark = [&]() -> int {
+    if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[next_event]), s));
+    ++next_event;
+    return MOE_OK;
+  };
+
+  MOE_CHECK(mark());
+  MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared, s));
+  MOE_CHECK(mark());
+  MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_mx_quantize(x, true, T, H, xq, xs, s));
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
+  MOE_CHECK(mark());
+  moe::GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M;
+  g.grid = cu >= 8 ? cu / 8 * 8 : 8;
+  g.partials = reinterpret_cast<float*>(w + L.scratch + gemm_prefix_bytes(E));
+  g.max_pieces = pieces;
+  // gate/up: rows of x gathered through the permutation, h quantized on the way out
+  g.A = xq; g.a_scale = xs; g.gather = perm; g.gather_div = k; g.a_rows = T;
+  g.B = w13q; g.b_scale = w13s; g.b_stride = static_cast<int64_t>(2) * I * H;
+  g.C = w + L.h_codes; g.c_scale = reinterpret_cast<uint8_t*>(w + L.h_scales); g.N = I; g.K = H;
+  MOE_HIP(moe::launch_gemm_mx_swiglu(g, s));
+  MOE_CHECK(mark());
+  // down: y rows go straight to token order (row t*k+j), so the combine streams them
+  g.A = w + L.h_codes; g.a_scale = reinterpret_cast<uint8_t*>(w + L.h_scales);
+  g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
+  g.B = w2q; g.b_scale = w2s; g.b_stride = static_cast<int64_t>(H) * I;
+  g.C = w + L.y; g.c_scale = nullptr; g.N = H; g.K = I; g.scatter = perm;
+  MOE_HIP(moe::launch_gemm_mx_down(g, s));
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_combine(w + L.y, nullptr, wts, T, H, k, true, out, s));
+  MOE_CHECK(mark());
+  if (next_event != MOE_PROFILE_EVENTS_MXFP8)
+    return fail(MOE_ERR_UNSUPPORTED, "internal: %d stage events recorded, %d expected", next_event,
+                MOE_PROFILE_EVENTS_MXFP8);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_mxfp8(const void* x, const void* w_router, const float* router_bias,
+                      const uint8_t* w13q, const uint8_t* w13s, const uint8_t* w2q,
+                      const uint8_t* w2s, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                      int32_t dtype, int32_t renormalize, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return forward_mxfp8_impl(x, w_router, router_bias, w13q, w13s, w2q, w2s, T, H, I, E, k, dtype,
+                            renormalize, out, workspace, workspace_bytes, nullptr,
+                            static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_mxfp8_profiled(const void* x, const void* w_router, const float* router_bias,
+                               const uint8_t* w13q, const uint8_t* w13s, const uint8_t* w2q,
+                               const uint8_t* w2s, int64_t T, int32_t H, int32_t I, int32_t E,
+                               int32_t k, int32_t dtype, int32_t renormalize, void* out,
+                               void* workspace, size_t workspace_bytes, void* const* events,
+                               int32_t n_events, void* stream) {
+  if (!events || n_events != MOE_PROFILE_EVENTS_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_MXFP8 (%d) handles",
+                MOE_PROFILE_EVENTS_MXFP8);
+  return forward_mxfp8_impl(x, w_router, router_bias, w13q, w13s, w2q, w2s, T, H, I, E, k, dtype,
+                            renormalize, out, workspace, workspace_bytes, events,
+                            static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_mxfp8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t dtype,
+                             moe_mxfp8_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  MOE_CHECK(check_mxfp8(T, H, I, E, k, dtype));
+  *layout = mxfp8_layout(T, H, I, E, k);
   return ok();
 }
 

@@ -65,6 +65,46 @@ __device__ __forceinline__ void dma16p(const void* sbase, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// 4-byte variant with a base already in scalar registers.
+__device__ __forceinline__ void dma4p(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// ------------------------------------------------------------------ MXFP8
+// OCP MX v1.0 MXFP8: e4m3 elements (bias 7, largest magnitude 448, no
+// infinities) sharing one E8M0 scale 2^e per block of 32 values.
+
+// Shared exponent of a block from its largest magnitude: floor(log2 amax) - 8
+// (8 = largest exponent of e4m3), clamped to the E8M0 range; a block of zeros
+// or of fp32 subnormals takes -127.  Read off the fp32 exponent field.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  const int be = static_cast<int>(__float_as_uint(amax) >> 23) & 255;
+  return be < 8 ? -127 : be - 135;
+}
+
+// 2^-e as fp32, for a block exponent e in [-127, 120]
+__device__ __forceinline__ float mx_inv_scale(int e) {
+  return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+
+// e4m3 codes of a*s .. d*s, packed in that order from the low byte: values
+// saturate at +-448 and round to the nearest code, ties to the even code
+// (v_cvt_pk_fp8_f32 under the default round-to-nearest-even mode); a value
+// that rounds to zero gets the code of +0.  s is a power of two, so every
+// product is exact (or far below the smallest e4m3 code).
+__device__ __forceinline__ uint32_t mx_encode4(float a, float b, float c, float d, float s) {
+  auto sat = [](float v) { return __builtin_amdgcn_fmed3f(v, -448.f, 448.f); };
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a * s), sat(b * s), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c * s), sat(d * s), r, true);
+  const uint32_t u = static_cast<uint32_t>(r);
+  // 0x80 in every byte whose magnitude bits are nonzero (no carry crosses a byte)
+  const uint32_t nz = ((u & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+  return u & (nz | 0x7F7F7F7Fu);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const void*)p));

@@ -1,8 +1,11 @@
-// Ragged grouped GEMMs of the expert SwiGLU MLPs on bf16 MFMA (gfx950).
+// Ragged grouped GEMMs of the expert SwiGLU MLPs on the MFMA units (gfx950),
+// with bf16 operands or MXFP8 operands (e4m3 elements, one E8M0 scale per 32
+// values along K).
 //
 // Page legend:
 //   [Qwen3-MoE page] "稀疏混合专家系统的并行化改造：Qwen3MoeSparseMoeBlock性能优化实战"
 //   [SonicMoE page]  "SonicMoE与传统MoE架构对比：Token舍入技术如何实现训练效率跃升"
+//   [Hunyuan page]   "混合专家架构大模型Hunyuan-Large：原理剖析与实现机制"
 //
 // [Qwen3-MoE page] §2.1 computes all experts in one batched launch over the
 // stacked expert weights, scheduled over the compute units; the rows of each
@@ -40,6 +43,26 @@
 // operand and the token rows as B, so each lane ends with 4 consecutive
 // output columns of one row: the epilogue applies silu(g)*u in registers,
 // stages bf16 rows in LDS and writes whole 128-byte lines.
+//
+// MXFP8 ([Hunyuan page] §七.1 runs the experts in FP8; the format is OCP
+// MXFP8): the same tiles, stages and DMA plan over e4m3 bytes, so a 128-byte
+// stage row holds 128 K values, multiplied in two K64 steps of the
+// block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4.  That instruction takes
+// 32 bytes per lane -- row lane % 32, bytes 0..15 holding K 16 (lane / 32) +
+// 0..15 of the step and bytes 16..31 holding K 32 + 16 (lane / 32) + 0..15,
+// exactly the 16-byte chunks of two bf16 K16 steps -- and per operand one
+// E8M0 scale per lane, for row lane % 32 and the K values 32 (lane / 32) ..
+// +31 of the step, taken from a byte of a 32-bit register that an immediate
+// selects.  The four scale bytes a stage covers of a row form one 32-bit
+// word; the words of the stage's 256 token rows and 256 weight rows are
+// fetched into LDS by two 4-byte DMAs per wave next to the data, and each
+// lane shifts the words it reads by 8 (lane / 32) bits, so that K64 step s
+// takes byte 2 s.  The SwiGLU epilogue quantizes h along its columns (the K
+// of the down GEMM): the 32 columns of a block of one token row sit in lanes
+// l and l + 32 of one 32x32 result tile, which agree on the block's largest
+// magnitude through one lane exchange.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "cdna4.h"
 
@@ -49,7 +72,15 @@ namespace {
 constexpr int BM = kGemmBM;   // 256 rows
 constexpr int BN = kGemmBN;   // 256 weight rows (swiglu: 128 gate + 128 up)
 constexpr int BK = kGemmBK;   // 64
+constexpr int kStageBytes = 128;  // bytes of a row per K stage (both formats)
 constexpr int kGroupM = 8;    // m-tiles walked together inside an expert
+
+// K values per stage: 64 bf16 or 128 e4m3
+template <bool MX>
+constexpr int stage_k() { return MX ? 2 * BK : BK; }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int swz(int r, int c) { return swz128(r, c); }
 
@@ -146,14 +177,16 @@ __device__ __forceinline__ Split split_work(int total, int G, int nk, int max_pi
   return sp;
 }
 
-template <bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+template <bool MX, bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // two stage buffers as distinct arrays (each holds the A rows then the B
-  // rows of one 64-wide K stage)
+  // rows of one 128-byte K stage)
   __shared__ uint4 S0[(BM + BN) * 8];
   __shared__ uint4 S1[(BM + BN) * 8];
   __shared__ uint4 STG[4 * 256];        // epilogue staging, 4 KB per wave
   __shared__ int32_t SROW[2 * 256];     // scattered output rows, by tile parity
+  // MX: scale words of the two stages, each 256 token rows then 256 weight rows
+  __shared__ uint32_t SSC[MX ? 2 * 512 : 1];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -167,14 +200,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int N = a.N, K = a.K;
   const int NT = (N + NOUT - 1) / NOUT;
   const int total = s_pre[E] * NT;
-  const int nk = K / BK;
+  const int nk = K / stage_k<MX>();
 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
   const Split sp = split_work(total, gridDim.x, nk, a.max_pieces);
   const int nf = sp.full / gridDim.x;          // whole tiles of this workgroup
   const int xbegin = xcd * (sp.full >> 3);     // its XCD's range of whole tiles
 
-  const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
   const uint16_t* Bb = static_cast<const uint16_t*>(a.B);
   uint16_t* Cb = static_cast<uint16_t*>(a.C);
 
@@ -230,11 +262,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // vector ALU work.  Gathered A rows are looked up when the DMA cursor
   // enters a tile and converted (permutation entry / k, clamped) at the
   // first issue after the next barrier, when the loads are known to be done.
+  //
+  // MX: lane l of wave w also fetches the scale words of tile row 64 w + l:
+  // a token row (clamped, or gathered) and a weight row (swiglu: waves 0-1
+  // gate rows, waves 2-3 up rows), at a lane offset of row * K / 32 bytes
+  // from bases that move by 4 bytes per stage.
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);
-  const uint64_t rowbytes = static_cast<uint64_t>(K) * 2;
+  const uint64_t rowbytes = static_cast<uint64_t>(K) * (MX ? 1 : 2);
   const uint32_t rb32 = static_cast<uint32_t>(rowbytes);
-  const char* Ach = reinterpret_cast<const char*>(Ab);
+  const char* Ach = static_cast<const char*>(a.A);
   const char* Bch = reinterpret_cast<const char*>(Bb);
   uint32_t voff[16];
   const char* dA;                 // A base of the DMA tile (stage 0)
@@ -242,7 +279,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const char* dB1;                // swiglu: up rows
   int32_t graw[GATHER ? 8 : 1];   // raw permutation entries of the gathered rows
   bool gpend = false;
+  const uint32_t srb = static_cast<uint32_t>(K / 32);   // MX: scale bytes per row
+  const int srow = 64 * wave + lane;                     // MX: tile row of this lane's scale words
+  uint32_t sxoff = 0, swoff = 0;  // MX: lane offsets of the token / weight scale DMAs
+  const uint8_t* dSx = nullptr;   // MX: scale bases of the DMA tile (stage 0)
+  const uint8_t* dSw = nullptr;
+  int32_t sgraw = 0;              // MX, gathered: raw permutation entry of the scale row
   auto set_rows = [&](const Tile& t) {
+    if constexpr (MX) {
+      const int sr = srow < t.rows ? srow : t.rows - 1;
+      if constexpr (GATHER) {
+        sgraw = a.gather[t.r0 + sr];
+        dSx = a.a_scale;
+      } else {
+        sxoff = static_cast<uint32_t>(sr) * srb;
+        dSx = a.a_scale + static_cast<uint64_t>(t.r0) * srb;
+      }
+      if constexpr (SWIGLU) {
+        const int nb = a.I - t.n0;
+        const int rr = srow & 127;
+        swoff = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * srb;
+        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * (2 * a.I) + t.n0 + (wave >= 2 ? a.I : 0)) * srb;
+      } else {
+        const int nb = N - t.n0;
+        swoff = static_cast<uint32_t>(srow < nb ? srow : nb - 1) * srb;
+        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * N + t.n0) * srb;
+      }
+    }
     if constexpr (GATHER) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -281,16 +344,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
   // gathered row = entry / k by multiply-high (exact for entries < 2^31),
   // clamped into A; A spans fewer than 2^32 bytes (checked at launch)
+  auto grow = [&](int32_t raw) -> uint32_t {
+    const uint32_t v = static_cast<uint32_t>(raw < 0 ? 0 : raw);
+    const uint32_t q = a.gather_magic ? (__umulhi(v, a.gather_magic) >> a.gather_shift) : (v >> a.gather_shift);
+    return q < static_cast<uint32_t>(a.a_rows) ? q : static_cast<uint32_t>(a.a_rows - 1);
+  };
   auto gconv = [&]() {
     if constexpr (GATHER) {
       if (gpend) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t v = static_cast<uint32_t>(graw[j] < 0 ? 0 : graw[j]);
-          uint32_t q = a.gather_magic ? (__umulhi(v, a.gather_magic) >> a.gather_shift) : (v >> a.gather_shift);
-          q = q < static_cast<uint32_t>(a.a_rows) ? q : static_cast<uint32_t>(a.a_rows - 1);
-          voff[j] = q * rb32 + lchunk * 16;
-        }
+        for (int j = 0; j < 8; ++j) voff[j] = grow(graw[j]) * rb32 + lchunk * 16;
+        if constexpr (MX) sxoff = grow(sgraw) * srb;
         gpend = false;
       }
     }
@@ -300,38 +364,89 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
   const uint32_t sb0 = __builtin_amdgcn_readfirstlane(lds_addr(S0) + wofs);
   const uint32_t sb1 = __builtin_amdgcn_readfirstlane(lds_addr(S1) + wofs);
+  // MX: LDS byte address of this wave's token scale words in stage buffer 0
+  // (buffer b: + 2048 b; weight scale words: + 1024)
+  const uint32_t scb = MX ? __builtin_amdgcn_readfirstlane(lds_addr(SSC) + wave * 256) : 0;
   auto dma1 = [&](int kc, uint32_t sb, int t) {   // t < 8: A rows 32t.., else B rows 32(t-8)..
-    const uint64_t ko = static_cast<uint64_t>(kc) * BK * 2;
+    const uint64_t ko = static_cast<uint64_t>(kc) * kStageBytes;
     const char* base = t < 8 ? dA : ((SWIGLU && t >= 12) ? dB1 : dB0);
     dma16s(base + ko, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
   };
-  // The three global bases of stage kc, pinned to scalar registers once, so
-  // that each DMA of the stage is one M0 write and the load.
+  auto dma_sc1 = [&](int kc, int buf) {           // MX: the scale words of stage kc
+    if constexpr (MX) {
+      dma4s(dSx + 4 * kc, sxoff, scb + buf * 2048);
+      dma4s(dSw + 4 * kc, swoff, scb + buf * 2048 + 1024);
+    }
+  };
+  // The global bases of stage kc, pinned to scalar registers once, so that
+  // each DMA of the stage is one M0 write and the load.
   struct StageBase {
     const char *a, *b0, *b1;
+    const uint8_t *sx, *sw;
   };
   auto stage_base = [&](int kc) -> StageBase {
-    const uint64_t ko = static_cast<uint64_t>(kc) * BK * 2;
-    auto pin = [](const char* p) {
+    const uint64_t ko = static_cast<uint64_t>(kc) * kStageBytes;
+    auto pin = [](const auto* p) {
       const uint64_t v = reinterpret_cast<uintptr_t>(p);
       const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
       const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
-      return reinterpret_cast<const char*>(static_cast<uintptr_t>((hi << 32) | lo));
+      return reinterpret_cast<decltype(p)>(static_cast<uintptr_t>((hi << 32) | lo));
     };
-    return StageBase{pin(dA + ko), pin(dB0 + ko), pin(SWIGLU ? dB1 + ko : dB0 + ko)};
+    StageBase g{pin(dA + ko), pin(dB0 + ko), pin(SWIGLU ? dB1 + ko : dB0 + ko), nullptr, nullptr};
+    if constexpr (MX) {
+      g.sx = pin(dSx + 4 * kc);
+      g.sw = pin(dSw + 4 * kc);
+    }
+    return g;
   };
   auto dma_pre = [&](const StageBase& g, uint32_t sb, int t) {
     const char* base = t < 8 ? g.a : ((SWIGLU && t >= 12) ? g.b1 : g.b0);
     dma16p(base, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
   };
+  auto dma_sc_pre = [&](const StageBase& g, int buf) {
+    if constexpr (MX) {
+      dma4p(g.sx, sxoff, scb + buf * 2048);
+      dma4p(g.sw, swoff, scb + buf * 2048 + 1024);
+    }
+  };
 
   f32x16_t acc[4][4];
-  struct Frag {
+  struct FragB {
     bf16x8_t x[4], w[4];
   };
+  struct FragM {                  // MX: one K64 step
+    i32x8_t x[4], w[4];
+  };
+  using Frag = typename std::conditional<MX, FragM, FragB>::type;
   auto mfma1 = [&](const Frag& F, int t) {
-    const int i = t >> 2, j = t & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[j], F.x[i], acc[i][j], 0, 0, 0);
+    if constexpr (!MX) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[j], F.x[i], acc[i][j], 0, 0, 0);
+    }
+  };
+  // MX: an empty asm that reads and rewrites every accumulator in place.  It
+  // keeps the MFMAs of a K64 step ahead of the barrier or loop edge that
+  // follows: the code generator would otherwise sink the MFMAs, whose results
+  // only feed the next iteration, past the stage's LDS reads and DMAs, which
+  // then no longer overlap the matrix work.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  };
+  // MX: K64 step `second` of a stage, with the stage's scale words (shifted
+  // by 8 (lane / 32) bits: byte 2 second is this lane's block)
+  auto mfma_mx = [&](const Frag& F, int t, bool second, const uint32_t* sx, const uint32_t* sw) {
+    if constexpr (MX) {
+      const int i = t >> 2, j = t & 3;
+      if (second)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            F.w[j], F.x[i], acc[i][j], 0, 0, 2, static_cast<int>(sw[j]), 2, static_cast<int>(sx[i]));
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            F.w[j], F.x[i], acc[i][j], 0, 0, 0, static_cast<int>(sw[j]), 0, static_cast<int>(sx[i]));
+    }
   };
   // Fragment rows are (multiple of 32) + lane % 32, so their swizzle term
   // ((row >> 1) & 7) is the same lane constant sl for every fragment: one
@@ -345,15 +460,45 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     xo[st] = static_cast<uint32_t>(((wm * 128 + (lane & 31)) * 8 + slotv) * 16);
     wo[st] = static_cast<uint32_t>((BM * 8 + ((SWIGLU ? wn * 64 : wn * 128) + (lane & 31)) * 8 + slotv) * 16);
   }
-  // fragment t (< 4: x[t], else w[t-4]) of K16 step s (0..3) of the stage in Ss
+  // fragment t (< 4: x[t], else w[t-4]) of K16 step s (0..3) of the stage in
+  // Ss; MX: of K64 step s (0..1), the chunks of K16 steps 2 s and 2 s + 1
   auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {
     const char* base = reinterpret_cast<const char*>(Ss);
-    if (t < 4) {
-      F.x[t] = *reinterpret_cast<const bf16x8_t*>(base + xo[s] + t * 32 * 128);
+    if constexpr (MX) {
+      if (t < 4) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + xo[2 * s] + t * 32 * 128);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + xo[2 * s + 1] + t * 32 * 128);
+        F.x[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        const int j = t - 4;
+        const int rowoff = SWIGLU ? ((j < 2) ? j * 32 : 128 + (j - 2) * 32) : j * 32;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + wo[2 * s] + rowoff * 128);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + wo[2 * s + 1] + rowoff * 128);
+        F.w[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     } else {
-      const int j = t - 4;
-      const int rowoff = SWIGLU ? ((j < 2) ? j * 32 : 128 + (j - 2) * 32) : j * 32;
-      F.w[j] = *reinterpret_cast<const bf16x8_t*>(base + wo[s] + rowoff * 128);
+      if (t < 4) {
+        F.x[t] = *reinterpret_cast<const bf16x8_t*>(base + xo[s] + t * 32 * 128);
+      } else {
+        const int j = t - 4;
+        const int rowoff = SWIGLU ? ((j < 2) ? j * 32 : 128 + (j - 2) * 32) : j * 32;
+        F.w[j] = *reinterpret_cast<const bf16x8_t*>(base + wo[s] + rowoff * 128);
+      }
+    }
+  };
+  // MX: scale words of the fragments of the stage in buffer buf (token rows
+  // of x[i], weight rows of w[j]), shifted by 8 (lane / 32) bits
+  const int lsh = 8 * (lane >> 5);
+  auto read_sc = [&](int buf, uint32_t* sx, uint32_t* sw) {
+    if constexpr (MX) {
+      const uint32_t* S = SSC + buf * 512;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sx[i] = S[wm * 128 + i * 32 + (lane & 31)] >> lsh;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int wr = SWIGLU ? (j < 2 ? wn * 64 + 32 * j : 128 + wn * 64 + 32 * (j - 2)) : wn * 128 + 32 * j;
+        sw[j] = S[256 + wr + (lane & 31)] >> lsh;
+      }
     }
   };
 
@@ -410,19 +555,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   gconv();
 #pragma unroll
   for (int t = 0; t < 16; ++t) dma1(dkc, sb0, t);
+  dma_sc1(dkc, 0);
   dma_advance();
   if (dlive) {
     gconv();
 #pragma unroll
     for (int t = 0; t < 16; ++t) dma1(dkc, sb1, t);
+    dma_sc1(dkc, 1);
     dma_advance();
   }
   wait_vmcnt0();
   lds_barrier();
 
   Frag Fa, Fb;
+  uint32_t csx[4], csw[4];         // MX: scale words of the stage being multiplied
 #pragma unroll
   for (int t = 0; t < 8; ++t) frag1(S0, 0, Fa, t);
+  read_sc(0, csx, csw);
   auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -440,42 +589,79 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const uint4* Sn = par ? S0 : S1;
     const uint32_t sbc = par ? sb1 : sb0;
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MX) {
+      // two K64 steps: step 0 reads the fragments of step 1; after the
+      // barrier step 1 reads the fragments and scale words of stage g+1 and
+      // fetches stage g+2 (data and scales) into the freed buffer
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 0; read step 1
-      mfma1(Fa, t);
-      if (t < 8) frag1(Sc, 1, Fb, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int t = 0; t < 16; ++t) {
+        mfma_mx(Fa, t, false, csx, csw);
+        if (t < 8) frag1(Sc, 1, Fb, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin_acc();
+      wait_vmcnt0();
+      lds_barrier();
+      const bool last = ckc == ci.k1 - 1;
+      if (dlive) gconv();
+      const StageBase gb = stage_base(dlive ? dkc : 0);
+      uint32_t nsx[4], nsw[4];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 1; read step 2
-      mfma1(Fb, t);
-      if (t < 8) frag1(Sc, 2, Fa, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int t = 0; t < 16; ++t) {
+        mfma_mx(Fb, t, true, csx, csw);
+        if (t < 8) frag1(Sn, 0, Fa, t);
+        if (t == 8) read_sc(par ^ 1, nsx, nsw);
+        dma_pre(gb, sbc, t);
+        if (t == 15) dma_sc_pre(gb, par);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin_acc();
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 2; read step 3
-      mfma1(Fa, t);
-      if (t < 8) frag1(Sc, 3, Fb, t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vmcnt0();                     // stage g+1 (the only DMAs in flight) landed
-    lds_barrier();                     // ... everywhere, and stage g is no longer read
-    const bool last = ckc == ci.k1 - 1;
-    if (dlive) gconv();
-    // One branch-free step 3.  With nothing left to fetch the DMAs re-read
-    // stage 0 of the last tile into the buffer just freed (valid memory,
-    // never read again); the kernel waits for them before it ends.
-    const StageBase gb = stage_base(dlive ? dkc : 0);
+      for (int i = 0; i < 4; ++i) {
+        csx[i] = nsx[i];
+        csw[i] = nsw[i];
+      }
+      if (dlive) dma_advance();
+      if (!last) ++ckc;
+      return last;
+    } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch g+2
-      mfma1(Fb, t);
-      if (t < 8) frag1(Sn, 0, Fa, t);  // stale but harmless when g+1 does not exist
-      dma_pre(gb, sbc, t);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 16; ++t) {     // step 0; read step 1
+        mfma1(Fa, t);
+        if (t < 8) frag1(Sc, 1, Fb, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {     // step 1; read step 2
+        mfma1(Fb, t);
+        if (t < 8) frag1(Sc, 2, Fa, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {     // step 2; read step 3
+        mfma1(Fa, t);
+        if (t < 8) frag1(Sc, 3, Fb, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vmcnt0();                     // stage g+1 (the only DMAs in flight) landed
+      lds_barrier();                     // ... everywhere, and stage g is no longer read
+      const bool last = ckc == ci.k1 - 1;
+      if (dlive) gconv();
+      // One branch-free step 3.  With nothing left to fetch the DMAs re-read
+      // stage 0 of the last tile into the buffer just freed (valid memory,
+      // never read again); the kernel waits for them before it ends.
+      const StageBase gb = stage_base(dlive ? dkc : 0);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch g+2
+        mfma1(Fb, t);
+        if (t < 8) frag1(Sn, 0, Fa, t);  // stale but harmless when g+1 does not exist
+        dma_pre(gb, sbc, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dlive) dma_advance();
+      if (!last) ++ckc;
+      return last;
     }
-    if (dlive) dma_advance();
-    if (!last) ++ckc;
-    return last;
   };
 
   int par = 0;      // buffer of the stage being multiplied
@@ -511,6 +697,60 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
             *reinterpret_cast<float4*>(P + row * BN + wrow) = v;
             __builtin_amdgcn_sched_barrier(0);
           }
+    } else if constexpr (MX && SWIGLU) {
+      // ---- MXFP8 epilogue: h = silu(g) * u quantized along its columns.
+      // Per 32x32 result tile a lane holds 16 of the 32 columns of one token
+      // row (columns 8 g + 4 (lane / 32) + 0..3); lanes l and l ^ 32 share
+      // the row and exchange their largest magnitudes.  The e4m3 codes of 32
+      // rows x the wave's 64 columns are staged in LDS (64-byte rows, 16-byte
+      // chunk c of row r in slot c ^ ((r >> 2) & 3)) and stored as whole
+      // 64-byte row segments; the two scale bytes of a row go out as one
+      // 16-bit store.
+      uint8_t* stg = reinterpret_cast<uint8_t*>(STG) + wave * 4096;
+      uint8_t* Cq = static_cast<uint8_t*>(a.C);
+      const int r = lane & 31;
+      const int col0 = ci.t.n0 + wn * 64;             // first h column of the wave
+      const int csw_r = ((r >> 2) & 3) << 2;           // staging swizzle of row r, in words
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t sc2 = 0;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const f32x16_t& gg = acc[i][jj];
+          const f32x16_t& uu = acc[i][jj + 2];
+          float v[16];
+          float m = 0.f;
+#pragma unroll
+          for (int b = 0; b < 16; ++b) {
+            v[b] = silu_f(acc_rd(gg[b])) * acc_rd(uu[b]);
+            m = __builtin_fmaxf(m, __builtin_fabsf(v[b]));
+          }
+          m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+          const int ex = mx_block_exp(m);
+          const float sc = mx_inv_scale(ex);
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int c4 = jj * 8 + 2 * grp + (lane >> 5);   // 4-column group 0..15
+            *reinterpret_cast<uint32_t*>(stg + r * 64 + ((c4 ^ csw_r) << 2)) =
+                mx_encode4(v[4 * grp], v[4 * grp + 1], v[4 * grp + 2], v[4 * grp + 3], sc);
+          }
+          sc2 |= static_cast<uint32_t>(ex + 127) << (8 * jj);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const int row0 = wm * 128 + i * 32;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int rr = q * 16 + (lane >> 2), c = lane & 3;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4));
+          const int m = row0 + rr;
+          if (m < ci.t.rows && col0 < N)
+            *reinterpret_cast<uint4*>(Cq + static_cast<int64_t>(ci.t.r0 + m) * N + col0 + c * 16) = v;
+        }
+        const int m = row0 + r;
+        if (lane < 32 && m < ci.t.rows && col0 < N)
+          *reinterpret_cast<uint16_t*>(a.c_scale + static_cast<int64_t>(ci.t.r0 + m) * (N / 32) + col0 / 32) =
+              static_cast<uint16_t>(sc2);
+      }
     } else
     // ---- epilogue (the next stages are in flight meanwhile).  The MFMA
     // result leaves each lane with 4 consecutive columns of one row per 32x32
@@ -580,12 +820,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 
 // Finish the K-split remainder tiles: sum each tile's partial slots in piece
 // order, apply the epilogue (swiglu: silu(gate) * up) and store bf16 rows.
-template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_bf16_fixup_kernel(GemmArgs a) {
+template <bool MX, bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs a) {
   constexpr int NOUT = SWIGLU ? BN / 2 : BN;
   const int NT = (a.N + NOUT - 1) / NOUT;
   const int total = a.prefix[a.E] * NT;
-  const Split sp = split_work(total, a.grid, a.K / BK, a.max_pieces);
+  const Split sp = split_work(total, a.grid, a.K / stage_k<MX>(), a.max_pieces);
   if (sp.ways < 2) return;
   constexpr int CPR = NOUT / 8;                  // 8-column groups per output row
   const int64_t work = static_cast<int64_t>(sp.rem) * BM * CPR;
@@ -626,43 +866,76 @@ __global__ __launch_bounds__(256) void gemm_bf16_fixup_kernel(GemmArgs a) {
   }
 }
 
-template <bool SWIGLU, bool GATHER>
+// MX SwiGLU: finish the K-split remainder tiles of the gate/up GEMM.  One
+// thread per (tile, row, 32-column block): the gate and up sums of the block
+// added in piece order, h = silu(g) * u quantized to MXFP8 as in the main
+// kernel's epilogue (32 codes and one scale byte).
+__global__ __launch_bounds__(256) void gemm_mx_swiglu_fixup_kernel(GemmArgs a) {
+  constexpr int NOUT = BN / 2;
+  const int NT = (a.N + NOUT - 1) / NOUT;
+  const int total = a.prefix[a.E] * NT;
+  const Split sp = split_work(total, a.grid, a.K / stage_k<true>(), a.max_pieces);
+  if (sp.ways < 2) return;
+  constexpr int BPR = NOUT / 32;                 // 32-column blocks per output row
+  const int64_t work = static_cast<int64_t>(sp.rem) * BM * BPR;
+  uint8_t* C = static_cast<uint8_t*>(a.C);
+  for (int64_t idx = blockIdx.x * 256LL + threadIdx.x; idx < work; idx += gridDim.x * 256LL) {
+    const int q = static_cast<int>(idx / (BM * BPR));
+    const int row = static_cast<int>(idx / BPR % BM);
+    const int blk = static_cast<int>(idx % BPR);
+    Tile t;
+    if (!decode_tile(sp.full + q, NT, NOUT, a.E, a.prefix, a.offsets, a.M, t)) continue;
+    const int col = t.n0 + blk * 32;
+    if (row >= t.rows || col >= a.N) continue;
+    float g[32], u[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) g[c] = u[c] = 0.f;
+    for (int p = 0; p < sp.ways; ++p) {
+      const float* P = a.partials + static_cast<int64_t>(q * sp.ways + p) * (BM * BN) + row * BN + blk * 32;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(P + 4 * c);
+        const float4 y = *reinterpret_cast<const float4*>(P + 128 + 4 * c);
+        g[4 * c] += x.x; g[4 * c + 1] += x.y; g[4 * c + 2] += x.z; g[4 * c + 3] += x.w;
+        u[4 * c] += y.x; u[4 * c + 1] += y.y; u[4 * c + 2] += y.z; u[4 * c + 3] += y.w;
+      }
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      g[c] = silu_f(g[c]) * u[c];
+      m = __builtin_fmaxf(m, __builtin_fabsf(g[c]));
+    }
+    const int ex = mx_block_exp(m);
+    const float sc = mx_inv_scale(ex);
+    uint32_t w[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w[c] = mx_encode4(g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3], sc);
+    const int64_t crow = t.r0 + row;
+    uint4* dst = reinterpret_cast<uint4*>(C + crow * a.N + col);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    a.c_scale[crow * (a.N / 32) + col / 32] = static_cast<uint8_t>(ex + 127);
+  }
+}
+
+template <bool MX, bool SWIGLU, bool GATHER>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_pieces < 2 || a.K / BK < 2 * kMinPiece) return e;
-  hipLaunchKernelGGL((gemm_bf16_fixup_kernel<SWIGLU>), dim3(512), dim3(256), 0, s, a);
+  if (e != hipSuccess || a.max_pieces < 2 || a.K / stage_k<MX>() < 2 * kMinPiece) return e;
+  if constexpr (MX && SWIGLU)
+    hipLaunchKernelGGL(gemm_mx_swiglu_fixup_kernel, dim3(512), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_fixup_kernel<MX, SWIGLU>), dim3(512), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-}  // namespace
-
-int gemm_bf16_pieces(int64_t M, int H, int I, int E) {
-  // a K split never makes more pieces than tiles x (K stages / kMinPiece) of
-  // either GEMM, and none when a tile cannot be cut in two
-  const int64_t mt = (M + BM - 1) / BM + E;           // m-tiles, upper bound
-  auto most = [&](int64_t nt, int nk) -> int64_t {
-    const int w = nk / kMinPiece;
-    return w >= 2 ? mt * nt * w : 0;
-  };
-  const int64_t up = most((I + BN / 2 - 1) / (BN / 2), H / BK);
-  const int64_t down = most((H + BN - 1) / BN, I / BK);
-  const int64_t m = up > down ? up : down;
-  return static_cast<int>(m < kGemmPieces ? m : kGemmPieces);
-}
-
-bool gemm_bf16_gather_fits(int64_t a_rows, int K) {
-  return static_cast<uint64_t>(a_rows) * static_cast<uint64_t>(K) * 2 <= (uint64_t{1} << 32);
-}
-
-hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
-  if (!a0.gather) return launch<true, false>(a0, s);
-  if (a0.gather_div < 1 || !gemm_bf16_gather_fits(a0.a_rows, a0.K)) return hipErrorInvalidValue;
-  GemmArgs a = a0;
-  // entry / d for entries in [0, 2^31): d = 2^l is a shift; otherwise, with
-  // l = ceil(log2 d) and m = floor(2^(31+l) / d) + 1 < 2^32, the quotient is
-  // floor(entry * m / 2^(31+l)): the excess entry * (m d - 2^(31+l)) / (d 2^(31+l))
-  // is below 2^-l < 1/d, too small to carry past the next integer.
+// entry / d for entries in [0, 2^31): d = 2^l is a shift; otherwise, with
+// l = ceil(log2 d) and m = floor(2^(31+l) / d) + 1 < 2^32, the quotient is
+// floor(entry * m / 2^(31+l)): the excess entry * (m d - 2^(31+l)) / (d 2^(31+l))
+// is below 2^-l < 1/d, too small to carry past the next integer.
+void set_gather_magic(GemmArgs& a) {
   const uint32_t d = static_cast<uint32_t>(a.gather_div);
   if ((d & (d - 1)) == 0) {
     a.gather_magic = 0;
@@ -672,11 +945,54 @@ hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
     a.gather_magic = static_cast<uint32_t>((uint64_t{1} << (31 + l)) / d + 1);
     a.gather_shift = l - 1;
   }
-  return launch<true, true>(a, s);
+}
+
+}  // namespace
+
+int gemm_pieces(int64_t M, int H, int I, int E, bool mx) {
+  // a K split never makes more pieces than tiles x (K stages / kMinPiece) of
+  // either GEMM, and none when a tile cannot be cut in two
+  const int64_t mt = (M + BM - 1) / BM + E;           // m-tiles, upper bound
+  const int ks = mx ? stage_k<true>() : stage_k<false>();
+  auto most = [&](int64_t nt, int nk) -> int64_t {
+    const int w = nk / kMinPiece;
+    return w >= 2 ? mt * nt * w : 0;
+  };
+  const int64_t up = most((I + BN / 2 - 1) / (BN / 2), H / ks);
+  const int64_t down = most((H + BN - 1) / BN, I / ks);
+  const int64_t m = up > down ? up : down;
+  return static_cast<int>(m < kGemmPieces ? m : kGemmPieces);
+}
+
+bool gemm_gather_fits(int64_t a_rows, int K, int elem_bytes) {
+  return static_cast<uint64_t>(a_rows) * static_cast<uint64_t>(K) * elem_bytes <= (uint64_t{1} << 32);
+}
+
+hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
+  if (!a0.gather) return launch<false, true, false>(a0, s);
+  if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 2)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  set_gather_magic(a);
+  return launch<false, true, true>(a, s);
 }
 
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s) {
-  return launch<false, false>(a, s);
+  return launch<false, false, false>(a, s);
+}
+
+hipError_t launch_gemm_mx_swiglu(const GemmArgs& a0, hipStream_t s) {
+  if (!a0.a_scale || !a0.b_scale || !a0.c_scale || a0.K % stage_k<true>() || a0.N % (BN / 2))
+    return hipErrorInvalidValue;
+  if (!a0.gather) return launch<true, true, false>(a0, s);
+  if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 1)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  set_gather_magic(a);
+  return launch<true, true, true>(a, s);
+}
+
+hipError_t launch_gemm_mx_down(const GemmArgs& a, hipStream_t s) {
+  if (!a.a_scale || !a.b_scale || a.K % stage_k<true>()) return hipErrorInvalidValue;
+  return launch<true, false, false>(a, s);
 }
 
 }  // namespace moe

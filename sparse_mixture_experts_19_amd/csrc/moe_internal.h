@@ -14,10 +14,11 @@ constexpr int kMaxE = 256;             // experts supported
 constexpr int kMaxK = 8;               // top-k supported
 constexpr int kRouteTok = 32;          // tokens per router workgroup
 constexpr int kPermChunk = 1024;       // assignments per permutation workgroup
-constexpr int kGemmBM = 256;           // bf16 grouped GEMM: rows per tile
-constexpr int kGemmBN = 256;           // bf16 grouped GEMM: weight rows per tile
-constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage
-constexpr int kGemmPieces = 256;       // bf16 grouped GEMM: most K-split partial tiles
+constexpr int kGemmBM = 256;           // MFMA grouped GEMMs: rows per tile
+constexpr int kGemmBN = 256;           // MFMA grouped GEMMs: weight rows per tile
+constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage (MXFP8: 128)
+constexpr int kGemmPieces = 256;       // MFMA grouped GEMMs: most K-split partial tiles
+constexpr int kMxBlock = 32;           // MXFP8: values per E8M0 scale
 constexpr int kF32BM = 64;             // fp32 grouped GEMM tile
 constexpr int kF32BN = 64;
 constexpr int kF32BK = 16;
@@ -85,10 +86,10 @@ hipError_t launch_tile_schedule(const int32_t* offsets, int E, int bm, int64_t M
 
 // --------------------------------------------- grouped GEMMs (gemm_*.hip)
 struct GemmArgs {
-  const void* A;          // rows: [*,K] (x, x_perm or h)
+  const void* A;          // rows: [*,K] (x, x_perm or h; MXFP8: e4m3 codes)
   const int32_t* gather;  // null: row r of A is r; else row r is gather[r] / gather_div
   int gather_div;
-  uint32_t gather_magic;  // bf16 kernels: entry / gather_div == umulhi(entry, magic) >> shift
+  uint32_t gather_magic;  // MFMA kernels: entry / gather_div == umulhi(entry, magic) >> shift
   int gather_shift;       // (magic 0: entry >> shift); set by the launcher
   int64_t a_rows;         // rows of A (gathered row indices are clamped to it)
   int64_t M;              // rows of C (tile rows are clamped to it)
@@ -104,13 +105,22 @@ struct GemmArgs {
   float* partials;        // bf16: fp32 partial sums of K-split tiles, max_pieces x BM x BN
   int max_pieces;         // capacity of partials in tiles (0: tiles are never split)
   const int32_t* scatter; // null: row r of C is row r; else row r is written to row scatter[r]
+  // MXFP8 kernels: E8M0 scales (biased exponents), one byte per 32 values of a row
+  const uint8_t* a_scale; // [*, K/32], rows as A (gathered like A)
+  const uint8_t* b_scale; // [E, rows of an expert, K/32]
+  uint8_t* c_scale;       // SwiGLU: scales of h [M, N/32] (h itself: e4m3 codes in C)
 };
-// Partial-sum slots the bf16 GEMMs of an [M rows, H, I, E] expert MLP can use.
-int gemm_bf16_pieces(int64_t M, int H, int I, int E);
+// Partial-sum slots the MFMA GEMMs (mx: MXFP8) of an [M rows, H, I, E]
+// expert MLP can use.
+int gemm_pieces(int64_t M, int H, int I, int E, bool mx);
 // The gathered form (gather != null) needs A to span at most 2^32 bytes.
-bool gemm_bf16_gather_fits(int64_t a_rows, int K);
+bool gemm_gather_fits(int64_t a_rows, int K, int elem_bytes);
 hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
+// MXFP8 operands: K a multiple of 128; SwiGLU: N (= I) a multiple of 128;
+// the down GEMM writes bf16 rows.
+hipError_t launch_gemm_mx_swiglu(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_mx_down(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32_down(const GemmArgs& a, hipStream_t s);
 
@@ -135,6 +145,12 @@ size_t round_scratch_bytes(int64_t T);
 // Carves the scratch arrays of `a` from `base` (round_scratch_bytes(T) bytes).
 void carve_round(char* base, RoundArgs& a);
 hipError_t launch_token_round(const RoundArgs& a, hipStream_t s);
+
+// ------------------------------------------------------ MXFP8 (mxfp8.hip)
+// rows x cols values (bf16 or fp32, cols a multiple of 32) -> e4m3 codes
+// [rows, cols] and E8M0 scales [rows, cols/32].
+hipError_t launch_mx_quantize(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
 
 // ------------------------------------------------------ combine (combine.hip)
 // inv != null: slot (t, j) is row inv[t*k+j] of y; inv == null: row t*k+j.

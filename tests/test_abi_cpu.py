@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 102
+    assert L.moe_version() == 103
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -183,6 +183,47 @@ def test_rounded_layout_and_argument_errors():
     lay = B.ForwardLayout()
     assert L.moe_forward_rounded_layout(8, 64, 100, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_forward_rounded_layout(8, 64, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_mxfp8_layout_and_argument_errors():
+    T, H, I, E, k = 4096, 4096, 14336, 8, 2
+    M = T * k
+    X = B.mxfp8_layout(T, H, I, E, k)
+    offs = [X.topk_ids, X.topk_weights, X.expert_counts, X.expert_offsets, X.perm, X.inv_perm,
+            X.x_codes, X.x_scales, X.h_codes, X.h_scales, X.y, X.scratch, X.total]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    assert X.x_scales - X.x_codes >= T * H and X.h_codes - X.x_scales >= T * H // 32
+    assert X.h_scales - X.h_codes >= M * I and X.y - X.h_scales >= M * I // 32
+    assert X.scratch - X.y >= M * H * 2
+    L = B.lib()
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("wr", FAKE), ("b", None), ("w13q", FAKE), ("w13s", FAKE), ("w2q", FAKE),
+        ("w2s", FAKE), ("T", 8), ("H", 128), ("I", 128), ("E", 4), ("k", 2), ("dt", 1), ("ren", 0),
+        ("out", FAKE), ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert L.moe_forward_mxfp8(*args(dt=0)) == B.MOE_ERR_UNSUPPORTED             # bf16 only
+    assert L.moe_forward_mxfp8(*args(H=64)) == B.MOE_ERR_UNSUPPORTED             # H % 128
+    assert L.moe_forward_mxfp8(*args(I=192)) == B.MOE_ERR_UNSUPPORTED            # I % 128
+    assert L.moe_forward_mxfp8(*args(k=5)) == B.MOE_ERR_INVALID_ARG              # k > E
+    assert L.moe_forward_mxfp8(*args(w2s=None)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_mxfp8(*args(w13q=FAKE + 4)) == B.MOE_ERR_INVALID_ARG    # misaligned
+    assert L.moe_forward_mxfp8(*args(wsb=1024)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_forward_mxfp8(*args(T=1 << 22, H=2048)) == B.MOE_ERR_UNSUPPORTED  # T*H > 2^32
+    assert L.moe_forward_mxfp8(*args(T=0, x=None, out=None, ws=None, wsb=0)) == B.MOE_OK
+    assert L.moe_forward_mxfp8_profiled(*args()[:-1], None, 0, None) == B.MOE_ERR_INVALID_ARG
+    ev = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert L.moe_forward_mxfp8_profiled(*args()[:-1], ev, 7, None) == B.MOE_ERR_INVALID_ARG
+    lay = B.Mxfp8Layout()
+    assert L.moe_forward_mxfp8_layout(8, 128, 100, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_mxfp8_layout(8, 128, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
+    # quantize: cols a positive multiple of 32, known dtype, aligned pointers
+    assert L.moe_mx_quantize(FAKE, 4, 48, 1, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_quantize(FAKE, 4, 0, 1, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_quantize(FAKE, -1, 32, 1, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_quantize(FAKE, 4, 32, 5, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_quantize(FAKE, 4, 32, 1, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_quantize(FAKE + 8, 4, 32, 1, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_quantize(None, 0, 32, 1, None, None, None) == B.MOE_OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
