@@ -24,9 +24,9 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/sec + grouped-GEMM % bf16 MFMA peak, 1× MI355X"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (block-scaled MXFP8 included)
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 BM = 256                       # rows per grouped-GEMM tile (bf16 kernels)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SOURCES = ["sparse_mixture_experts_19_amd/csrc/gemm_mfma.hip",
@@ -45,11 +45,13 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic(wl, counts, Is: int = 0):
+def algorithmic(wl, counts, Is: int = 0, mx: bool = False):
     """Algorithmic flops / bytes per launch of every stage (real rows only;
     only the weights of experts that own rows are counted).  Is: intermediate
-    size of the shared expert (0: none)."""
+    size of the shared expert (0: none).  mx: MXFP8 expert GEMMs (operands of
+    1 byte plus one scale byte per 32; y stays bf16)."""
     b = 2 if wl.dtype == "bf16" else 4
+    q = 1 + 1 / 32 if mx else b          # bytes per GEMM operand element
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     M = T * k
     active = int(sum(1 for c in counts if c > 0))
@@ -57,9 +59,10 @@ def algorithmic(wl, counts, Is: int = 0):
     st["route"] = dict(bytes=T * H * b + E * H * b + 8 * M, flops=2 * T * H * E)
     st["permute"] = dict(bytes=4 * M + 4 * M + 4 * M + 8 * E, flops=0)
     st["schedule"] = dict(bytes=8 * E, flops=0)
+    st["quantize_x"] = dict(bytes=T * H * b + T * H * (1 + 1 / 32), flops=0)
     st["gemm_gate_up_swiglu"] = dict(flops=4 * M * H * I,
-                                     bytes=2 * active * I * H * b + M * H * b + M * I * b + 4 * M)
-    st["gemm_down"] = dict(flops=2 * M * I * H, bytes=active * H * I * b + M * I * b + M * H * b)
+                                     bytes=2 * active * I * H * q + M * H * q + M * I * q + 4 * M)
+    st["gemm_down"] = dict(flops=2 * M * I * H, bytes=active * H * I * q + M * I * q + M * H * b)
     st["combine"] = dict(bytes=M * H * b + T * H * b + 8 * M + (T * H * b if Is else 0), flops=0)
     # token rounding: permutation of the routed ids (12 B per assignment), the
     # pooled-slot pass (8 B read per assignment, 9 B written per token) and the
@@ -126,6 +129,9 @@ def main():
                     help="token rounding to the grouped GEMM's row tile (moe_forward_rounded)")
     ap.add_argument("--round-tile", type=int, default=0, metavar="B",
                     help="token rounding to B rows (moe_forward_rounded)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="MXFP8 expert GEMMs (moe_forward_mxfp8; weights quantized once, "
+                         "before the timed steps)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -169,10 +175,27 @@ def main():
     out = torch.empty((wl.T, wl.H), dtype=x.dtype, device=dev)
     Is = args.shared_intermediate
     RB = args.round_tile or (B.gemm_tile_rows(dt_code) if args.round else 0)
-    if RB and Is:
-        print("bench.py: --round and --shared-intermediate do not combine", file=sys.stderr)
+    MX = args.mxfp8
+    if (RB and Is) or (MX and (RB or Is)):
+        print("bench.py: --round, --shared-intermediate and --mxfp8 do not combine",
+              file=sys.stderr)
         sys.exit(2)
-    if RB:
+    wq_ms = None
+    if MX:
+        if wl.dtype != "bf16":
+            print("bench.py: --mxfp8 needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        w13q, w13s = B.mx_quantize(w13)
+        w2q, w2s = B.mx_quantize(w2)
+        e1.record()
+        torch.cuda.synchronize()
+        wq_ms = e0.elapsed_time(e1)
+        del w13, w2
+        nbytes = B.mxfp8_layout(wl.T, wl.H, wl.I, wl.E, wl.k).total
+        stages, n_ev = B.PROFILE_STAGES_MXFP8, B.PROFILE_EVENTS_MXFP8
+    elif RB:
         nbytes = B.rounded_layout(wl.T, wl.H, wl.I, wl.E, wl.k, dt_code).total
         stages, n_ev = B.PROFILE_STAGES_ROUNDED, B.PROFILE_EVENTS_ROUNDED
     elif Is:
@@ -192,7 +215,10 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
-        if RB:
+        if MX:
+            B.moe_forward_mxfp8(x, wr, bias, w13q, w13s, w2q, w2s, wl.k, wl.renormalize, out, ws,
+                                events=evs[i % len(evs)])
+        elif RB:
             B.moe_forward_rounded(x, wr, bias, w13, w2, wl.k, wl.renormalize, RB, out, ws,
                                   events=evs[i % len(evs)])
         elif Is:
@@ -218,10 +244,13 @@ def main():
     for i in range(args.steps):
         for j, s in enumerate(stages):
             stage_ms[s] += evs[i][j].elapsed_time(evs[i][j + 1]) / args.steps
-    mid = B.forward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
+    if MX:
+        mid = B.mxfp8_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k)
+    else:
+        mid = B.forward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
     counts = mid["counts"].cpu().numpy().tolist()
 
-    alg = algorithmic(wl, counts, Is)
+    alg = algorithmic(wl, counts, Is, MX)
     detail = {}
     for s in stages:
         t = stage_ms[s] * 1e-3
@@ -233,7 +262,7 @@ def main():
         detail[s] = d
     g_t = (stage_ms["gemm_gate_up_swiglu"] + stage_ms["gemm_down"]) * 1e-3
     g_flops = alg["gemm_gate_up_swiglu"]["flops"] + alg["gemm_down"]["flops"]
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_FP8_TFLOPS if MX else PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     grouped_tflops = g_flops / g_t / 1e12
 
     # dominant kernel roofline
@@ -241,7 +270,7 @@ def main():
     a = alg[dom]
     tdom = stage_ms[dom] * 1e-3
     ai = a["flops"] / a["bytes"] if a["bytes"] else 0.0
-    if a["flops"] and (wl.dtype != "bf16" or ai >= RIDGE_BF16):
+    if a["flops"] and (wl.dtype != "bf16" or ai >= peak * 1e12 / (PEAK_HBM_GBS * 1e9)):
         roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": a["flops"] / tdom / 1e12,
                 "peak": peak, "unit": "TFLOP/s"}
     else:
@@ -255,7 +284,7 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(wl.name, {}).get(dom)
+        rec = tr.get(wl.name + ("+mxfp8" if MX else ""), {}).get(dom)
         if rec and rec.get("source_sha256") == gemm_source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
@@ -272,10 +301,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": "mxfp8" if MX else "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name + (f"+shared{Is}" if Is else "") +
-                   (f"+round{RB}" if RB else ""), "tokens": wl.T,
+                   (f"+round{RB}" if RB else "") + ("+mxfp8" if MX else ""), "tokens": wl.T,
                    "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
                    "shared_intermediate": Is, "round_tile": RB, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},
@@ -285,7 +314,14 @@ def main():
         "stages": detail,
         "roofline": roof,
     }
-    if not args.no_cpu:
+    if MX:
+        rec["weight_quantization_ms"] = round(wq_ms, 3)
+    if MX and not args.no_cpu:
+        rec["cpu_baseline"] = None
+        rec["cpu_baseline_note"] = ("not timed for --mxfp8: the oracle's quantization of the "
+                                    "expert weights alone takes minutes at this size; the bf16 "
+                                    "line of the same workload carries the CPU baseline")
+    elif not args.no_cpu:
         sample = args.cpu_sample or {"tiny_f32": 512, "coarse_bf16": 4096, "fine_bf16": 4096,
                                      "vfine_bf16": 4096, "skewed_bf16": 8192}.get(wl.name, 1024)
         log(f"[bench] CPU oracle baseline on {sample} tokens")
