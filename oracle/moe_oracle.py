@@ -30,7 +30,9 @@ reason in the design notes of the repository):
     whose output is added with weight 1 to the routed sum;
   * token rounding (optional) follows the integer rule in ``token_round``;
   * MXFP8 (optional): expert GEMMs on e4m3 values with E8M0 block scales of
-    32 along the reduction axis (``mx_quantize``), router unquantized.
+    32 along the reduction axis (``mx_quantize``), router unquantized;
+  * the backward (``backward``) differentiates L = sum(dout * out) with the
+    top-k choice held fixed (it is piecewise constant).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (brute force, closed forms, library routines,
@@ -508,6 +510,99 @@ def forward_mxfp8(x, w_router, bias, w13q, w13s, w2q, w2s, k: int,
     out = combine(Y, inv, w, T, k)
     return dict(out=out, ids=ids, weights=w, logits=l, probs=p, counts=counts,
                 offsets=offsets, perm=perm, inv_perm=inv, Y=Y, Hq=Hq, Hs=Hs, H=Hf)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the block (the gradients of a training step).
+# ---------------------------------------------------------------------------
+# [SonicMoE page] 核心差异 §1 keeps only the gate outputs and the final expert
+# outputs of the forward and recomputes the rest in the backward; [Hunyuan
+# page] §二.2 gives parameter gradients only to the experts a token
+# activated.  The top-k choice is piecewise constant, so the gradients flow
+# through the selected experts' routing weights and MLPs; the loss is
+# L = sum(dout * out) for an upstream gradient dout [T,H].
+
+def silu_grad(z) -> np.ndarray:
+    """d silu(z) / dz = s (1 + z (1 - s)) with s = 1 / (1 + e^-z)."""
+    z = np.asarray(z, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def weights_grad(dw, probs_sel, renormalize: bool) -> np.ndarray:
+    """Gradient with respect to the selected probabilities [T,k] from the
+    gradient dw of the routing weights: the identity, or, through the
+    renormalisation w_j = p_j / S with S = sum_i p_i,
+    (dw_j - sum_i dw_i w_i) / S."""
+    dw = _f64(dw)
+    if not renormalize:
+        return dw
+    ps = _f64(probs_sel)
+    S = ps.sum(axis=1, keepdims=True)
+    w = ps / S
+    return (dw - (dw * w).sum(axis=1, keepdims=True)) / S
+
+
+def softmax_grad(p, dp) -> np.ndarray:
+    """Gradient with respect to the logits of p = softmax(l):
+    p * (dp - sum_e dp_e p_e) per token."""
+    p, dp = _f64(p), _f64(dp)
+    return p * (dp - (dp * p).sum(axis=1, keepdims=True))
+
+
+def expert_mlp_backward(xe, w13_e, w2_e, dy):
+    """One expert's SwiGLU MLP backward for its rows xe and their output
+    gradient dy (the routing weight already applied), with g, u and h
+    recomputed from xe: (dx of the rows, dW13_e, dW2_e)."""
+    xe, w13_e, w2_e, dy = _f64(xe), _f64(w13_e), _f64(w2_e), _f64(dy)
+    I = w13_e.shape[0] // 2
+    g = xe @ w13_e[:I].T
+    u = xe @ w13_e[I:].T
+    h = silu(g) * u
+    dw2 = dy.T @ h
+    dh = dy @ w2_e
+    dg = dh * u * silu_grad(g)
+    du = dh * silu(g)
+    dw13 = np.concatenate([dg.T @ xe, du.T @ xe])
+    return dg @ w13_e[:I] + du @ w13_e[I:], dw13, dw2
+
+
+def backward(x, w_router, bias, w13, w2, k: int, renormalize: bool, dout) -> Dict[str, np.ndarray]:
+    """Gradients of L = sum(dout * out) for the block of ``forward``: dx
+    [T,H], dw_router [E,H], dbias [E], dw13 [E,2I,H], dw2 [E,H,I]; also dw
+    [T,k] (routing weights) and dlogits [T,E].  The forward's routing, its
+    permutation and its expert outputs Y are reused; g, u and h are
+    recomputed per expert."""
+    fw = forward(x, w_router, bias, w13, w2, k, renormalize)
+    x, w_router, dout = _f64(x), _f64(w_router), _f64(dout)
+    T, H = x.shape
+    E = np.asarray(w13).shape[0]
+    ids, w, p = fw["ids"], fw["weights"], fw["probs"]
+    perm, offsets, inv = fw["perm"], fw["offsets"], fw["inv_perm"]
+    # routing weights: out_t = sum_j w_tj y_tj, so dL/dw_tj = <dout_t, y_tj>
+    y_slots = fw["Y"][inv].reshape(T, k, H)
+    dw = (dout[:, None, :] * y_slots).sum(axis=2)
+    # experts, on the permuted rows
+    xp = gather_rows(x, perm, k)
+    dp_rows = gather_rows(dout, perm, k)
+    w_rows = w.reshape(-1)[perm]
+    dxp = np.zeros_like(xp)
+    dw13 = np.zeros(np.asarray(w13).shape)
+    dw2 = np.zeros(np.asarray(w2).shape)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            dy = w_rows[a:b, None] * dp_rows[a:b]
+            dxp[a:b], dw13[e], dw2[e] = expert_mlp_backward(xp[a:b], w13[e], w2[e], dy)
+    dx = combine(dxp, inv, np.ones((T, k)), T, k)
+    # router: through the selected probabilities and the softmax
+    dp = np.zeros((T, E))
+    np.put_along_axis(dp, ids, weights_grad(dw, np.take_along_axis(p, ids, axis=1), renormalize),
+                      axis=1)
+    dl = softmax_grad(p, dp)
+    dx = dx + dl @ w_router
+    return dict(dx=dx, dw_router=dl.T @ x, dbias=dl.sum(axis=0), dw13=dw13, dw2=dw2, dw=dw,
+                dlogits=dl, fw=fw)
 
 
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],

@@ -593,6 +593,90 @@ def pin_forward_mxfp8():
     assert 1e-3 < rel < 0.15, rel
 
 
+# --------------------------------------------------------------------------
+# Backward: directional derivatives of the (pinned) forward by central
+# differences, exact special cases, linearity in dout
+# --------------------------------------------------------------------------
+
+def _loss(x, wr, b, w13, w2, k, renorm, dout):
+    r = O.forward(x, wr, b, w13, w2, k, renorm)
+    return float((dout * r["out"]).sum()), r["ids"]
+
+
+_BWD_CASES = [
+    # T, H, E, k, I, bias, renormalize
+    (6, 5, 4, 2, 3, True, False),
+    (6, 5, 4, 2, 3, True, True),
+    (5, 4, 3, 3, 2, False, False),   # k = E: every expert, soft mixture
+    (4, 6, 5, 1, 4, True, True),     # k = 1 renormalised: weight 1, no router gradient
+]
+
+
+def pin_backward_finite_differences():
+    for ci, (T, H, E, k, I, bias, renorm) in enumerate(_BWD_CASES):
+        x, wr, b, w13, w2 = _rand_case(T=T, H=H, E=E, k=k, I=I, seed=40 + ci, bias=bias)
+        r = np.random.default_rng(90 + ci)
+        dout = r.standard_normal((T, H))
+        g = O.backward(x, wr, b, w13, w2, k, renorm, dout)
+        params = {"x": x, "w_router": wr, "w13": w13, "w2": w2}
+        if bias:
+            params["bias"] = b
+        grads = {"x": g["dx"], "w_router": g["dw_router"], "bias": g["dbias"], "w13": g["dw13"],
+                 "w2": g["dw2"]}
+        ids0 = g["fw"]["ids"]
+        for name, val in params.items():
+            for trial in range(2):
+                V = r.standard_normal(val.shape)
+                eps = 1e-5
+                args = {"x": x, "w_router": wr, "bias": b, "w13": w13, "w2": w2}
+                args[name] = val + eps * V
+                fp, idp = _loss(args["x"], args["w_router"], args["bias"], args["w13"], args["w2"],
+                                k, renorm, dout)
+                args[name] = val - eps * V
+                fm, idm = _loss(args["x"], args["w_router"], args["bias"], args["w13"], args["w2"],
+                                k, renorm, dout)
+                assert np.array_equal(idp, ids0) and np.array_equal(idm, ids0), "selection moved"
+                fd = (fp - fm) / (2 * eps)
+                an = float((grads[name] * V).sum())
+                assert abs(fd - an) <= 1e-6 * (abs(an) + 1.0), (ci, name, fd, an)
+
+
+def pin_backward_special_cases():
+    # a single expert: p = 1, so the router receives no gradient at all
+    x, wr, b, w13, w2 = _rand_case(T=4, H=5, E=1, k=1, I=3, seed=3)
+    dout = np.random.default_rng(1).standard_normal((4, 5))
+    g = O.backward(x, wr, b, w13, w2, 1, False, dout)
+    assert np.array_equal(g["dw_router"], np.zeros_like(wr)) and np.array_equal(g["dbias"], np.zeros(1))
+    # the same block is then a plain SwiGLU MLP: torch's float64 autograd gives its gradients
+    xt = torch.tensor(x, requires_grad=True)
+    w13t = torch.tensor(w13[0], requires_grad=True)
+    w2t = torch.tensor(w2[0], requires_grad=True)
+    gt = torch.nn.functional.linear(xt, w13t[:3])
+    ut = torch.nn.functional.linear(xt, w13t[3:])
+    out = torch.nn.functional.linear(torch.nn.functional.silu(gt) * ut, w2t)
+    (out * torch.tensor(dout)).sum().backward()
+    assert np.allclose(g["dx"], xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dw13"][0], w13t.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dw2"][0], w2t.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # W2 = 0: every expert output is zero, so the routing weights, the logits
+    # and the gate/up weights receive nothing
+    x, wr, b, w13, w2 = _rand_case(T=6, H=5, E=4, k=2, I=3, seed=5)
+    dout = np.random.default_rng(2).standard_normal((6, 5))
+    g = O.backward(x, wr, b, w13, np.zeros_like(w2), 2, True, dout)
+    assert np.array_equal(g["dlogits"], np.zeros((6, 4))) and np.array_equal(g["dw13"], np.zeros_like(w13))
+    # experts no token chose get exactly zero gradients ([Hunyuan page] §二.2)
+    b2 = np.array([5.0, 5.0, -50.0, -50.0])
+    g = O.backward(x, wr, b2, w13, w2, 2, False, dout)
+    assert set(g["fw"]["ids"].ravel().tolist()) == {0, 1}
+    assert not g["dw13"][2:].any() and not g["dw2"][2:].any()
+    assert g["dw13"][:2].any() and g["dw2"][:2].any()
+    # linear in dout
+    g2 = O.backward(x, wr, b, w13, w2, 2, True, 2 * dout)
+    g1 = O.backward(x, wr, b, w13, w2, 2, True, dout)
+    for n in ("dx", "dw_router", "dbias", "dw13", "dw2"):
+        assert np.allclose(g2[n], 2 * g1[n], rtol=1e-12, atol=1e-14), n
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
 
 
@@ -754,6 +838,30 @@ def _mut_mx_no_floor(amax):
     return np.where(a > 0, np.clip(np.round(np.log2(np.where(a > 0, a, 1))) - 8, -127, 127), -127)
 
 
+_orig_expert_mlp_backward = O.expert_mlp_backward
+
+
+def _mut_silu_grad_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, float)))
+
+
+def _mut_weights_grad_no_mean(dw, probs_sel, renormalize):
+    dw = np.asarray(dw, float)
+    if not renormalize:
+        return dw
+    return dw / np.asarray(probs_sel, float).sum(axis=1, keepdims=True)
+
+
+def _mut_softmax_grad_uncentred(p, dp):
+    return np.asarray(p, float) * np.asarray(dp, float)
+
+
+def _mut_expert_bwd_swapped(xe, w13_e, w2_e, dy):
+    dxe, dw13, dw2 = _orig_expert_mlp_backward(xe, w13_e, w2_e, dy)
+    I = dw13.shape[0] // 2
+    return dxe, np.concatenate([dw13[I:], dw13[:I]]), dw2
+
+
 MUTATIONS = {
     "topk ties to the highest index": ("topk_ids", _mut_topk_ties_high),
     "topk slots ascending": ("topk_ids", _mut_topk_ascending_slots),
@@ -778,6 +886,10 @@ MUTATIONS = {
     "e4m3 overflow to NaN": ("e4m3_encode", _mut_e4m3_no_saturation),
     "MX scale exponent one too large": ("_mx_exponent", _mut_mx_emax7),
     "MX scale exponent rounded": ("_mx_exponent", _mut_mx_no_floor),
+    "silu gradient without its z s (1 - s) term": ("silu_grad", _mut_silu_grad_sigmoid),
+    "renormalisation gradient without the mean term": ("weights_grad", _mut_weights_grad_no_mean),
+    "softmax gradient not centred": ("softmax_grad", _mut_softmax_grad_uncentred),
+    "gate and up gradients swapped": ("expert_mlp_backward", _mut_expert_bwd_swapped),
 }
 
 
