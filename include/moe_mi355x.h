@@ -441,6 +441,98 @@ int moe_forward_mxfp8_layout(int64_t T, int32_t H, int32_t I, int32_t E,
                              moe_mxfp8_layout* layout);
 
 /*
+ * Backward
+ * --------
+ * moe_backward -- the gradients of L = sum(dout * out) for the block of
+ * moe_forward, with the top-k choice held fixed (it is piecewise constant):
+ * dx, the router weight and bias, W13 and W2.  Following [SonicMoE page]
+ * 核心差异 §1, the forward keeps only its routing and its expert outputs y
+ * (in the moe_forward workspace) and the backward recomputes the rest: g and
+ * u by the grouped GEMM, h from them.  Per [Hunyuan page] §二.2 only the
+ * experts a token activated get gradients (the others' come out zero).
+ *   dw[t,j] = <dout_t, y_tj>;  through the renormalisation (renormalize != 0)
+ *   and the softmax, dl = dL/dlogits; dx = sum_j [dg du] W13_e + dl W_r;
+ *   dW_r = dl^T x; dbias = sum_t dl; dW2_e = sum (w dout)^T h;
+ *   dW13_e = sum [dg du]^T x, with dh = (w dout) W2_e, dg = dh u silu'(g),
+ *   du = dh silu(g).
+ * dtype must be MOE_DTYPE_BF16 (bf16 operands, fp32 accumulation; g, u, dh,
+ * dg, du, h and the per-slot dx rounded to bf16 once).
+ *   x, w_router, router_bias, w13, w2, sizes, renormalize: exactly as passed
+ *               to the moe_forward call whose workspace is given.
+ *   forward_workspace  that call's workspace (moe_forward_workspace_layout
+ *               size), left unchanged since; read only.
+ *   dout        [T,H] bf16, device.
+ *   dx          [T,H] bf16, device, output.
+ *   dw_router   [E,H] fp32, device, output.
+ *   dbias       [E] fp32, device, output, or NULL (not computed).
+ *   dw13        [E,2I,H] fp32, device, output (layout of w13).
+ *   dw2         [E,H,I] fp32, device, output (layout of w2).
+ *   workspace   moe_backward_workspace_layout(...).total bytes, device, 256-byte
+ *               aligned; afterwards it holds the intermediates at the
+ *               layout's offsets.
+ * Limits as moe_forward, plus T*H*2 <= 2^32.  Deterministic (no atomics).
+ */
+int moe_backward(const void* x, const void* w_router, const float* router_bias,
+                 const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
+                 int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
+                 const void* forward_workspace, size_t forward_workspace_bytes,
+                 const void* dout, void* dx, float* dw_router, float* dbias,
+                 float* dw13, float* dw2, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * moe_backward_profiled -- moe_backward recording caller-created HIP events
+ * around its stages, n_events == MOE_PROFILE_EVENTS_BACKWARD:
+ *   0 router gradients (dw, the router's logits again, dl, dl W_r, dW_r, dbias)
+ *   1 transposed copies of W13 and W2
+ *   2 g and u again (grouped GEMM)
+ *   3 dh (grouped GEMM) and the SwiGLU backward (dg, du, h)
+ *   4 dx: [dg du] W13 (grouped GEMM) and the sum over a token's slots
+ *   5 transposed operands of the weight-gradient GEMMs
+ *   6 dW2 (grouped GEMM over each expert's rows)
+ *   7 dW13 (same)
+ */
+#define MOE_PROFILE_EVENTS_BACKWARD 9
+int moe_backward_profiled(const void* x, const void* w_router,
+                          const float* router_bias, const void* w13,
+                          const void* w2, int64_t T, int32_t H, int32_t I,
+                          int32_t E, int32_t k, int32_t dtype,
+                          int32_t renormalize, const void* forward_workspace,
+                          size_t forward_workspace_bytes, const void* dout,
+                          void* dx, float* dw_router, float* dbias,
+                          float* dw13, float* dw2, void* workspace,
+                          size_t workspace_bytes, void* const* events,
+                          int32_t n_events, void* stream);
+
+/* Byte offsets of the moe_backward workspace regions (M = T*k; ld = the
+ * padded row count of the weight-gradient operands). */
+typedef struct moe_backward_layout {
+    size_t dw;           /* [T,k] fp32: dL/d(routing weight) */
+    size_t dlogits;      /* [T,E] fp32: dL/d(router logit) */
+    size_t dx_router;    /* [T,H] bf16: dl W_r */
+    size_t gu;           /* [M,2I] bf16: g then u of each expert-sorted row */
+    size_t dh;           /* [M,I] bf16: dout W2_e (before the routing weight) */
+    size_t dgdu;         /* [M,2I] bf16: dg then du */
+    size_t h;            /* [M,I] bf16: silu(g) u */
+    size_t dx_slots;     /* [M,H] bf16: [dg du] W13_e, row t*k+j */
+    size_t w13t;         /* [E,H,2I] bf16 */
+    size_t w2t;          /* [E,I,H] bf16 */
+    size_t padded_offsets; /* [E+1] int32: column offsets of the experts in the operands below */
+    size_t dyT;          /* [H,ld] bf16 */
+    size_t hT;           /* [I,ld] bf16 */
+    size_t dgduT;        /* [2I,ld] bf16 */
+    size_t xT;           /* [H,ld] bf16 */
+    size_t ld;           /* elements */
+    size_t scratch;
+    size_t total;
+} moe_backward_layout;
+
+/* Host-only.  Fills *layout; validates the sizes as moe_backward. */
+int moe_backward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E,
+                                  int32_t k, int32_t dtype,
+                                  moe_backward_layout* layout);
+
+/*
  * Host-only.  Workspace bytes needed by `entry` (a moe_entry) for these
  * sizes, written to *bytes (host pointer).  For MOE_ENTRY_GROUPED_GEMM pass
  * T = M and k = 1.  Sizes that the entry ignores may be given as 1.

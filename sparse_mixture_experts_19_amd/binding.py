@@ -39,6 +39,12 @@ class SharedLayout(ctypes.Structure):
         "h_shared", "y_shared", "scratch", "total")]
 
 
+class BackwardLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "dw", "dlogits", "dx_router", "gu", "dh", "dgdu", "h", "dx_slots", "w13t", "w2t",
+        "padded_offsets", "dyT", "hT", "dgduT", "xT", "ld", "scratch", "total")]
+
+
 class Mxfp8Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_ids", "topk_weights", "expert_counts", "expert_offsets", "perm", "inv_perm",
@@ -60,6 +66,9 @@ _SIGS = {
     "moe_forward_rounded_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_gemm_tile_rows": [_c_i32],
     "moe_mx_quantize": [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp],
+    "moe_backward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_backward_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_backward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(BackwardLayout)],
     "moe_forward_mxfp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
     "moe_forward_mxfp8_profiled": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
     "moe_forward_mxfp8_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(Mxfp8Layout)],
@@ -446,4 +455,75 @@ def mxfp8_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int
         h_codes=view(L.h_codes, M * I, torch.uint8, 1, (M, I)),
         h_scales=view(L.h_scales, M * I // 32, torch.uint8, 1, (M, I // 32)),
         y=view(L.y, M * H, torch.bfloat16, 2, (M, H)),
+    )
+
+
+def backward_layout(T: int, H: int, I: int, E: int, k: int,
+                    dtype: int = MOE_DTYPE_BF16) -> BackwardLayout:
+    L = BackwardLayout()
+    _check(lib().moe_backward_workspace_layout(T, H, I, E, k, dtype, ctypes.byref(L)))
+    return L
+
+
+PROFILE_EVENTS_BACKWARD = 9
+PROFILE_STAGES_BACKWARD = ("router_grads", "weight_transpose", "recompute_gate_up", "dgrad_down_swiglu",
+                           "dgrad_gate_up", "wgrad_transpose", "wgrad_down", "wgrad_gate_up")
+
+
+def moe_backward(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, forward_ws, dout,
+                 dx=None, dw_router=None, dbias=None, dw13=None, dw2=None, workspace=None,
+                 events=None, want_dbias: bool = True):
+    """Gradients of sum(dout * out) for the moe_forward call that left
+    ``forward_ws``.  Returns (dx, dw_router, dbias, dw13, dw2, workspace); the
+    weight gradients are float32.  With ``events`` (9 timing events) the
+    stages are recorded as PROFILE_STAGES_BACKWARD."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, H), dtype=x.dtype, device=dev)
+    if dw_router is None:
+        dw_router = torch.empty((E, H), dtype=torch.float32, device=dev)
+    if dbias is None and want_dbias:
+        dbias = torch.empty(E, dtype=torch.float32, device=dev)
+    if dw13 is None:
+        dw13 = torch.empty((E, I2, H), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((E, H, I), dtype=torch.float32, device=dev)
+    ws = _workspace(backward_layout(T, H, I, E, k, dt).total, dev, workspace)
+    args = [_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2), T, H, I, E, k, dt,
+            int(bool(renormalize)), _ptr(forward_ws), forward_ws.numel() * forward_ws.element_size(),
+            _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dbias), _ptr(dw13), _ptr(dw2), _ptr(ws),
+            ws.numel() * ws.element_size()]
+    if events is None:
+        _check(lib().moe_backward(*args, _stream(dev)))
+    else:
+        if len(events) != PROFILE_EVENTS_BACKWARD:
+            raise ValueError(f"need {PROFILE_EVENTS_BACKWARD} events")
+        handles = (ctypes.c_void_p * PROFILE_EVENTS_BACKWARD)(*[ev.cuda_event for ev in events])
+        _check(lib().moe_backward_profiled(*args, handles, PROFILE_EVENTS_BACKWARD, _stream(dev)))
+    return dx, dw_router, dbias, dw13, dw2, ws
+
+
+def backward_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int):
+    """Typed views of the intermediates moe_backward leaves in its workspace."""
+    L = backward_layout(T, H, I, E, k)
+    M = T * k
+
+    def view(off, n, dt, esz, shape):
+        return ws[off:off + n * esz].view(dt).view(shape)
+
+    bf = torch.bfloat16
+    return dict(
+        dw=view(L.dw, M, torch.float32, 4, (T, k)),
+        dlogits=view(L.dlogits, T * E, torch.float32, 4, (T, E)),
+        dx_router=view(L.dx_router, T * H, bf, 2, (T, H)),
+        gu=view(L.gu, M * 2 * I, bf, 2, (M, 2 * I)),
+        dh=view(L.dh, M * I, bf, 2, (M, I)),
+        dgdu=view(L.dgdu, M * 2 * I, bf, 2, (M, 2 * I)),
+        h=view(L.h, M * I, bf, 2, (M, I)),
+        dx_slots=view(L.dx_slots, M * H, bf, 2, (M, H)),
+        padded_offsets=view(L.padded_offsets, E + 1, torch.int32, 4, (E + 1,)),
     )

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "route.hip", "permute.hip", "round.hip", "gemm_mfma.hip", "gemm_f32.hip", "mxfp8.hip",
+SOURCES = ["api.hip", "route.hip", "permute.hip", "round.hip", "gemm_mfma.hip", "gemm_f32.hip", "mxfp8.hip", "backward.hip",
            "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -255,7 +255,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 103; }
+int moe_version(void) { return 104; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -826,6 +826,232 @@ int moe_forward_mxfp8_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t
   if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
   MOE_CHECK(check_mxfp8(T, H, I, E, k, dtype));
   *layout = mxfp8_layout(T, H, I, E, k);
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_backward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t dtype) {
+  MOE_CHECK(check_sizes(T, H, I, E, k, dtype, true));
+  if (dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_backward needs dtype MOE_DTYPE_BF16");
+  if (!moe::gemm_gather_fits(T, H, 2))
+    return fail(MOE_ERR_UNSUPPORTED, "T*H*2 (%lld) exceeds 2^32", (long long)(T * H * 2));
+  return MOE_OK;
+}
+
+// Padded row count of the weight-gradient operands: every expert's rows
+// rounded up to a multiple of 64, and at least 64.
+int64_t backward_ld(int64_t M, int E) { return (M + 63) / 64 * 64 + 64 * static_cast<int64_t>(E); }
+
+// Workspace of moe_backward: the public regions, then the scratch (routing
+// recompute, dW_r partials, small tables, ones, grouped-GEMM scratch).
+struct BwdScratch {
+  size_t route, ids, wts, dwr_part, tables, ones, gemm, end;
+};
+moe_backward_layout backward_layout(int64_t T, int H, int I, int E, int k, BwdScratch* sc = nullptr) {
+  const size_t M = static_cast<size_t>(T) * k;
+  const int64_t ld = backward_ld(static_cast<int64_t>(M), E);
+  Carver c;
+  moe_backward_layout L;
+  L.dw = c.take(M * 4);
+  L.dlogits = c.take(static_cast<size_t>(T) * E * 4);
+  L.dx_router = c.take(static_cast<size_t>(T) * H * 2);
+  L.gu = c.take(M * 2 * I * 2);
+  L.dh = c.take(M * I * 2);
+  L.dgdu = c.take(M * 2 * I * 2);
+  L.h = c.take(M * I * 2);
+  L.dx_slots = c.take(M * H * 2);
+  L.w13t = c.take(static_cast<size_t>(E) * 2 * I * H * 2);
+  L.w2t = c.take(static_cast<size_t>(E) * H * I * 2);
+  L.padded_offsets = c.take(static_cast<size_t>(E + 1) * 4);
+  L.dyT = c.take(static_cast<size_t>(H) * ld * 2);
+  L.hT = c.take(static_cast<size_t>(I) * ld * 2);
+  L.dgduT = c.take(static_cast<size_t>(2 * I) * ld * 2);
+  L.xT = c.take(static_cast<size_t>(H) * ld * 2);
+  L.ld = static_cast<size_t>(ld);
+  L.scratch = c.o;
+  BwdScratch b;
+  b.route = c.take(moe::route_scratch_bytes(T, H, E, true));
+  b.ids = c.take(M * 4);
+  b.wts = c.take(M * 4);
+  b.dwr_part = c.take(static_cast<size_t>(moe::bwd_dwr_slices(T)) * E * H * 4);
+  b.tables = c.take(static_cast<size_t>(E + 1) * 4 * 4);
+  b.ones = c.take(M * 4);
+  b.gemm = c.take(gemm_prefix_bytes(E) +
+                  static_cast<size_t>(moe::gemm_pieces(static_cast<int64_t>(M), H, 2 * I, E, false)) *
+                      moe::kGemmBM * moe::kGemmBN * 4);
+  b.end = c.o;
+  L.total = c.o;
+  if (sc) *sc = b;
+  return L;
+}
+
+int backward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
+                  const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                  int32_t dtype, int32_t renormalize, const void* fws, size_t fws_bytes,
+                  const void* dout, void* dx, float* dwr, float* dbias, float* dw13, float* dw2,
+                  void* workspace, size_t workspace_bytes, void* const* events, hipStream_t s) {
+  MOE_CHECK(check_backward(T, H, I, E, k, dtype));
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(x, "x", 16));
+  MOE_CHECK(need_ptr(w_router, "w_router", 16));
+  if (router_bias) MOE_CHECK(need_ptr(router_bias, "router_bias", 4));
+  MOE_CHECK(need_ptr(w13, "w13", 16));
+  MOE_CHECK(need_ptr(w2, "w2", 16));
+  MOE_CHECK(need_ptr(dout, "dout", 16));
+  MOE_CHECK(need_ptr(dx, "dx", 16));
+  MOE_CHECK(need_ptr(dwr, "dw_router", 16));
+  if (dbias) MOE_CHECK(need_ptr(dbias, "dbias", 4));
+  MOE_CHECK(need_ptr(dw13, "dw13", 16));
+  MOE_CHECK(need_ptr(dw2, "dw2", 16));
+  const moe_forward_layout F = forward_layout(T, H, I, E, k, dtype);
+  if (!fws || fws_bytes < F.total)
+    return fail(MOE_ERR_WORKSPACE, "forward_workspace must hold %zu bytes (the moe_forward workspace), got %zu",
+                F.total, fws_bytes);
+  MOE_CHECK(need_ptr(fws, "forward_workspace", 256));
+  BwdScratch b;
+  const moe_backward_layout L = backward_layout(T, H, I, E, k, &b);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", L.total,
+                workspace_bytes);
+  MOE_CHECK(need_ptr(workspace, "workspace", 256));
+  if (events)
+    for (int i = 0; i < MOE_PROFILE_EVENTS_BACKWARD; ++i)
+      if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  int cu = 0;
+  MOE_CHECK(current_device(nullptr, &cu));
+  const char* f = static_cast<const char*>(fws);
+  const int32_t* ids = reinterpret_cast<const int32_t*>(f + F.topk_ids);
+  const float* wts = reinterpret_cast<const float*>(f + F.topk_weights);
+  const int32_t* counts = reinterpret_cast<const int32_t*>(f + F.expert_counts);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(f + F.expert_offsets);
+  const int32_t* perm = reinterpret_cast<const int32_t*>(f + F.perm);
+  const void* y = f + F.y;
+  char* w = static_cast<char*>(workspace);
+  float* dw = reinterpret_cast<float*>(w + L.dw);
+  float* dl = reinterpret_cast<float*>(w + L.dlogits);
+  int32_t* tab = reinterpret_cast<int32_t*>(w + b.tables);
+  int32_t* poff = reinterpret_cast<int32_t*>(w + L.padded_offsets);
+  int32_t* goff_h = tab;
+  int32_t* pre_h = tab + (E + 1);
+  int32_t* goff_i = tab + 2 * (E + 1);
+  int32_t* pre_i = tab + 3 * (E + 1);
+  float* ones = reinterpret_cast<float*>(w + b.ones);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + b.gemm);
+  const int64_t M = T * k;
+  const int64_t ld = static_cast<int64_t>(L.ld);
+  const int pieces = moe::gemm_pieces(M, H, 2 * I, E, false);
+  int next_event = 0;
+  auto mark = [&]() -> int {
+    if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[next_event]), s));
+    ++next_event;
+    return MOE_OK;
+  };
+
+  // 0: router gradients
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_bwd_dw(dout, y, T, H, k, dw, s));
+  moe::RouteArgs ra{};
+  MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize,
+                      reinterpret_cast<int32_t*>(w + b.ids), reinterpret_cast<float*>(w + b.wts),
+                      w + b.route, s, &ra));
+  MOE_HIP(moe::launch_bwd_router(ra.logits, ra.meta, ids, dw, T, E, k, renormalize, dl, s));
+  MOE_HIP(moe::launch_bwd_router_grads(dl, x, w_router, T, H, E, w + L.dx_router, dwr, dbias,
+                                       reinterpret_cast<float*>(w + b.dwr_part), s));
+  // 1: transposed weights
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_transpose(w13, w + L.w13t, E, 2 * I, H, s));
+  MOE_HIP(moe::launch_transpose(w2, w + L.w2t, E, H, I, s));
+  // 2: g and u again
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
+  moe::GemmArgs g{};
+  g.E = E; g.offsets = offsets; g.prefix = prefix; g.M = M; g.I = I;
+  g.grid = cu >= 8 ? cu / 8 * 8 : 8;
+  g.partials = reinterpret_cast<float*>(w + b.gemm + gemm_prefix_bytes(E));
+  g.max_pieces = pieces;
+  g.A = x; g.gather = perm; g.gather_div = k; g.a_rows = T;
+  g.B = w13; g.C = w + L.gu; g.N = 2 * I; g.K = H;
+  MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
+  // 3: dh = dout W2_e, then the SwiGLU backward
+  MOE_CHECK(mark());
+  g.A = dout; g.B = w + L.w2t; g.C = w + L.dh; g.N = I; g.K = H;
+  MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
+  MOE_HIP(moe::launch_bwd_swiglu(w + L.dh, w + L.gu, wts, perm, M, I, w + L.dgdu, w + L.h, s));
+  // 4: dx = sum over a token's slots of [dg du] W13_e, plus dl W_r
+  MOE_CHECK(mark());
+  g.A = w + L.dgdu; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
+  g.B = w + L.w13t; g.C = w + L.dx_slots; g.N = H; g.K = 2 * I; g.scatter = perm;
+  MOE_HIP(moe::launch_gemm_bf16_down(g, s));
+  MOE_HIP(moe::launch_fill(ones, M, 1.f, s));
+  MOE_HIP(moe::launch_combine(w + L.dx_slots, nullptr, ones, T, H, k, true, dx, s, w + L.dx_router));
+  // 5: transposed, padded operands of the weight-gradient GEMMs
+  MOE_CHECK(mark());
+  MOE_HIP(moe::launch_bwd_tables(counts, E, H, I, poff, goff_h, pre_h, goff_i, pre_i, s));
+  MOE_HIP(moe::launch_gather_transpose(dout, H, perm, true, k, wts, offsets, counts, poff, E, ld,
+                                       w + L.dyT, s));
+  MOE_HIP(moe::launch_gather_transpose(w + L.h, I, perm, false, k, nullptr, offsets, counts, poff, E,
+                                       ld, w + L.hT, s));
+  MOE_HIP(moe::launch_gather_transpose(w + L.dgdu, 2 * I, perm, false, k, nullptr, offsets, counts,
+                                       poff, E, ld, w + L.dgduT, s));
+  MOE_HIP(moe::launch_gather_transpose(x, H, perm, true, k, nullptr, offsets, counts, poff, E, ld,
+                                       w + L.xT, s));
+  // 6: dW2_e = sum (w dout)^T h over the expert's rows
+  MOE_CHECK(mark());
+  moe::GemmArgs v{};
+  v.E = E; v.koff = poff; v.ld = ld; v.grid = g.grid;
+  v.offsets = goff_h; v.prefix = pre_h; v.group_rows = H; v.M = static_cast<int64_t>(E) * H;
+  v.A = w + L.dyT; v.B = w + L.hT; v.N = I; v.Cf = dw2; v.a_rows = H;
+  MOE_HIP(moe::launch_gemm_bf16_wgrad(v, s));
+  // 7: dW13_e = sum [dg du]^T x over the expert's rows
+  MOE_CHECK(mark());
+  v.offsets = goff_i; v.prefix = pre_i; v.group_rows = 2 * I; v.M = static_cast<int64_t>(E) * 2 * I;
+  v.A = w + L.dgduT; v.B = w + L.xT; v.N = H; v.Cf = dw13; v.a_rows = 2 * I;
+  MOE_HIP(moe::launch_gemm_bf16_wgrad(v, s));
+  MOE_CHECK(mark());
+  if (next_event != MOE_PROFILE_EVENTS_BACKWARD)
+    return fail(MOE_ERR_UNSUPPORTED, "internal: %d stage events recorded, %d expected", next_event,
+                MOE_PROFILE_EVENTS_BACKWARD);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_backward(const void* x, const void* w_router, const float* router_bias, const void* w13,
+                 const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                 int32_t dtype, int32_t renormalize, const void* forward_workspace,
+                 size_t forward_workspace_bytes, const void* dout, void* dx, float* dw_router,
+                 float* dbias, float* dw13, float* dw2, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return backward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize,
+                       forward_workspace, forward_workspace_bytes, dout, dx, dw_router, dbias, dw13,
+                       dw2, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int moe_backward_profiled(const void* x, const void* w_router, const float* router_bias,
+                          const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
+                          int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
+                          const void* forward_workspace, size_t forward_workspace_bytes,
+                          const void* dout, void* dx, float* dw_router, float* dbias, float* dw13,
+                          float* dw2, void* workspace, size_t workspace_bytes, void* const* events,
+                          int32_t n_events, void* stream) {
+  if (!events || n_events != MOE_PROFILE_EVENTS_BACKWARD)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_BACKWARD (%d) handles",
+                MOE_PROFILE_EVENTS_BACKWARD);
+  return backward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize,
+                       forward_workspace, forward_workspace_bytes, dout, dx, dw_router, dbias, dw13,
+                       dw2, workspace, workspace_bytes, events, static_cast<hipStream_t>(stream));
+}
+
+int moe_backward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  int32_t dtype, moe_backward_layout* layout) {
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  MOE_CHECK(check_backward(T, H, I, E, k, dtype));
+  *layout = backward_layout(T, H, I, E, k);
   return ok();
 }
 

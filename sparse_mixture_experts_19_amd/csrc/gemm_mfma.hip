@@ -177,7 +177,7 @@ __device__ __forceinline__ Split split_work(int total, int G, int nk, int max_pi
   return sp;
 }
 
-template <bool MX, bool SWIGLU, bool GATHER>
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // two stage buffers as distinct arrays (each holds the A rows then the B
   // rows of one 128-byte K stage)
@@ -189,11 +189,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   __shared__ uint32_t SSC[MX ? 2 * 512 : 1];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
+  __shared__ int s_koff[WG ? kMaxE + 1 : 1];   // WG: K range of each group, in stages
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int E = a.E;
-  for (int i = tid; i <= E; i += 256) { s_off[i] = a.offsets[i]; s_pre[i] = a.prefix[i]; }
+  for (int i = tid; i <= E; i += 256) {
+    s_off[i] = a.offsets[i];
+    s_pre[i] = a.prefix[i];
+    if constexpr (WG) s_koff[i] = a.koff[i] / BK;
+  }
   __syncthreads();
 
   constexpr int NOUT = SWIGLU ? BN / 2 : BN;   // output columns per tile
@@ -240,7 +245,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     } else {
       return 0;
     }
-    return decode_tile(L, NT, NOUT, E, s_pre, s_off, a.M, it.t) ? 1 : 2;
+    if (!decode_tile(L, NT, NOUT, E, s_pre, s_off, a.M, it.t)) return 2;
+    if constexpr (WG) {
+      it.k0 = s_koff[it.t.e];
+      it.k1 = s_koff[it.t.e + 1];
+      if (it.k1 <= it.k0) return 2;
+    }
+    return 1;
   };
   auto next_item = [&](int i, Item& it) -> int {   // index of the first item >= i, or -1
     for (;; ++i) {
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // from bases that move by 4 bytes per stage.
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);
-  const uint64_t rowbytes = static_cast<uint64_t>(K) * (MX ? 1 : 2);
+  const uint64_t rowbytes = WG ? static_cast<uint64_t>(a.ld) * 2 : static_cast<uint64_t>(K) * (MX ? 1 : 2);
   const uint32_t rb32 = static_cast<uint32_t>(rowbytes);
   const char* Ach = static_cast<const char*>(a.A);
   const char* Bch = reinterpret_cast<const char*>(Bb);
@@ -320,7 +331,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
         const int ri = lrow + 32 * j;
         voff[j] = static_cast<uint32_t>(ri < t.rows ? ri : t.rows - 1) * rb32 + lchunk * 16;
       }
-      dA = Ach + static_cast<uint64_t>(t.r0) * rowbytes;
+      // WG: the rows of group e are rows 0.. of A (its K range selects the expert)
+      dA = Ach + static_cast<uint64_t>(WG ? t.r0 - t.e * a.group_rows : t.r0) * rowbytes;
     }
     if constexpr (SWIGLU) {
       const int nb = a.I - t.n0;          // rows of each half left from n0
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
         const int rr = lrow + 32 * j;
         voff[8 + j] = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * rb32 + lchunk * 16;
       }
-      dB0 = Bch + (static_cast<uint64_t>(t.e) * N + t.n0) * rowbytes;
+      dB0 = Bch + (static_cast<uint64_t>(WG ? 0 : t.e) * N + t.n0) * rowbytes;
       dB1 = dB0;
     }
   };
@@ -697,6 +709,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
             *reinterpret_cast<float4*>(P + row * BN + wrow) = v;
             __builtin_amdgcn_sched_barrier(0);
           }
+    } else if constexpr (WG) {
+      // ---- weight gradient: fp32 sums straight to Cf (row-major, N columns)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int grp = 0; grp < 4; ++grp) {
+            const int row = wm * 128 + i * 32 + (lane & 31);
+            const int col = ci.t.n0 + wn * 128 + 32 * j + 8 * grp + 4 * (lane >> 5);
+            float4 v;
+            v.x = acc_rd(acc[i][j][4 * grp]);
+            v.y = acc_rd(acc[i][j][4 * grp + 1]);
+            v.z = acc_rd(acc[i][j][4 * grp + 2]);
+            v.w = acc_rd(acc[i][j][4 * grp + 3]);
+            if (row < ci.t.rows && col < N)
+              *reinterpret_cast<float4*>(a.Cf + static_cast<int64_t>(ci.t.r0 + row) * N + col) = v;
+            __builtin_amdgcn_sched_barrier(0);
+          }
     } else if constexpr (MX && SWIGLU) {
       // ---- MXFP8 epilogue: h = silu(g) * u quantized along its columns.
       // Per 32x32 result tile a lane holds 16 of the 32 columns of one token
@@ -919,9 +950,10 @@ __global__ __launch_bounds__(256) void gemm_mx_swiglu_fixup_kernel(GemmArgs a) {
   }
 }
 
-template <bool MX, bool SWIGLU, bool GATHER>
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER, WG>), dim3(a.grid), dim3(256), 0, s, a);
+  if constexpr (WG) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_pieces < 2 || a.K / stage_k<MX>() < 2 * kMinPiece) return e;
   if constexpr (MX && SWIGLU)
@@ -978,6 +1010,26 @@ hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
 
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s) {
   return launch<false, false, false>(a, s);
+}
+
+hipError_t launch_gemm_bf16_plain(const GemmArgs& a0, hipStream_t s) {
+  if (!a0.gather) return launch<false, false, false>(a0, s);
+  if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 2)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  set_gather_magic(a);
+  return launch<false, false, true>(a, s);
+}
+
+hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a0, hipStream_t s) {
+  if (!a0.koff || !a0.Cf || a0.ld <= 0 || a0.ld % BK || a0.group_rows <= 0 || a0.N % 64 ||
+      a0.ld * 2 * BM > (int64_t{1} << 32))
+    return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.K = BK;              // the K loop is per group; no tile is cut along K
+  a.max_pieces = 0;
+  a.gather = nullptr;
+  a.scatter = nullptr;
+  return launch<false, false, false, true>(a, s);
 }
 
 hipError_t launch_gemm_mx_swiglu(const GemmArgs& a0, hipStream_t s) {

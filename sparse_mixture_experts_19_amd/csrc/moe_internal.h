@@ -109,6 +109,14 @@ struct GemmArgs {
   const uint8_t* a_scale; // [*, K/32], rows as A (gathered like A)
   const uint8_t* b_scale; // [E, rows of an expert, K/32]
   uint8_t* c_scale;       // SwiGLU: scales of h [M, N/32] (h itself: e4m3 codes in C)
+  // Weight-gradient form (launch_gemm_bf16_wgrad): group g owns output rows
+  // [g*group_rows, (g+1)*group_rows) and reduces over the K range
+  // [koff[g], koff[g+1]) (multiples of 64) of A and B, whose rows have pitch ld
+  // elements; fp32 results go to Cf [E*group_rows, N].
+  const int32_t* koff;    // [E+1] device
+  int64_t ld;
+  int64_t group_rows;
+  float* Cf;
 };
 // Partial-sum slots the MFMA GEMMs (mx: MXFP8) of an [M rows, H, I, E]
 // expert MLP can use.
@@ -117,6 +125,10 @@ int gemm_pieces(int64_t M, int H, int I, int E, bool mx);
 bool gemm_gather_fits(int64_t a_rows, int K, int elem_bytes);
 hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
+// The down kernel's plain product C = A B^T with A rows gathered (gather != null).
+hipError_t launch_gemm_bf16_plain(const GemmArgs& a, hipStream_t s);
+// Weight gradients: per group g, Cf rows of g = A[rows of g] B^T over K range g.
+hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a, hipStream_t s);
 // MXFP8 operands: K a multiple of 128; SwiGLU: N (= I) a multiple of 128;
 // the down GEMM writes bf16 rows.
 hipError_t launch_gemm_mx_swiglu(const GemmArgs& a, hipStream_t s);
@@ -151,6 +163,32 @@ hipError_t launch_token_round(const RoundArgs& a, hipStream_t s);
 // [rows, cols] and E8M0 scales [rows, cols/32].
 hipError_t launch_mx_quantize(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+
+// ------------------------------------------------------ backward (backward.hip)
+hipError_t launch_bwd_dw(const void* dout, const void* y, int64_t T, int H, int k, float* dw,
+                         hipStream_t s);
+hipError_t launch_bwd_router(const float* logits, const float* meta, const int32_t* ids,
+                             const float* dw, int64_t T, int E, int k, int renorm, float* dl,
+                             hipStream_t s);
+// Token slices of the dW_r reduction (partials: slices x E x H fp32).
+int bwd_dwr_slices(int64_t T);
+// dxr = dl W_r (bf16), dwr = dl^T x (fp32), db = column sums of dl (null: skipped).
+hipError_t launch_bwd_router_grads(const float* dl, const void* x, const void* w_router, int64_t T,
+                                   int H, int E, void* dxr, float* dwr, float* db, float* part,
+                                   hipStream_t s);
+// batch x [R, C] -> batch x [C, R] (bf16; R, C multiples of 64)
+hipError_t launch_transpose(const void* src, void* dst, int batch, int R, int C, hipStream_t s);
+// poff [E+1] padded expert segments; goff/pre [E+1] row offsets and tile
+// prefixes of the two weight-gradient GEMMs (H and 2I rows per expert).
+hipError_t launch_bwd_tables(const int32_t* counts, int E, int H, int I, int32_t* poff,
+                             int32_t* goff_h, int32_t* pre_h, int32_t* goff_i, int32_t* pre_i,
+                             hipStream_t s);
+hipError_t launch_gather_transpose(const void* src, int C, const int32_t* perm, bool gather, int k,
+                                   const float* scale, const int32_t* offsets, const int32_t* counts,
+                                   const int32_t* poff, int E, int64_t ld, void* dst, hipStream_t s);
+hipError_t launch_bwd_swiglu(const void* dh, const void* gu, const float* wts, const int32_t* perm,
+                             int64_t M, int I, void* dgdu, void* h, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 // ------------------------------------------------------ combine (combine.hip)
 // inv != null: slot (t, j) is row inv[t*k+j] of y; inv == null: row t*k+j.

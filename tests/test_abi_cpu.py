@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 103
+    assert L.moe_version() == 104
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -224,6 +224,42 @@ def test_mxfp8_layout_and_argument_errors():
     assert L.moe_mx_quantize(FAKE, 4, 32, 1, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_mx_quantize(FAKE + 8, 4, 32, 1, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_mx_quantize(None, 0, 32, 1, None, None, None) == B.MOE_OK
+
+
+def test_backward_layout_and_argument_errors():
+    T, H, I, E, k = 4096, 4096, 14336, 8, 2
+    M = T * k
+    Lb = B.backward_layout(T, H, I, E, k)
+    assert Lb.ld % 64 == 0 and Lb.ld >= M + 64 * E
+    offs = [Lb.dw, Lb.dlogits, Lb.dx_router, Lb.gu, Lb.dh, Lb.dgdu, Lb.h, Lb.dx_slots, Lb.w13t,
+            Lb.w2t, Lb.padded_offsets, Lb.dyT, Lb.hT, Lb.dgduT, Lb.xT, Lb.scratch, Lb.total]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    assert Lb.dh - Lb.gu >= M * 2 * I * 2 and Lb.w2t - Lb.w13t >= E * 2 * I * H * 2
+    assert Lb.scratch - Lb.xT >= H * Lb.ld * 2
+    L = B.lib()
+    fw = B.forward_layout(8, 128, 128, 4, 2, B.MOE_DTYPE_BF16).total
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("wr", FAKE), ("b", None), ("w13", FAKE), ("w2", FAKE), ("T", 8), ("H", 128),
+        ("I", 128), ("E", 4), ("k", 2), ("dt", 1), ("ren", 0), ("fws", FAKE), ("fwsb", fw),
+        ("dout", FAKE), ("dx", FAKE), ("dwr", FAKE), ("db", None), ("dw13", FAKE), ("dw2", FAKE),
+        ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert L.moe_backward(*args(dt=0)) == B.MOE_ERR_UNSUPPORTED             # bf16 only
+    assert L.moe_backward(*args(k=5)) == B.MOE_ERR_INVALID_ARG              # k > E
+    assert L.moe_backward(*args(I=100)) == B.MOE_ERR_UNSUPPORTED            # I % 64
+    assert L.moe_backward(*args(dout=None)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_backward(*args(dw2=FAKE + 4)) == B.MOE_ERR_INVALID_ARG     # misaligned
+    assert L.moe_backward(*args(fwsb=fw - 1)) == B.MOE_ERR_WORKSPACE        # forward workspace too small
+    assert L.moe_backward(*args(fws=None)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_backward(*args(wsb=1024)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_backward(*args(T=0, x=None, dout=None, dx=None, fws=None, fwsb=0, ws=None,
+                                wsb=0)) == B.MOE_OK
+    assert L.moe_backward_profiled(*args()[:-1], None, 0, None) == B.MOE_ERR_INVALID_ARG
+    ev = (ctypes.c_void_p * 9)(*([FAKE] * 9))
+    assert L.moe_backward_profiled(*args()[:-1], ev, 8, None) == B.MOE_ERR_INVALID_ARG
+    lay = B.BackwardLayout()
+    assert L.moe_backward_workspace_layout(8, 128, 128, 4, 2, 0, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_backward_workspace_layout(8, 128, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
