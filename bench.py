@@ -71,6 +71,21 @@ def algorithmic(wl, counts, Is: int = 0, mx: bool = False):
     if Is:
         st["shared_expert"] = dict(flops=6 * T * H * Is,
                                    bytes=3 * Is * H * b + T * H * b + 2 * T * Is * b + T * H * b)
+    # backward (moe_backward), bf16: per stage its GEMM flops and the bytes its
+    # kernels must move at least (weights of active experts once, activations
+    # once per pass; fp32 weight gradients written once)
+    W13, W2 = 2 * active * I * H * b, active * H * I * b
+    st["router_grads"] = dict(flops=4 * T * H * E + 2 * M * H,
+                              bytes=M * H * b + 2 * T * H * b + E * H * (b + 4) + T * H * b)
+    st["weight_transpose"] = dict(flops=0, bytes=2 * (2 * E * I * H * b + E * H * I * b))
+    st["recompute_gate_up"] = dict(flops=4 * M * H * I, bytes=W13 + M * H * b + 2 * M * I * b)
+    st["dgrad_down_swiglu"] = dict(flops=2 * M * H * I,
+                                   bytes=W2 + M * H * b + M * I * b + 3 * M * I * b + 3 * M * I * b)
+    st["dgrad_gate_up"] = dict(flops=4 * M * H * I, bytes=W13 + 2 * M * I * b + 2 * M * H * b + T * H * b)
+    st["wgrad_transpose"] = dict(flops=0, bytes=2 * (2 * M * H * b + 3 * M * I * b))
+    st["wgrad_down"] = dict(flops=2 * M * H * I, bytes=M * H * b + M * I * b + active * H * I * 4)
+    st["wgrad_gate_up"] = dict(flops=4 * M * H * I,
+                               bytes=2 * M * I * b + M * H * b + 2 * active * I * H * 4)
     return st
 
 
@@ -79,10 +94,11 @@ def padding_waste(counts, bm=BM):
     return 1.0 - sum(counts) / (tiles * bm) if tiles else 0.0
 
 
-def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0):
+def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0, train: bool = False):
     """Time the oracle as it stands on the first ``sample_tokens`` tokens
     (with ``shared`` = (ws13, ws2) float32 arrays: the block with a shared expert;
-    with ``round_tile``: the block with token rounding over those tokens)."""
+    with ``round_tile``: the block with token rounding over those tokens; with
+    ``train``: the backward, which runs the forward itself)."""
     import numpy as np
     from oracle import moe_oracle as O
     try:
@@ -95,8 +111,13 @@ def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0):
     S = min(sample_tokens, wl.T)
     x = inp.f32("x")[:S]
     wr, w13, w2 = inp.f32("w_router"), inp.f32("w13"), inp.f32("w2")
+    if train:
+        dout = np.random.default_rng(12345).standard_normal((S, wl.H))
     t0 = time.perf_counter()
-    if round_tile:
+    if train:
+        res = O.backward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize, dout)
+        res = {"out": res["dx"]}
+    elif round_tile:
         res = O.forward_rounded(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize, round_tile)
     elif shared is None:
         res = O.forward(x, wr, inp.bias, w13, w2, wl.k, wl.renormalize)
@@ -107,6 +128,7 @@ def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0):
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {wl.T} tokens of {wl.name}, float64 numpy oracle "
                       f"(route{'+token rounding' if round_tile else ''}+permute+experts"
+                      f"{'+backward' if train else ''}"
                       f"{'+shared expert' if shared is not None else ''}"
                       f"+combine), {dt:.1f} s"}
 
@@ -129,6 +151,9 @@ def main():
                     help="token rounding to the grouped GEMM's row tile (moe_forward_rounded)")
     ap.add_argument("--round-tile", type=int, default=0, metavar="B",
                     help="token rounding to B rows (moe_forward_rounded)")
+    ap.add_argument("--train", action="store_true",
+                    help="forward + backward per step (moe_forward_profiled + moe_backward_profiled, "
+                         "gradients of sum(dout * out) for a seeded dout)")
     ap.add_argument("--mxfp8", action="store_true",
                     help="MXFP8 expert GEMMs (moe_forward_mxfp8; weights quantized once, "
                          "before the timed steps)")
@@ -176,9 +201,13 @@ def main():
     Is = args.shared_intermediate
     RB = args.round_tile or (B.gemm_tile_rows(dt_code) if args.round else 0)
     MX = args.mxfp8
-    if (RB and Is) or (MX and (RB or Is)):
-        print("bench.py: --round, --shared-intermediate and --mxfp8 do not combine",
+    TR = args.train
+    if (RB and Is) or (MX and (RB or Is)) or (TR and (RB or Is or MX)):
+        print("bench.py: --round, --shared-intermediate, --mxfp8 and --train do not combine",
               file=sys.stderr)
+        sys.exit(2)
+    if TR and wl.dtype != "bf16":
+        print("bench.py: --train needs a bf16 workload", file=sys.stderr)
         sys.exit(2)
     wq_ms = None
     if MX:
@@ -207,6 +236,17 @@ def main():
         nbytes = B.workspace_size(B.ENTRY_FORWARD, wl.T, wl.H, wl.I, wl.E, wl.k, dt_code)
         stages, n_ev = B.PROFILE_STAGES, B.PROFILE_EVENTS
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if TR:
+        r = np.random.default_rng(12345)
+        dout = up(W.f32_to_bf16_bits(r.standard_normal((wl.T, wl.H)).astype(np.float32)))
+        bws = torch.empty(B.backward_layout(wl.T, wl.H, wl.I, wl.E, wl.k).total, dtype=torch.uint8,
+                          device=dev)
+        grads = dict(dx=torch.empty_like(x), dw_router=torch.empty((wl.E, wl.H), device=dev),
+                     dbias=torch.empty(wl.E, device=dev),
+                     dw13=torch.empty((wl.E, 2 * wl.I, wl.H), device=dev),
+                     dw2=torch.empty((wl.E, wl.H, wl.I), device=dev))
+        stages = tuple(stages) + B.PROFILE_STAGES_BACKWARD
+        n_ev = n_ev + B.PROFILE_EVENTS_BACKWARD
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
            for _ in range(max(args.steps, 1))]
     for row in evs:
@@ -225,8 +265,12 @@ def main():
             B.moe_forward_shared(x, wr, bias, w13, w2, ws13, ws2, wl.k, wl.renormalize, out, ws,
                                  events=evs[i % len(evs)])
         else:
+            ev = evs[i % len(evs)]
             B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
-                                   evs[i % len(evs)])
+                                   ev[:B.PROFILE_EVENTS])
+            if TR:
+                B.moe_backward(x, wr, bias, w13, w2, wl.k, wl.renormalize, ws, dout,
+                               workspace=bws, events=ev[B.PROFILE_EVENTS:], **grads)
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -241,9 +285,15 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     stage_ms = {s: 0.0 for s in stages}
+    # event index of each stage's start (with --train the backward's events
+    # follow the forward's, whose last one closes the forward's last stage)
+    starts = list(range(len(stages)))
+    if TR:
+        nf = B.PROFILE_EVENTS - 1
+        starts = list(range(nf)) + [B.PROFILE_EVENTS + j for j in range(len(stages) - nf)]
     for i in range(args.steps):
         for j, s in enumerate(stages):
-            stage_ms[s] += evs[i][j].elapsed_time(evs[i][j + 1]) / args.steps
+            stage_ms[s] += evs[i][starts[j]].elapsed_time(evs[i][starts[j] + 1]) / args.steps
     if MX:
         mid = B.mxfp8_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k)
     else:
@@ -260,8 +310,12 @@ def main():
         if alg[s]["flops"]:
             d["TFLOP/s"] = round(alg[s]["flops"] / t / 1e12, 1)
         detail[s] = d
-    g_t = (stage_ms["gemm_gate_up_swiglu"] + stage_ms["gemm_down"]) * 1e-3
-    g_flops = alg["gemm_gate_up_swiglu"]["flops"] + alg["gemm_down"]["flops"]
+    gemm_stages = ["gemm_gate_up_swiglu", "gemm_down"]
+    if TR:
+        gemm_stages += ["recompute_gate_up", "dgrad_down_swiglu", "dgrad_gate_up", "wgrad_down",
+                        "wgrad_gate_up"]
+    g_t = sum(stage_ms[s] for s in gemm_stages) * 1e-3
+    g_flops = sum(alg[s]["flops"] for s in gemm_stages)
     peak = PEAK_FP8_TFLOPS if MX else PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     grouped_tflops = g_flops / g_t / 1e12
 
@@ -304,7 +358,8 @@ def main():
         "dtype": "mxfp8" if MX else "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name + (f"+shared{Is}" if Is else "") +
-                   (f"+round{RB}" if RB else "") + ("+mxfp8" if MX else ""), "tokens": wl.T,
+                   (f"+round{RB}" if RB else "") + ("+mxfp8" if MX else "") +
+                   ("+train" if TR else ""), "tokens": wl.T,
                    "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
                    "shared_intermediate": Is, "round_tile": RB, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},
@@ -329,7 +384,9 @@ def main():
         if Is:
             cv = (lambda a: W.bf16_bits_to_f32(a)) if wl.dtype == "bf16" else (lambda a: a)
             sh = (cv(hs13), cv(hs2))
-        rec["cpu_baseline"] = cpu_baseline(inp, sample, sh, RB)
+        if TR:
+            sample = min(sample, 1024)
+        rec["cpu_baseline"] = cpu_baseline(inp, sample, sh, RB, train=TR)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.report:
