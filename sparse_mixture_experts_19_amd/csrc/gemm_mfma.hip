@@ -710,24 +710,37 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
     } else if constexpr (WG) {
-      // ---- weight gradient: fp32 sums straight to Cf (row-major, N columns)
+      // ---- weight gradient: fp32 sums to Cf (row-major, N columns).  Each
+      // 32x32 result tile is staged in the wave's 4 KB of LDS (128-byte rows,
+      // 16-byte chunk c of row r in slot c ^ (r & 7)) and stored as whole
+      // 128-byte row segments.
+      float* stg = reinterpret_cast<float*>(STG) + wave * 1024;
+      const int r = lane & 31;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int grp = 0; grp < 4; ++grp) {
-            const int row = wm * 128 + i * 32 + (lane & 31);
-            const int col = ci.t.n0 + wn * 128 + 32 * j + 8 * grp + 4 * (lane >> 5);
+            const int c = 2 * grp + (lane >> 5);          // 16-byte chunk of the row
             float4 v;
             v.x = acc_rd(acc[i][j][4 * grp]);
             v.y = acc_rd(acc[i][j][4 * grp + 1]);
             v.z = acc_rd(acc[i][j][4 * grp + 2]);
             v.w = acc_rd(acc[i][j][4 * grp + 3]);
+            *reinterpret_cast<float4*>(stg + r * 32 + ((c ^ (r & 7)) << 2)) = v;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = q * 8 + (lane >> 3), c = lane & 7;
+            const float4 v = *reinterpret_cast<const float4*>(stg + rr * 32 + ((c ^ (rr & 7)) << 2));
+            const int row = wm * 128 + i * 32 + rr;
+            const int col = ci.t.n0 + wn * 128 + 32 * j + 4 * c;
             if (row < ci.t.rows && col < N)
               *reinterpret_cast<float4*>(a.Cf + static_cast<int64_t>(ci.t.r0 + row) * N + col) = v;
-            __builtin_amdgcn_sched_barrier(0);
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
     } else if constexpr (MX && SWIGLU) {
       // ---- MXFP8 epilogue: h = silu(g) * u quantized along its columns.
       // Per 32x32 result tile a lane holds 16 of the 32 columns of one token
