@@ -338,7 +338,7 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(wl.name + ("+mxfp8" if MX else ""), {}).get(dom)
+        rec = tr.get(wl.name + ("+mxfp8" if MX else "") + ("+train" if TR else ""), {}).get(dom)
         if rec and rec.get("source_sha256") == gemm_source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
