@@ -152,8 +152,10 @@ def main():
     ap.add_argument("--round-tile", type=int, default=0, metavar="B",
                     help="token rounding to B rows (moe_forward_rounded)")
     ap.add_argument("--train", action="store_true",
-                    help="forward + backward per step (moe_forward_profiled + moe_backward_profiled, "
-                         "gradients of sum(dout * out) for a seeded dout)")
+                    help="forward + backward per step (moe_forward_train keeping g and u + "
+                         "moe_backward reading them; gradients of sum(dout * out) for a seeded dout)")
+    ap.add_argument("--train-recompute", action="store_true",
+                    help="as --train, with the backward recomputing g and u (moe_forward + moe_backward)")
     ap.add_argument("--mxfp8", action="store_true",
                     help="MXFP8 expert GEMMs (moe_forward_mxfp8; weights quantized once, "
                          "before the timed steps)")
@@ -201,7 +203,8 @@ def main():
     Is = args.shared_intermediate
     RB = args.round_tile or (B.gemm_tile_rows(dt_code) if args.round else 0)
     MX = args.mxfp8
-    TR = args.train
+    TR = args.train or args.train_recompute
+    CACHE = not args.train_recompute
     if (RB and Is) or (MX and (RB or Is)) or (TR and (RB or Is or MX)):
         print("bench.py: --round, --shared-intermediate, --mxfp8 and --train do not combine",
               file=sys.stderr)
@@ -247,6 +250,7 @@ def main():
                      dw2=torch.empty((wl.E, wl.H, wl.I), device=dev))
         stages = tuple(stages) + B.PROFILE_STAGES_BACKWARD
         n_ev = n_ev + B.PROFILE_EVENTS_BACKWARD
+        gate_up = torch.empty((wl.T * wl.k, 2 * wl.I), dtype=x.dtype, device=dev) if CACHE else None
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
            for _ in range(max(args.steps, 1))]
     for row in evs:
@@ -266,11 +270,15 @@ def main():
                                  events=evs[i % len(evs)])
         else:
             ev = evs[i % len(evs)]
-            B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
-                                   ev[:B.PROFILE_EVENTS])
+            if TR and CACHE:
+                B.moe_forward_train(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, gate_up, ws,
+                                    events=ev[:B.PROFILE_EVENTS])
+            else:
+                B.moe_forward_profiled(x, wr, bias, w13, w2, wl.k, wl.renormalize, out, ws,
+                                       ev[:B.PROFILE_EVENTS])
             if TR:
                 B.moe_backward(x, wr, bias, w13, w2, wl.k, wl.renormalize, ws, dout,
-                               workspace=bws, events=ev[B.PROFILE_EVENTS:], **grads)
+                               workspace=bws, events=ev[B.PROFILE_EVENTS:], gate_up=gate_up, **grads)
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -301,6 +309,10 @@ def main():
     counts = mid["counts"].cpu().numpy().tolist()
 
     alg = algorithmic(wl, counts, Is, MX)
+    if TR and CACHE:
+        # the backward reads the kept g and u instead of forming them again
+        alg["recompute_gate_up"] = dict(flops=0, bytes=0)
+        alg["gemm_gate_up_swiglu"]["bytes"] += 4 * wl.T * wl.k * wl.I
     detail = {}
     for s in stages:
         t = stage_ms[s] * 1e-3
@@ -312,8 +324,9 @@ def main():
         detail[s] = d
     gemm_stages = ["gemm_gate_up_swiglu", "gemm_down"]
     if TR:
-        gemm_stages += ["recompute_gate_up", "dgrad_down_swiglu", "dgrad_gate_up", "wgrad_down",
-                        "wgrad_gate_up"]
+        gemm_stages += ["dgrad_down_swiglu", "dgrad_gate_up", "wgrad_down", "wgrad_gate_up"]
+        if not CACHE:
+            gemm_stages.append("recompute_gate_up")
     g_t = sum(stage_ms[s] for s in gemm_stages) * 1e-3
     g_flops = sum(alg[s]["flops"] for s in gemm_stages)
     peak = PEAK_FP8_TFLOPS if MX else PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -338,7 +351,8 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(wl.name + ("+mxfp8" if MX else "") + ("+train" if TR else ""), {}).get(dom)
+        rec = tr.get(rec_key := wl.name + ("+mxfp8" if MX else "") +
+                      ((("+train" if CACHE else "+train_recompute")) if TR else ""), {}).get(dom)
         if rec and rec.get("source_sha256") == gemm_source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
@@ -359,7 +373,7 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
         "config": {"workload": wl.name + (f"+shared{Is}" if Is else "") +
                    (f"+round{RB}" if RB else "") + ("+mxfp8" if MX else "") +
-                   ("+train" if TR else ""), "tokens": wl.T,
+                   (("+train" if CACHE else "+train_recompute") if TR else ""), "tokens": wl.T,
                    "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
                    "shared_intermediate": Is, "round_tile": RB, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},

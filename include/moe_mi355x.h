@@ -222,6 +222,25 @@ int moe_forward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E,
                                  moe_forward_layout* layout);
 
 /*
+ * moe_forward_train -- moe_forward that also keeps what the caching variant
+ * of moe_backward needs: the gate/up GEMM writes, besides h, its gate and up
+ * sums rounded to bf16.
+ *   gate_up  [T*k, 2I] bf16, device, output, 16-byte aligned: row r (the
+ *            expert-sorted row of the permutation) holds g (I values) then u.
+ *   events   NULL, or MOE_PROFILE_EVENTS caller-created HIP events recorded
+ *            as moe_forward_profiled records them (n_events must match).
+ * dtype must be MOE_DTYPE_BF16.  Other arguments and results as moe_forward;
+ * the workspace (moe_forward_workspace_layout) is the one moe_backward reads.
+ */
+int moe_forward_train(const void* x, const void* w_router,
+                      const float* router_bias, const void* w13,
+                      const void* w2, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
+                      void* out, void* gate_up, void* workspace,
+                      size_t workspace_bytes, void* const* events,
+                      int32_t n_events, void* stream);
+
+/*
  * moe_forward_shared -- moe_forward plus a shared expert.  [Hunyuan page]
  * §二.1 routes tokens through a shared-expert pool besides the gated experts
  * without giving its formula; the reading implemented here is a dense expert
@@ -461,6 +480,10 @@ int moe_forward_mxfp8_layout(int64_t T, int32_t H, int32_t I, int32_t E,
  *               to the moe_forward call whose workspace is given.
  *   forward_workspace  that call's workspace (moe_forward_workspace_layout
  *               size), left unchanged since; read only.
+ *   gate_up     NULL: g and u are recomputed (the memory-saving variant of
+ *               [SonicMoE page] 核心差异 §1); or the [T*k, 2I] bf16 sums the
+ *               matching moe_forward_train call kept (the caching variant:
+ *               one grouped GEMM less, 4*T*k*I bytes more kept), read only.
  *   dout        [T,H] bf16, device.
  *   dx          [T,H] bf16, device, output.
  *   dw_router   [E,H] fp32, device, output.
@@ -476,16 +499,16 @@ int moe_backward(const void* x, const void* w_router, const float* router_bias,
                  const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
                  int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
                  const void* forward_workspace, size_t forward_workspace_bytes,
-                 const void* dout, void* dx, float* dw_router, float* dbias,
-                 float* dw13, float* dw2, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 const void* gate_up, const void* dout, void* dx,
+                 float* dw_router, float* dbias, float* dw13, float* dw2,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_backward_profiled -- moe_backward recording caller-created HIP events
  * around its stages, n_events == MOE_PROFILE_EVENTS_BACKWARD:
  *   0 router gradients (dw, the router's logits again, dl, dl W_r, dW_r, dbias)
  *   1 transposed copies of W13 and W2
- *   2 g and u again (grouped GEMM)
+ *   2 g and u again (grouped GEMM; empty when gate_up is given)
  *   3 dh (grouped GEMM) and the SwiGLU backward (dg, du, h)
  *   4 dx: [dg du] W13 (grouped GEMM) and the sum over a token's slots
  *   5 transposed operands of the weight-gradient GEMMs
@@ -498,11 +521,11 @@ int moe_backward_profiled(const void* x, const void* w_router,
                           const void* w2, int64_t T, int32_t H, int32_t I,
                           int32_t E, int32_t k, int32_t dtype,
                           int32_t renormalize, const void* forward_workspace,
-                          size_t forward_workspace_bytes, const void* dout,
-                          void* dx, float* dw_router, float* dbias,
-                          float* dw13, float* dw2, void* workspace,
-                          size_t workspace_bytes, void* const* events,
-                          int32_t n_events, void* stream);
+                          size_t forward_workspace_bytes, const void* gate_up,
+                          const void* dout, void* dx, float* dw_router,
+                          float* dbias, float* dw13, float* dw2,
+                          void* workspace, size_t workspace_bytes,
+                          void* const* events, int32_t n_events, void* stream);
 
 /* Byte offsets of the moe_backward workspace regions (M = T*k; ld = the
  * padded row count of the weight-gradient operands). */

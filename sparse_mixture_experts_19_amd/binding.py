@@ -66,8 +66,9 @@ _SIGS = {
     "moe_forward_rounded_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(ForwardLayout)],
     "moe_gemm_tile_rows": [_c_i32],
     "moe_mx_quantize": [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp],
-    "moe_backward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
-    "moe_backward_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_backward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_backward_profiled": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
+    "moe_forward_train": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
     "moe_backward_workspace_layout": [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(BackwardLayout)],
     "moe_forward_mxfp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
     "moe_forward_mxfp8_profiled": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, ctypes.POINTER(ctypes.c_void_p), _c_i32, _vp],
@@ -470,13 +471,42 @@ PROFILE_STAGES_BACKWARD = ("router_grads", "weight_transpose", "recompute_gate_u
                            "dgrad_gate_up", "wgrad_transpose", "wgrad_down", "wgrad_gate_up")
 
 
+def moe_forward_train(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, out=None,
+                      gate_up=None, workspace=None, events=None):
+    """moe_forward that also keeps the gate and up sums [T*k, 2I] (bf16) for the
+    caching variant of the backward.  Returns (out, gate_up, workspace); with
+    ``events`` (7 timing events) the stages are recorded as PROFILE_STAGES."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dt = _dtype_code(x.dtype)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    if gate_up is None:
+        gate_up = torch.empty((T * k, I2), dtype=x.dtype, device=dev)
+    ws = _workspace(workspace_size(ENTRY_FORWARD, T, H, I, E, k, dt), dev, workspace)
+    handles, n = None, 0
+    if events is not None:
+        if len(events) != PROFILE_EVENTS:
+            raise ValueError(f"need {PROFILE_EVENTS} events")
+        handles = (ctypes.c_void_p * PROFILE_EVENTS)(*[ev.cuda_event for ev in events])
+        n = PROFILE_EVENTS
+    _check(lib().moe_forward_train(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2),
+                                   T, H, I, E, k, dt, int(bool(renormalize)), _ptr(out),
+                                   _ptr(gate_up), _ptr(ws), ws.numel() * ws.element_size(), handles,
+                                   n, _stream(dev)))
+    return out, gate_up, ws
+
+
 def moe_backward(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, forward_ws, dout,
                  dx=None, dw_router=None, dbias=None, dw13=None, dw2=None, workspace=None,
-                 events=None, want_dbias: bool = True):
-    """Gradients of sum(dout * out) for the moe_forward call that left
-    ``forward_ws``.  Returns (dx, dw_router, dbias, dw13, dw2, workspace); the
-    weight gradients are float32.  With ``events`` (9 timing events) the
-    stages are recorded as PROFILE_STAGES_BACKWARD."""
+                 events=None, want_dbias: bool = True, gate_up=None):
+    """Gradients of sum(dout * out) for the moe_forward (or moe_forward_train)
+    call that left ``forward_ws``; ``gate_up`` (from moe_forward_train) skips
+    the recompute of g and u.  Returns (dx, dw_router, dbias, dw13, dw2,
+    workspace); the weight gradients are float32.  With ``events`` (9 timing
+    events) the stages are recorded as PROFILE_STAGES_BACKWARD."""
     T, H = x.shape
     E, I2, _ = w13.shape
     I = I2 // 2
@@ -495,7 +525,8 @@ def moe_backward(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, f
     ws = _workspace(backward_layout(T, H, I, E, k, dt).total, dev, workspace)
     args = [_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w13), _ptr(w2), T, H, I, E, k, dt,
             int(bool(renormalize)), _ptr(forward_ws), forward_ws.numel() * forward_ws.element_size(),
-            _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dbias), _ptr(dw13), _ptr(dw2), _ptr(ws),
+            _ptr(gate_up), _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dbias), _ptr(dw13), _ptr(dw2),
+            _ptr(ws),
             ws.numel() * ws.element_size()]
     if events is None:
         _check(lib().moe_backward(*args, _stream(dev)))

@@ -255,7 +255,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 104; }
+int moe_version(void) { return 105; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -406,6 +406,7 @@ struct Options {
   const void* ws2 = nullptr;
   int32_t Is = 0;
   int32_t round_tile = 0;
+  void* gate_up = nullptr;   // bf16 [T*k, 2I]: the routed gate/up GEMM also writes its sums here
 };
 
 int forward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
@@ -513,10 +514,11 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
     g.A = w + L.y; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   }
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
-  g.C = w + L.h; g.N = I; g.K = H;
+  g.C = w + L.h; g.N = I; g.K = H; g.C2 = opt.gate_up;
   MOE_HIP(bf16 ? moe::launch_gemm_bf16_swiglu(g, s) : moe::launch_gemm_f32_swiglu(g, s));
   MOE_CHECK(mark());
   // y rows go straight to token order (row t*k+j), so the combine streams them
+  g.C2 = nullptr;
   g.A = w + L.h; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   g.B = w2; g.b_stride = static_cast<int64_t>(H) * I;
   g.C = w + L.y; g.N = H; g.K = I; g.scatter = perm;
@@ -578,6 +580,22 @@ int moe_forward_profiled(const void* x, const void* w_router, const float* route
                 MOE_PROFILE_EVENTS);
   return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
                       workspace, workspace_bytes, events, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_train(const void* x, const void* w_router, const float* router_bias,
+                      const void* w13, const void* w2, int64_t T, int32_t H, int32_t I, int32_t E,
+                      int32_t k, int32_t dtype, int32_t renormalize, void* out, void* gate_up,
+                      void* workspace, size_t workspace_bytes, void* const* events,
+                      int32_t n_events, void* stream) {
+  if (dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_forward_train needs dtype MOE_DTYPE_BF16");
+  if (T > 0) MOE_CHECK(need_ptr(gate_up, "gate_up", 16));
+  if (events && n_events != MOE_PROFILE_EVENTS)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS (%d) handles",
+                MOE_PROFILE_EVENTS);
+  Options o;
+  o.gate_up = gate_up;
+  return forward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize, out,
+                      workspace, workspace_bytes, events, static_cast<hipStream_t>(stream), o);
 }
 
 int moe_forward_shared(const void* x, const void* w_router, const float* router_bias,
@@ -891,8 +909,9 @@ moe_backward_layout backward_layout(int64_t T, int H, int I, int E, int k, BwdSc
 int backward_impl(const void* x, const void* w_router, const float* router_bias, const void* w13,
                   const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                   int32_t dtype, int32_t renormalize, const void* fws, size_t fws_bytes,
-                  const void* dout, void* dx, float* dwr, float* dbias, float* dw13, float* dw2,
-                  void* workspace, size_t workspace_bytes, void* const* events, hipStream_t s) {
+                  const void* gate_up, const void* dout, void* dx, float* dwr, float* dbias,
+                  float* dw13, float* dw2, void* workspace, size_t workspace_bytes,
+                  void* const* events, hipStream_t s) {
   MOE_CHECK(check_backward(T, H, I, E, k, dtype));
   if (T == 0) return ok();
   MOE_CHECK(need_ptr(x, "x", 16));
@@ -901,6 +920,7 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
   MOE_CHECK(need_ptr(w13, "w13", 16));
   MOE_CHECK(need_ptr(w2, "w2", 16));
   MOE_CHECK(need_ptr(dout, "dout", 16));
+  if (gate_up) MOE_CHECK(need_ptr(gate_up, "gate_up", 16));
   MOE_CHECK(need_ptr(dx, "dx", 16));
   MOE_CHECK(need_ptr(dwr, "dw_router", 16));
   if (dbias) MOE_CHECK(need_ptr(dbias, "dbias", 4));
@@ -964,7 +984,7 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_transpose(w13, w + L.w13t, E, 2 * I, H, s));
   MOE_HIP(moe::launch_transpose(w2, w + L.w2t, E, H, I, s));
-  // 2: g and u again
+  // 2: g and u again, unless the training forward kept them
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
   moe::GemmArgs g{};
@@ -973,13 +993,16 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
   g.partials = reinterpret_cast<float*>(w + b.gemm + gemm_prefix_bytes(E));
   g.max_pieces = pieces;
   g.A = x; g.gather = perm; g.gather_div = k; g.a_rows = T;
-  g.B = w13; g.C = w + L.gu; g.N = 2 * I; g.K = H;
-  MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
+  const void* gu = gate_up ? gate_up : w + L.gu;
+  if (!gate_up) {
+    g.B = w13; g.C = w + L.gu; g.N = 2 * I; g.K = H;
+    MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
+  }
   // 3: dh = dout W2_e, then the SwiGLU backward
   MOE_CHECK(mark());
   g.A = dout; g.B = w + L.w2t; g.C = w + L.dh; g.N = I; g.K = H;
   MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
-  MOE_HIP(moe::launch_bwd_swiglu(w + L.dh, w + L.gu, wts, perm, M, I, w + L.dgdu, w + L.h, s));
+  MOE_HIP(moe::launch_bwd_swiglu(w + L.dh, gu, wts, perm, M, I, w + L.dgdu, w + L.h, s));
   // 4: dx = sum over a token's slots of [dg du] W13_e, plus dl W_r
   MOE_CHECK(mark());
   g.A = w + L.dgdu; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
@@ -1024,27 +1047,30 @@ extern "C" {
 int moe_backward(const void* x, const void* w_router, const float* router_bias, const void* w13,
                  const void* w2, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                  int32_t dtype, int32_t renormalize, const void* forward_workspace,
-                 size_t forward_workspace_bytes, const void* dout, void* dx, float* dw_router,
-                 float* dbias, float* dw13, float* dw2, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 size_t forward_workspace_bytes, const void* gate_up, const void* dout, void* dx,
+                 float* dw_router, float* dbias, float* dw13, float* dw2, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   return backward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize,
-                       forward_workspace, forward_workspace_bytes, dout, dx, dw_router, dbias, dw13,
-                       dw2, workspace, workspace_bytes, nullptr, static_cast<hipStream_t>(stream));
+                       forward_workspace, forward_workspace_bytes, gate_up, dout, dx, dw_router,
+                       dbias, dw13, dw2, workspace, workspace_bytes, nullptr,
+                       static_cast<hipStream_t>(stream));
 }
 
 int moe_backward_profiled(const void* x, const void* w_router, const float* router_bias,
                           const void* w13, const void* w2, int64_t T, int32_t H, int32_t I,
                           int32_t E, int32_t k, int32_t dtype, int32_t renormalize,
                           const void* forward_workspace, size_t forward_workspace_bytes,
-                          const void* dout, void* dx, float* dw_router, float* dbias, float* dw13,
-                          float* dw2, void* workspace, size_t workspace_bytes, void* const* events,
-                          int32_t n_events, void* stream) {
+                          const void* gate_up, const void* dout, void* dx, float* dw_router,
+                          float* dbias, float* dw13, float* dw2, void* workspace,
+                          size_t workspace_bytes, void* const* events, int32_t n_events,
+                          void* stream) {
   if (!events || n_events != MOE_PROFILE_EVENTS_BACKWARD)
     return fail(MOE_ERR_INVALID_ARG, "events must hold MOE_PROFILE_EVENTS_BACKWARD (%d) handles",
                 MOE_PROFILE_EVENTS_BACKWARD);
   return backward_impl(x, w_router, router_bias, w13, w2, T, H, I, E, k, dtype, renormalize,
-                       forward_workspace, forward_workspace_bytes, dout, dx, dw_router, dbias, dw13,
-                       dw2, workspace, workspace_bytes, events, static_cast<hipStream_t>(stream));
+                       forward_workspace, forward_workspace_bytes, gate_up, dout, dx, dw_router,
+                       dbias, dw13, dw2, workspace, workspace_bytes, events,
+                       static_cast<hipStream_t>(stream));
 }
 
 int moe_backward_workspace_layout(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,

@@ -177,7 +177,7 @@ __device__ __forceinline__ Split split_work(int total, int G, int nk, int max_pi
   return sp;
 }
 
-template <bool MX, bool SWIGLU, bool GATHER, bool WG = false>
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // two stage buffers as distinct arrays (each holds the A rows then the B
   // rows of one 128-byte K stage)
@@ -848,6 +848,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
               __builtin_amdgcn_sched_barrier(0);   // bounds the registers in flight
             }
           write_back(wm * 128 + i * 32, ci.t.n0 + (SWIGLU ? wn * 64 : wn * 128 + h * 64));
+          if constexpr (SWIGLU && SAVE) {
+            // the gate and the up sums too, rounded to bf16, into C2 [M, 2I]
+            uint16_t* C2 = static_cast<uint16_t*>(a.C2);
+            const int hcol = ci.t.n0 + wn * 64;
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                  const int c4 = jj * 8 + 2 * grp + (lane >> 5);
+                  const f32x16_t& cc = acc[i][jj + 2 * part];
+                  const int b = grp * 4;
+                  *reinterpret_cast<uint2*>(stg + r * 128 + (((c4 >> 1) ^ ((r >> 1) & 7)) << 4) + (c4 & 1) * 8) =
+                      pack4_bf16(acc_rd(cc[b]), acc_rd(cc[b + 1]), acc_rd(cc[b + 2]), acc_rd(cc[b + 3]));
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              const int rl = lane >> 3, c = lane & 7;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int rr = q * 8 + rl;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4));
+                const int m = wm * 128 + i * 32 + rr;
+                if (m < ci.t.rows && hcol < N)
+                  *reinterpret_cast<uint4*>(C2 + static_cast<int64_t>(ci.t.r0 + m) * (2 * N) + part * N + hcol + c * 8) = v;
+              }
+            }
+          }
         }
       }
     }
@@ -898,6 +926,17 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs a) {
       }
     }
     if constexpr (SWIGLU) {
+      if (a.C2) {            // the gate and up sums too (bf16), into C2 [M, 2I]
+        uint16_t* C2 = static_cast<uint16_t*>(a.C2) + (t.r0 + row) * (2LL * a.N) + t.n0 + c8 * 8;
+        uint4 g4, u4;
+        uint2 lo = pack4_bf16(v[0], v[1], v[2], v[3]), hi = pack4_bf16(v[4], v[5], v[6], v[7]);
+        g4.x = lo.x; g4.y = lo.y; g4.z = hi.x; g4.w = hi.y;
+        lo = pack4_bf16(up[0], up[1], up[2], up[3]);
+        hi = pack4_bf16(up[4], up[5], up[6], up[7]);
+        u4.x = lo.x; u4.y = lo.y; u4.z = hi.x; u4.w = hi.y;
+        *reinterpret_cast<uint4*>(C2) = g4;
+        *reinterpret_cast<uint4*>(C2 + a.N) = u4;
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = silu_f(v[u]) * up[u];
     }
@@ -963,9 +1002,9 @@ __global__ __launch_bounds__(256) void gemm_mx_swiglu_fixup_kernel(GemmArgs a) {
   }
 }
 
-template <bool MX, bool SWIGLU, bool GATHER, bool WG = false>
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER, WG>), dim3(a.grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER, WG, SAVE>), dim3(a.grid), dim3(256), 0, s, a);
   if constexpr (WG) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_pieces < 2 || a.K / stage_k<MX>() < 2 * kMinPiece) return e;
@@ -1014,11 +1053,12 @@ bool gemm_gather_fits(int64_t a_rows, int K, int elem_bytes) {
 }
 
 hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a0, hipStream_t s) {
-  if (!a0.gather) return launch<false, true, false>(a0, s);
+  if (!a0.gather)
+    return a0.C2 ? launch<false, true, false, false, true>(a0, s) : launch<false, true, false>(a0, s);
   if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 2)) return hipErrorInvalidValue;
   GemmArgs a = a0;
   set_gather_magic(a);
-  return launch<false, true, true>(a, s);
+  return a.C2 ? launch<false, true, true, false, true>(a, s) : launch<false, true, true>(a, s);
 }
 
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s) {

@@ -113,6 +113,9 @@ struct GemmArgs {
   // [g*group_rows, (g+1)*group_rows) and reduces over the K range
   // [koff[g], koff[g+1]) (multiples of 64) of A and B, whose rows have pitch ld
   // elements; fp32 results go to Cf [E*group_rows, N].
+  // bf16 SwiGLU: also the gate and up sums, rounded to bf16, into C2
+  // [M, 2I] (row r: I gate values, then I up values), or null
+  void* C2;
   const int32_t* koff;    // [E+1] device
   int64_t ld;
   int64_t group_rows;

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 104
+    assert L.moe_version() == 105
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -242,7 +242,7 @@ def test_backward_layout_and_argument_errors():
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("x", FAKE), ("wr", FAKE), ("b", None), ("w13", FAKE), ("w2", FAKE), ("T", 8), ("H", 128),
         ("I", 128), ("E", 4), ("k", 2), ("dt", 1), ("ren", 0), ("fws", FAKE), ("fwsb", fw),
-        ("dout", FAKE), ("dx", FAKE), ("dwr", FAKE), ("db", None), ("dw13", FAKE), ("dw2", FAKE),
+        ("gu", None), ("dout", FAKE), ("dx", FAKE), ("dwr", FAKE), ("db", None), ("dw13", FAKE), ("dw2", FAKE),
         ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
     assert L.moe_backward(*args(dt=0)) == B.MOE_ERR_UNSUPPORTED             # bf16 only
     assert L.moe_backward(*args(k=5)) == B.MOE_ERR_INVALID_ARG              # k > E
@@ -251,6 +251,16 @@ def test_backward_layout_and_argument_errors():
     assert L.moe_backward(*args(dw2=FAKE + 4)) == B.MOE_ERR_INVALID_ARG     # misaligned
     assert L.moe_backward(*args(fwsb=fw - 1)) == B.MOE_ERR_WORKSPACE        # forward workspace too small
     assert L.moe_backward(*args(fws=None)) == B.MOE_ERR_WORKSPACE
+    assert L.moe_backward(*args(gu=FAKE + 2)) == B.MOE_ERR_INVALID_ARG       # misaligned gate_up
+    # the training forward: bf16 only, gate_up required, events count checked
+    targs = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("wr", FAKE), ("b", None), ("w13", FAKE), ("w2", FAKE), ("T", 8), ("H", 128),
+        ("I", 128), ("E", 4), ("k", 2), ("dt", 1), ("ren", 0), ("out", FAKE), ("gu", FAKE),
+        ("ws", FAKE), ("wsb", 1 << 30), ("ev", None), ("nev", 0), ("s", None))]
+    assert L.moe_forward_train(*targs(dt=0)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_train(*targs(gu=None)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_train(*targs(ev=(ctypes.c_void_p * 7)(*([FAKE] * 7)), nev=6)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_train(*targs(wsb=64)) == B.MOE_ERR_WORKSPACE
     assert L.moe_backward(*args(wsb=1024)) == B.MOE_ERR_WORKSPACE
     assert L.moe_backward(*args(T=0, x=None, dout=None, dx=None, fws=None, fwsb=0, ws=None,
                                 wsb=0)) == B.MOE_OK

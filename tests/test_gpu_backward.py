@@ -145,3 +145,36 @@ def test_backward_deterministic_and_events():
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
     log("  stage ms " + " ".join(f"{s}={t:.3f}" for s, t in zip(B.PROFILE_STAGES_BACKWARD, times)))
     assert all(t >= 0 for t in times)
+
+
+@pytest.mark.parametrize("case", ["coarse", "ksplit_h", "skewed"])
+def test_backward_cached_gate_up(case):
+    """The caching variant: moe_forward_train keeps g and u (its output is
+    moe_forward's, bit for bit); they equal the sums the recomputing backward
+    forms again, to one bf16 ulp (the two GEMMs tile the columns differently,
+    so a tile cut along K may group its partial sums differently); and the
+    backward that reads them meets the same bounds against the oracle."""
+    base, ch = CASES[case]
+    wl = W.scaled(W.WORKLOADS[base], **ch)
+    log(f"backward cached {case}: {wl}")
+    inp = W.make_inputs(wl)
+    dbits = _dout(wl.T, wl.H, seed=wl.T + 7)
+    d = upload(inp)
+    out_t, gu, fws = B.moe_forward_train(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                                         wl.renormalize)
+    out_f, _ = B.moe_forward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                             wl.renormalize)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t.view(torch.int16), out_f.view(torch.int16))
+    dout = dev_tensor(dbits, "bf16")
+    cached = B.moe_backward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                            wl.renormalize, fws, dout, gate_up=gu)
+    recomp = B.moe_backward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                            wl.renormalize, fws, dout)
+    torch.cuda.synchronize()
+    g_rec = B.backward_intermediates(recomp[5], wl.T, wl.H, wl.I, wl.E, wl.k)["gu"].float()
+    g_kept = gu.float()
+    ulp = torch.maximum(g_rec.abs(), g_kept.abs()) * 2.0 ** -7
+    assert bool(((g_kept - g_rec).abs() <= ulp).all()), "kept g/u differ from the recomputed ones"
+    log(f"  kept g/u: {int((g_kept != g_rec).sum())} of {g_kept.numel()} differ by one ulp")
+    _compare(inp, dbits, cached, case + " cached")
