@@ -133,6 +133,56 @@ def cpu_baseline(inp, sample_tokens: int, shared=None, round_tile: int = 0, trai
                       f"+combine), {dt:.1f} s"}
 
 
+def standalone_calls(B, x, wr, bias, w13, w2, wl, iters: int = 10):
+    """Median time of each of the four separate entry points (route, permute
+    with the gathered rows, grouped SwiGLU GEMM, combine) over ``iters`` runs
+    after one warm-up, buffers and workspaces allocated beforehand; and their
+    sum.  The fused moe_forward gathers rows while loading instead of writing
+    x_perm, so the sum is expected to exceed its time."""
+    import torch
+    T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
+    dev = x.device
+    dt = B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws_r = torch.empty(max(B.workspace_size(B.ENTRY_ROUTE, T, H, 64, E, k, dt), 256), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(max(B.workspace_size(B.ENTRY_PERMUTE, T, H, 64, E, k, dt), 256), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(B.workspace_size(B.ENTRY_GROUPED_GEMM, T * k, H, I, E, 1, dt), 256), dtype=torch.uint8, device=dev)
+    h = torch.empty((T * k, I), dtype=x.dtype, device=dev)
+    y = torch.empty((T * k, H), dtype=x.dtype, device=dev)
+    out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    state = {}
+
+    def route():
+        B.moe_route(x, wr, bias, k, wl.renormalize, ids, wts, ws_r)
+
+    def permute():
+        state["p"] = B.moe_permute(ids, E, x, ws_p)
+
+    def gemm():
+        B.moe_grouped_swiglu_gemm(state["p"][4], state["p"][1], w13, w2, h, y, ws_g)
+
+    def combine():
+        B.moe_combine(y, state["p"][3], wts, out)
+
+    res = {}
+    for name, fn in (("route", route), ("permute", permute), ("grouped_gemm", gemm),
+                     ("combine", combine)):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        res[name + "_ms"] = round(sorted(times)[len(times) // 2], 5)
+    res["sum_ms"] = round(sum(v for n, v in res.items()), 5)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +433,9 @@ def main():
         "stages": detail,
         "roofline": roof,
     }
+    if not (MX or TR or RB or Is):
+        log("[bench] standalone entry points")
+        rec["standalone_calls"] = standalone_calls(B, x, wr, bias, w13, w2, wl)
     if MX:
         rec["weight_quantization_ms"] = round(wq_ms, 3)
     if MX and not args.no_cpu:
