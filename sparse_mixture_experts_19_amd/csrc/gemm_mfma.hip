@@ -32,9 +32,9 @@
 // L2/HBM into LDS (global_load_lds_dwordx4, no staging registers).  The
 // stages of all of a workgroup's tiles form one sequence: one barrier per
 // stage both publishes stage g+1 and frees stage g's buffer, stage g+2 is
-// fetched while the last K16 step of stage g is multiplied, so a DMA has a
-// whole stage of MFMAs to land in, also across tile boundaries and under
-// the epilogue.  DMAs take a scalar base plus a per-lane 32-bit offset set
+// fetched while the last K16 step of stage g and the first of stage g+1 are
+// multiplied, half in each, so a DMA has at least two K16 steps of MFMAs to
+// land in, also across tile boundaries and under the epilogue.  DMAs take a scalar base plus a per-lane 32-bit offset set
 // once per tile, so issuing one costs no vector ALU work.  Operand fragments
 // are double-buffered across the four K16 steps, and the first fragments of
 // a stage are read during the previous one.  LDS rows are 128 bytes whose
@@ -519,14 +519,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // steps 0..2 are multiplied while the fragments of steps 1..3 are read;
   // then one barrier, reached after this lane's DMAs of stage g+1 landed and
   // its reads of stage g completed, both publishes stage g+1 and frees
-  // buffer g & 1.  Step 3 is multiplied while stage g+2 is fetched into that
-  // buffer and the step-0 fragments of stage g+1 are read, so every DMA has
-  // a whole stage of MFMAs to land in and no stage starts with an LDS wait.
-  // The last stage of a tile fetches nothing during step 3: its buffer stages
-  // the tile's outputs, and stage g+2 is fetched right after the epilogue.
-  // The DMA cursor (dkc and the bases above) runs up to two stages ahead of the MFMAs and
-  // decodes tiles on its own; gathered rows of a new tile are loaded one
-  // barrier before their first use.
+  // buffer g & 1.  Step 3 is multiplied while the step-0 fragments of stage
+  // g+1 are read and the first half of stage g+2 is fetched into that
+  // buffer; the second half is fetched during step 0 of stage g+1.  Spread
+  // over two K16 steps, 8 DMAs per wave in each, the fetch no longer stalls
+  // the MFMA issue the way 16 DMAs in one step did, and every DMA still has
+  // at least two K16 steps of MFMAs to land in (one step, as a three-step
+  // spread leaves, is too short).  No stage starts with an LDS wait.  The
+  // DMA cursor (dkc and the bases above) runs up to two stages ahead of the
+  // MFMAs, across tile boundaries and under the epilogue, and decodes tiles
+  // on its own; gathered rows of a new tile are loaded one barrier before
+  // their first use.  MX stages are two K64 steps, and the whole fetch of
+  // stage g+2 already spans the second one.
   Item ci;                                   // item whose outputs the MFMAs compute
   int cidx = next_item(0, ci);
   if (cidx < 0) return;
@@ -564,17 +568,26 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   };
 
   int ckc = ci.k0;  // K stage being multiplied
+  StageBase gq{};   // bf16: bases of the stage whose fetch is under way
   gconv();
 #pragma unroll
   for (int t = 0; t < 16; ++t) dma1(dkc, sb0, t);
   dma_sc1(dkc, 0);
   dma_advance();
-  if (dlive) {
-    gconv();
+  if constexpr (MX) {
+    if (dlive) {
+      gconv();
 #pragma unroll
-    for (int t = 0; t < 16; ++t) dma1(dkc, sb1, t);
-    dma_sc1(dkc, 1);
-    dma_advance();
+      for (int t = 0; t < 16; ++t) dma1(dkc, sb1, t);
+      dma_sc1(dkc, 1);
+      dma_advance();
+    }
+  } else {
+    // the first half of stage 1; the first stage fetches the rest
+    if (dlive) gconv();
+    gq = stage_base(dlive ? dkc : 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dma_pre(gq, sb1, t);
   }
   wait_vmcnt0();
   lds_barrier();
@@ -600,6 +613,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     const uint4* Sc = par ? S1 : S0;
     const uint4* Sn = par ? S0 : S1;
     const uint32_t sbc = par ? sb1 : sb0;
+    const uint32_t sbn = par ? sb0 : sb1;
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MX) {
       // two K64 steps: step 0 reads the fragments of step 1; after the
@@ -638,11 +652,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       return last;
     } else {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {     // step 0; read step 1
+      for (int t = 0; t < 16; ++t) {     // step 0; read step 1, fetch the rest of g+1
         mfma1(Fa, t);
         if (t < 8) frag1(Sc, 1, Fb, t);
+        if ((t & 1) == 0) dma_pre(gq, sbn, 8 + (t >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (dlive) dma_advance();
 #pragma unroll
       for (int t = 0; t < 16; ++t) {     // step 1; read step 2
         mfma1(Fb, t);
@@ -659,18 +675,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       lds_barrier();                     // ... everywhere, and stage g is no longer read
       const bool last = ckc == ci.k1 - 1;
       if (dlive) gconv();
-      // One branch-free step 3.  With nothing left to fetch the DMAs re-read
+      // Branch-free fetches.  With nothing left to fetch the DMAs re-read
       // stage 0 of the last tile into the buffer just freed (valid memory,
       // never read again); the kernel waits for them before it ends.
-      const StageBase gb = stage_base(dlive ? dkc : 0);
+      gq = stage_base(dlive ? dkc : 0);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch g+2
+      for (int t = 0; t < 16; ++t) {     // step 3; read step 0 of g+1, fetch half of g+2
         mfma1(Fb, t);
         if (t < 8) frag1(Sn, 0, Fa, t);  // stale but harmless when g+1 does not exist
-        dma_pre(gb, sbc, t);
+        if ((t & 1) == 0) dma_pre(gq, sbc, t >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (dlive) dma_advance();
       if (!last) ++ckc;
       return last;
     }
