@@ -213,35 +213,33 @@ __global__ __launch_bounds__(256) void bwd_dbias_kernel(const float* __restrict_
   if (threadIdx.x == 0) db[e] = red[0];
 }
 
-// dst[b][c][r] = src[b][r][c] for R x C bf16 matrices (R, C multiples of 64),
-// through a 64x64 LDS tile.
+// dst[b][c][r] = src[b][r][c] for bf16 [R, C] matrices (R, C multiples of
+// 64).  A wave transposes one 64x64 tile without LDS: lane (r8, c8) =
+// (lane / 8, lane % 8) loads 16 bytes (columns 8 c8 .. +7) of each of the
+// rows 8 r8 .. +7, transposes that 8x8 block in registers (v_perm_b32 picks
+// the 16-bit halves) and stores 16 bytes (rows 8 r8 .. +7) of each of the
+// columns 8 c8 .. +7.  Loads and stores move whole 128-byte lines per 8 lanes.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
                                                         uint16_t* __restrict__ dst, int R, int C) {
-  __shared__ uint16_t tile[64][66];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r8 = lane >> 3, c8 = lane & 7;
+  const int c0 = (blockIdx.x * 4 + wave) * 64, r0 = blockIdx.y * 64;
+  if (c0 >= C) return;
   const int64_t base = static_cast<int64_t>(blockIdx.z) * R * C;
-  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;   // 8 lanes x 16 bytes per 64-value row
+  uint4 in[8];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = ty + 32 * p;
-    const uint4 q = *reinterpret_cast<const uint4*>(src + base + static_cast<int64_t>(r0 + r) * C + c0 + tx * 8);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  for (int u = 0; u < 8; ++u)
+    in[u] = *reinterpret_cast<const uint4*>(src + base + static_cast<int64_t>(r0 + 8 * r8 + u) * C + c0 + 8 * c8);
+  auto dw = [](const uint4& q, int d) -> uint32_t { return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w; };
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      tile[r][tx * 8 + 2 * u] = static_cast<uint16_t>(w[u]);
-      tile[r][tx * 8 + 2 * u + 1] = static_cast<uint16_t>(w[u] >> 16);
-    }
-  }
-  __syncthreads();
+  for (int v = 0; v < 8; ++v) {
+    // column v of the block: dword d holds rows 2d (low half) and 2d + 1
+    const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c = ty + 32 * p;
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = tile[tx * 8 + 2 * u][c] | (static_cast<uint32_t>(tile[tx * 8 + 2 * u + 1][c]) << 16);
-    *reinterpret_cast<uint4*>(dst + base + static_cast<int64_t>(c0 + c) * R + r0 + tx * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(dw(in[2 * d + 1], v >> 1), dw(in[2 * d], v >> 1), sel);
+    *reinterpret_cast<uint4*>(dst + base + static_cast<int64_t>(c0 + 8 * c8 + v) * R + r0 + 8 * r8) =
+        make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -412,7 +410,7 @@ hipError_t launch_bwd_router_grads(const float* dl, const void* x, const void* w
 
 hipError_t launch_transpose(const void* src, void* dst, int batch, int R, int C, hipStream_t s) {
   if (R % 64 || C % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_kernel, dim3(C / 64, R / 64, batch), dim3(256), 0, s,
+  hipLaunchKernelGGL(transpose_kernel, dim3((C / 64 + 3) / 4, R / 64, batch), dim3(256), 0, s,
                      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C);
   return hipGetLastError();
 }
