@@ -402,7 +402,10 @@ int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, int32_t dtype,
  * x quantized along H; per expert, h = silu(x Wg^T) * (x Wu^T) from the
  * block-scaled MFMA (products of the dequantized values, fp32 sums),
  * quantized along I; y = h W2^T (fp32 sums) rounded to bf16; the weighted
- * combine as moe_forward.
+ * combine as moe_forward.  The GEMMs read the scales as stage-major 32-bit
+ * words (the four scales of 128 consecutive K values of one row in one word,
+ * the words of consecutive rows adjacent); the call writes those of x (in the
+ * permuted row order) and of the weights into its workspace first.
  *   w13q [E,2I,H] uint8 codes, w13s [E,2I,H/32] uint8 scales;
  *   w2q [E,H,I] uint8 codes, w2s [E,H,I/32] uint8 scales (moe_mx_quantize
  *   of the expert weights); codes 16-byte aligned.
@@ -423,8 +426,8 @@ int moe_forward_mxfp8(const void* x, const void* w_router,
 /*
  * moe_forward_mxfp8_profiled -- moe_forward_mxfp8 recording caller-created
  * HIP events around its stages (as moe_forward_profiled), n_events ==
- * MOE_PROFILE_EVENTS_MXFP8: 0 router, 1 permutation, 2 quantization of x,
- * 3 tile schedule, 4 gate/up GEMM (with the quantization of h), 5 down GEMM,
+ * MOE_PROFILE_EVENTS_MXFP8: 0 router, 1 permutation, 2 quantization of x
+ * and the stage-major scale words, 3 tile schedule, 4 gate/up GEMM (with the quantization of h), 5 down GEMM,
  * 6 combine.
  */
 #define MOE_PROFILE_EVENTS_MXFP8 8
@@ -448,8 +451,14 @@ typedef struct moe_mxfp8_layout {
     size_t x_codes;        /* [T,H] uint8: x quantized along H */
     size_t x_scales;       /* [T,H/32] uint8 */
     size_t h_codes;        /* [M,I] uint8: h of the expert-sorted rows */
-    size_t h_scales;       /* [M,I/32] uint8 */
+    size_t h_scales;       /* [I/128,M] uint32 words, stage-major: word (s,r)
+                              holds the scales of blocks 4s..4s+3 of row r,
+                              block 4s+b in byte b */
     size_t y;              /* [M,H] bf16: expert outputs, row t*k+j */
+    size_t x_scale_words;  /* [H/128,M] uint32: x_scales of row perm[r]/k as
+                              word (s,r), in the same stage-major form */
+    size_t w13_scale_words;/* [H/128,E*2I] uint32: w13s, stage-major */
+    size_t w2_scale_words; /* [I/128,E*H] uint32: w2s, stage-major */
     size_t scratch;        /* kernel scratch */
     size_t total;          /* bytes of the whole workspace */
 } moe_mxfp8_layout;

@@ -48,7 +48,8 @@ class BackwardLayout(ctypes.Structure):
 class Mxfp8Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_ids", "topk_weights", "expert_counts", "expert_offsets", "perm", "inv_perm",
-        "x_codes", "x_scales", "h_codes", "h_scales", "y", "scratch", "total")]
+        "x_codes", "x_scales", "h_codes", "h_scales", "y", "x_scale_words", "w13_scale_words",
+        "w2_scale_words", "scratch", "total")]
 
 
 _SIGS = {
@@ -454,8 +455,11 @@ def mxfp8_intermediates(ws: torch.Tensor, T: int, H: int, I: int, E: int, k: int
         x_codes=view(L.x_codes, T * H, torch.uint8, 1, (T, H)),
         x_scales=view(L.x_scales, T * H // 32, torch.uint8, 1, (T, H // 32)),
         h_codes=view(L.h_codes, M * I, torch.uint8, 1, (M, I)),
-        h_scales=view(L.h_scales, M * I // 32, torch.uint8, 1, (M, I // 32)),
+        # stage-major words [I/128, M] of 4 scale bytes -> [M, I/32]
+        h_scales=view(L.h_scales, M * I // 32, torch.uint8, 1, (I // 128, M, 4))
+        .permute(1, 0, 2).reshape(M, I // 32),
         y=view(L.y, M * H, torch.bfloat16, 2, (M, H)),
+        x_scale_words=view(L.x_scale_words, M * H // 128, torch.int32, 4, (H // 128, M)),
     )
 
 

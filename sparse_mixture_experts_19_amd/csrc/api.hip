@@ -720,6 +720,9 @@ moe_mxfp8_layout mxfp8_layout(int64_t T, int H, int I, int E, int k) {
   L.h_codes = c.take(M * I);
   L.h_scales = c.take(M * I / 32);
   L.y = c.take(M * H * 2);
+  L.x_scale_words = c.take(M * H / 32);
+  L.w13_scale_words = c.take(static_cast<size_t>(E) * 2 * I * H / 32);
+  L.w2_scale_words = c.take(static_cast<size_t>(E) * H * I / 32);
   const size_t rs = moe::route_scratch_bytes(T, H, E, true);
   const size_t ps = moe::permute_scratch_bytes(static_cast<int64_t>(M), E);
   const size_t gs = gemm_prefix_bytes(E) +
@@ -782,6 +785,14 @@ int forward_mxfp8_impl(const void* x, const void* w_router, const float* router_
   MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_mx_quantize(x, true, T, H, xq, xs, s));
+  // stage-major scale words for the GEMMs: x's in the expert-sorted row order
+  // (the GEMM gathers the codes, not the scales), the weights' as given
+  uint32_t* xsw = reinterpret_cast<uint32_t*>(w + L.x_scale_words);
+  uint32_t* w13sw = reinterpret_cast<uint32_t*>(w + L.w13_scale_words);
+  uint32_t* w2sw = reinterpret_cast<uint32_t*>(w + L.w2_scale_words);
+  MOE_HIP(moe::launch_mx_scale_words(xs, M, H, perm, k, xsw, s));
+  MOE_HIP(moe::launch_mx_scale_words(w13s, static_cast<int64_t>(E) * 2 * I, H, nullptr, 1, w13sw, s));
+  MOE_HIP(moe::launch_mx_scale_words(w2s, static_cast<int64_t>(E) * H, I, nullptr, 1, w2sw, s));
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
   MOE_CHECK(mark());
@@ -791,16 +802,20 @@ int forward_mxfp8_impl(const void* x, const void* w_router, const float* router_
   g.partials = reinterpret_cast<float*>(w + L.scratch + gemm_prefix_bytes(E));
   g.max_pieces = pieces;
   // gate/up: rows of x gathered through the permutation, h quantized on the way out
-  g.A = xq; g.a_scale = xs; g.gather = perm; g.gather_div = k; g.a_rows = T;
-  g.B = w13q; g.b_scale = w13s; g.b_stride = static_cast<int64_t>(2) * I * H;
-  g.C = w + L.h_codes; g.c_scale = reinterpret_cast<uint8_t*>(w + L.h_scales); g.N = I; g.K = H;
+  g.A = xq; g.gather = perm; g.gather_div = k; g.a_rows = T;
+  g.a_scale = reinterpret_cast<const uint8_t*>(xsw); g.a_srows = M;
+  g.B = w13q; g.b_stride = static_cast<int64_t>(2) * I * H;
+  g.b_scale = reinterpret_cast<const uint8_t*>(w13sw); g.b_srows = static_cast<int64_t>(E) * 2 * I;
+  g.C = w + L.h_codes; g.c_scale = reinterpret_cast<uint8_t*>(w + L.h_scales); g.c_srows = M;
+  g.N = I; g.K = H;
   MOE_HIP(moe::launch_gemm_mx_swiglu(g, s));
   MOE_CHECK(mark());
   // down: y rows go straight to token order (row t*k+j), so the combine streams them
-  g.A = w + L.h_codes; g.a_scale = reinterpret_cast<uint8_t*>(w + L.h_scales);
+  g.A = w + L.h_codes; g.a_scale = reinterpret_cast<uint8_t*>(w + L.h_scales); g.a_srows = M;
   g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
-  g.B = w2q; g.b_scale = w2s; g.b_stride = static_cast<int64_t>(H) * I;
-  g.C = w + L.y; g.c_scale = nullptr; g.N = H; g.K = I; g.scatter = perm;
+  g.B = w2q; g.b_stride = static_cast<int64_t>(H) * I;
+  g.b_scale = reinterpret_cast<const uint8_t*>(w2sw); g.b_srows = static_cast<int64_t>(E) * H;
+  g.C = w + L.y; g.c_scale = nullptr; g.c_srows = 0; g.N = H; g.K = I; g.scatter = perm;
   MOE_HIP(moe::launch_gemm_mx_down(g, s));
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_combine(w + L.y, nullptr, wts, T, H, k, true, out, s));

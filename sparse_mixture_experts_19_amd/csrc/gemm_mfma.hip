@@ -54,7 +54,10 @@
 // E8M0 scale per lane, for row lane % 32 and the K values 32 (lane / 32) ..
 // +31 of the step, taken from a byte of a 32-bit register that an immediate
 // selects.  The four scale bytes a stage covers of a row form one 32-bit
-// word; the words of the stage's 256 token rows and 256 weight rows are
+// word, stored stage-major (the words of one stage of consecutive rows are
+// contiguous: a row-major [rows, K/32] array would make each 4-byte DMA touch
+// 64 cache lines, which stalled the fetch of the data behind it); the words
+// of the stage's 256 token rows and 256 weight rows are
 // fetched into LDS by two 4-byte DMAs per wave next to the data, and each
 // lane shifts the words it reads by 8 (lane / 32) bits, so that K64 step s
 // takes byte 2 s.  The SwiGLU epilogue quantizes h along its columns (the K
@@ -274,10 +277,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // enters a tile and converted (permutation entry / k, clamped) at the
   // first issue after the next barrier, when the loads are known to be done.
   //
-  // MX: lane l of wave w also fetches the scale words of tile row 64 w + l:
-  // a token row (clamped, or gathered) and a weight row (swiglu: waves 0-1
-  // gate rows, waves 2-3 up rows), at a lane offset of row * K / 32 bytes
-  // from bases that move by 4 bytes per stage.
+  // MX: lane l of wave w also fetches the scale words of tile row 64 w + l
+  // (clamped): a token row and a weight row (swiglu: waves 0-1 gate rows,
+  // waves 2-3 up rows).  The words are stage-major (word s of row r at index
+  // s * rows + r), so a wave's 64 words are 256 contiguous bytes; the A-side
+  // words follow the GEMM's own rows, also when A itself is gathered (the
+  // forward writes them in permuted row order).  The bases move by rows * 4
+  // bytes per stage.
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);
   const uint64_t rowbytes = WG ? static_cast<uint64_t>(a.ld) * 2 : static_cast<uint64_t>(K) * (MX ? 1 : 2);
@@ -290,31 +296,24 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   const char* dB1;                // swiglu: up rows
   int32_t graw[GATHER ? 8 : 1];   // raw permutation entries of the gathered rows
   bool gpend = false;
-  const uint32_t srb = static_cast<uint32_t>(K / 32);   // MX: scale bytes per row
   const int srow = 64 * wave + lane;                     // MX: tile row of this lane's scale words
   uint32_t sxoff = 0, swoff = 0;  // MX: lane offsets of the token / weight scale DMAs
   const uint8_t* dSx = nullptr;   // MX: scale bases of the DMA tile (stage 0)
   const uint8_t* dSw = nullptr;
-  int32_t sgraw = 0;              // MX, gathered: raw permutation entry of the scale row
   auto set_rows = [&](const Tile& t) {
     if constexpr (MX) {
       const int sr = srow < t.rows ? srow : t.rows - 1;
-      if constexpr (GATHER) {
-        sgraw = a.gather[t.r0 + sr];
-        dSx = a.a_scale;
-      } else {
-        sxoff = static_cast<uint32_t>(sr) * srb;
-        dSx = a.a_scale + static_cast<uint64_t>(t.r0) * srb;
-      }
+      sxoff = static_cast<uint32_t>(sr) * 4u;
+      dSx = a.a_scale + static_cast<uint64_t>(t.r0) * 4;
       if constexpr (SWIGLU) {
         const int nb = a.I - t.n0;
         const int rr = srow & 127;
-        swoff = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * srb;
-        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * (2 * a.I) + t.n0 + (wave >= 2 ? a.I : 0)) * srb;
+        swoff = static_cast<uint32_t>(rr < nb ? rr : nb - 1) * 4u;
+        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * (2 * a.I) + t.n0 + (wave >= 2 ? a.I : 0)) * 4;
       } else {
         const int nb = N - t.n0;
-        swoff = static_cast<uint32_t>(srow < nb ? srow : nb - 1) * srb;
-        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * N + t.n0) * srb;
+        swoff = static_cast<uint32_t>(srow < nb ? srow : nb - 1) * 4u;
+        dSw = a.b_scale + (static_cast<uint64_t>(t.e) * N + t.n0) * 4;
       }
     }
     if constexpr (GATHER) {
@@ -366,7 +365,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       if (gpend) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) voff[j] = grow(graw[j]) * rb32 + lchunk * 16;
-        if constexpr (MX) sxoff = grow(sgraw) * srb;
         gpend = false;
       }
     }
@@ -386,8 +384,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   };
   auto dma_sc1 = [&](int kc, int buf) {           // MX: the scale words of stage kc
     if constexpr (MX) {
-      dma4s(dSx + 4 * kc, sxoff, scb + buf * 2048);
-      dma4s(dSw + 4 * kc, swoff, scb + buf * 2048 + 1024);
+      dma4s(dSx + static_cast<uint64_t>(kc) * a.a_srows * 4, sxoff, scb + buf * 2048);
+      dma4s(dSw + static_cast<uint64_t>(kc) * a.b_srows * 4, swoff, scb + buf * 2048 + 1024);
     }
   };
   // The global bases of stage kc, pinned to scalar registers once, so that
@@ -406,8 +404,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     };
     StageBase g{pin(dA + ko), pin(dB0 + ko), pin(SWIGLU ? dB1 + ko : dB0 + ko), nullptr, nullptr};
     if constexpr (MX) {
-      g.sx = pin(dSx + 4 * kc);
-      g.sw = pin(dSw + 4 * kc);
+      g.sx = pin(dSx + static_cast<uint64_t>(kc) * a.a_srows * 4);
+      g.sw = pin(dSw + static_cast<uint64_t>(kc) * a.b_srows * 4);
     }
     return g;
   };
@@ -807,8 +805,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
         }
         const int m = row0 + r;
         if (lane < 32 && m < ci.t.rows && col0 < N)
-          *reinterpret_cast<uint16_t*>(a.c_scale + static_cast<int64_t>(ci.t.r0 + m) * (N / 32) + col0 / 32) =
-              static_cast<uint16_t>(sc2);
+          *reinterpret_cast<uint16_t*>(a.c_scale + (static_cast<int64_t>(col0 / 128) * a.c_srows + ci.t.r0 + m) * 4 +
+                                       (col0 / 32) % 4) = static_cast<uint16_t>(sc2);
       }
     } else
     // ---- epilogue (the next stages are in flight meanwhile).  The MFMA
@@ -1013,7 +1011,8 @@ __global__ __launch_bounds__(256) void gemm_mx_swiglu_fixup_kernel(GemmArgs a) {
     uint4* dst = reinterpret_cast<uint4*>(C + crow * a.N + col);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    a.c_scale[crow * (a.N / 32) + col / 32] = static_cast<uint8_t>(ex + 127);
+    a.c_scale[(static_cast<int64_t>(col / 128) * a.c_srows + crow) * 4 + (col / 32) % 4] =
+        static_cast<uint8_t>(ex + 127);
   }
 }
 
@@ -1101,7 +1100,8 @@ hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a0, hipStream_t s) {
 }
 
 hipError_t launch_gemm_mx_swiglu(const GemmArgs& a0, hipStream_t s) {
-  if (!a0.a_scale || !a0.b_scale || !a0.c_scale || a0.K % stage_k<true>() || a0.N % (BN / 2))
+  if (!a0.a_scale || !a0.b_scale || !a0.c_scale || a0.K % stage_k<true>() || a0.N % (BN / 2) ||
+      a0.a_srows < a0.M || a0.b_srows < static_cast<int64_t>(a0.E) * 2 * a0.I || a0.c_srows < a0.M)
     return hipErrorInvalidValue;
   if (!a0.gather) return launch<true, true, false>(a0, s);
   if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 1)) return hipErrorInvalidValue;
@@ -1111,7 +1111,9 @@ hipError_t launch_gemm_mx_swiglu(const GemmArgs& a0, hipStream_t s) {
 }
 
 hipError_t launch_gemm_mx_down(const GemmArgs& a, hipStream_t s) {
-  if (!a.a_scale || !a.b_scale || a.K % stage_k<true>()) return hipErrorInvalidValue;
+  if (!a.a_scale || !a.b_scale || a.K % stage_k<true>() || a.a_srows < a.M ||
+      a.b_srows < static_cast<int64_t>(a.E) * a.N)
+    return hipErrorInvalidValue;
   return launch<true, false, false>(a, s);
 }
 

@@ -105,10 +105,14 @@ struct GemmArgs {
   float* partials;        // bf16: fp32 partial sums of K-split tiles, max_pieces x BM x BN
   int max_pieces;         // capacity of partials in tiles (0: tiles are never split)
   const int32_t* scatter; // null: row r of C is row r; else row r is written to row scatter[r]
-  // MXFP8 kernels: E8M0 scales (biased exponents), one byte per 32 values of a row
-  const uint8_t* a_scale; // [*, K/32], rows as A (gathered like A)
-  const uint8_t* b_scale; // [E, rows of an expert, K/32]
-  uint8_t* c_scale;       // SwiGLU: scales of h [M, N/32] (h itself: e4m3 codes in C)
+  // MXFP8 kernels: E8M0 scales (biased exponents), one byte per 32 values of
+  // a row, as stage-major 32-bit words: word s of row r (the scales of K
+  // blocks 4s .. 4s+3) at word index s * rows + r, so that the words of one
+  // 128-wide K stage of consecutive rows are contiguous
+  const uint8_t* a_scale; // rows as the GEMM's own rows (r0 + i; never gathered)
+  const uint8_t* b_scale; // rows e * (rows of an expert) + n
+  uint8_t* c_scale;       // SwiGLU: scales of h, rows as C (h itself: e4m3 codes in C)
+  int64_t a_srows, b_srows, c_srows;   // rows of the three word arrays
   // Weight-gradient form (launch_gemm_bf16_wgrad): group g owns output rows
   // [g*group_rows, (g+1)*group_rows) and reduces over the K range
   // [koff[g], koff[g+1]) (multiples of 64) of A and B, whose rows have pitch ld
@@ -166,6 +170,11 @@ hipError_t launch_token_round(const RoundArgs& a, hipStream_t s);
 // [rows, cols] and E8M0 scales [rows, cols/32].
 hipError_t launch_mx_quantize(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+// Stage-major scale words (see GemmArgs) of R rows from row-major E8M0 scales
+// [*, K/32] (K a multiple of 128): dst[s * R + r] = word s of source row r,
+// or of source row rows[r] / div when rows is given (a gathered copy).
+hipError_t launch_mx_scale_words(const uint8_t* scales, int64_t R, int K, const int32_t* rows, int div,
+                                 uint32_t* dst, hipStream_t s);
 
 // ------------------------------------------------------ backward (backward.hip)
 hipError_t launch_bwd_dw(const void* dout, const void* y, int64_t T, int H, int k, float* dw,

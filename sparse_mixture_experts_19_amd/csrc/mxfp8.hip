@@ -70,7 +70,43 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
   }
 }
 
+// Stage-major scale words: thread r copies the S = K/128 words of its source
+// row to word column r of each stage, reading 16 bytes at a time when the
+// rows allow it (S % 4 == 0, i.e. K a multiple of 512, and a 16-byte aligned
+// source; single words otherwise); the stores of a wave cover 256 contiguous
+// bytes.
+__global__ __launch_bounds__(256) void mx_scale_words_kernel(const uint32_t* __restrict__ src, int64_t R,
+                                                             int S, const int32_t* __restrict__ rows,
+                                                             int div, uint32_t* __restrict__ dst) {
+  const int64_t r = blockIdx.x * 256LL + threadIdx.x;
+  if (r >= R) return;
+  const int64_t sr = rows ? rows[r] / div : r;
+  const uint32_t* p = src + sr * S;
+  if (S % 4 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    for (int st = 0; st < S; st += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(p + st);
+      dst[st * R + r] = q.x;
+      dst[(st + 1) * R + r] = q.y;
+      dst[(st + 2) * R + r] = q.z;
+      dst[(st + 3) * R + r] = q.w;
+    }
+  } else {
+    for (int st = 0; st < S; ++st) dst[st * R + r] = p[st];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mx_scale_words(const uint8_t* scales, int64_t R, int K, const int32_t* rows, int div,
+                                 uint32_t* dst, hipStream_t s) {
+  if (R < 0 || K <= 0 || K % (4 * kMxBlock) || div < 1) return hipErrorInvalidValue;
+  if (R == 0) return hipSuccess;
+  const int64_t blocks = (R + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_scale_words_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(scales), R, K / (4 * kMxBlock), rows, div, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_quantize(const void* src, bool bf16, int64_t rows, int cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s) {

@@ -190,12 +190,16 @@ def test_mxfp8_layout_and_argument_errors():
     M = T * k
     X = B.mxfp8_layout(T, H, I, E, k)
     offs = [X.topk_ids, X.topk_weights, X.expert_counts, X.expert_offsets, X.perm, X.inv_perm,
-            X.x_codes, X.x_scales, X.h_codes, X.h_scales, X.y, X.scratch, X.total]
+            X.x_codes, X.x_scales, X.h_codes, X.h_scales, X.y, X.x_scale_words, X.w13_scale_words,
+            X.w2_scale_words, X.scratch, X.total]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and len(set(offs)) == len(offs)
     assert X.x_scales - X.x_codes >= T * H and X.h_codes - X.x_scales >= T * H // 32
     assert X.h_scales - X.h_codes >= M * I and X.y - X.h_scales >= M * I // 32
-    assert X.scratch - X.y >= M * H * 2
+    assert X.x_scale_words - X.y >= M * H * 2
+    assert X.w13_scale_words - X.x_scale_words >= M * H // 32
+    assert X.w2_scale_words - X.w13_scale_words >= E * 2 * I * H // 32
+    assert X.scratch - X.w2_scale_words >= E * H * I // 32
     L = B.lib()
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("x", FAKE), ("wr", FAKE), ("b", None), ("w13q", FAKE), ("w13s", FAKE), ("w2q", FAKE),

@@ -249,6 +249,11 @@ def test_forward_mxfp8_small_full_compare(case):
     xq, xs, _ = O.mx_quantize(x)
     _check_quantized(mid["x_codes"], mid["x_scales"], xq, xs, "x")
     ref = O.forward_mxfp8(x, wr, inp.bias, oq13, os13, oq2, os2, wl.k, wl.renormalize)
+    # the GEMM's copy of x's scales: words of 4 scale bytes, stage-major, rows in
+    # the permuted order (row r: token perm[r] // k)
+    words = np.ascontiguousarray(np.asarray(xs, np.uint8).reshape(wl.T, wl.H // 128, 4)).view(np.int32)
+    want = words.reshape(wl.T, wl.H // 128)[ref["perm"] // wl.k].T
+    assert np.array_equal(mid["x_scale_words"].numpy(), want), "stage-major x scale words"
     assert not compare_ids(ids0_gpu, ref["ids"], ref["logits"]), "float64 ties in the routing"
     assert np.array_equal(mid["ids"].numpy(), ref["ids"])
     assert np.abs(mid["weights"].numpy() - ref["weights"]).max() <= 1e-5
