@@ -77,7 +77,6 @@ def algorithmic(wl, counts, Is: int = 0, mx: bool = False):
     W13, W2 = 2 * active * I * H * b, active * H * I * b
     st["router_grads"] = dict(flops=4 * T * H * E + 2 * M * H,
                               bytes=M * H * b + 2 * T * H * b + E * H * (b + 4) + T * H * b)
-    st["weight_transpose"] = dict(flops=0, bytes=2 * (2 * E * I * H * b + E * H * I * b))
     st["recompute_gate_up"] = dict(flops=4 * M * H * I, bytes=W13 + M * H * b + 2 * M * I * b)
     st["dgrad_down_swiglu"] = dict(flops=2 * M * H * I,
                                    bytes=W2 + M * H * b + M * I * b + 3 * M * I * b + 3 * M * I * b)

@@ -516,15 +516,15 @@ int moe_backward(const void* x, const void* w_router, const float* router_bias,
  * moe_backward_profiled -- moe_backward recording caller-created HIP events
  * around its stages, n_events == MOE_PROFILE_EVENTS_BACKWARD:
  *   0 router gradients (dw, the router's logits again, dl, dl W_r, dW_r, dbias)
- *   1 transposed copies of W13 and W2
- *   2 g and u again (grouped GEMM; empty when gate_up is given)
- *   3 dh (grouped GEMM) and the SwiGLU backward (dg, du, h)
- *   4 dx: [dg du] W13 (grouped GEMM) and the sum over a token's slots
- *   5 transposed operands of the weight-gradient GEMMs
- *   6 dW2 (grouped GEMM over each expert's rows)
- *   7 dW13 (same)
+ *   1 g and u again (grouped GEMM; empty when gate_up is given)
+ *   2 dh (grouped GEMM reading W2 as stored) and the SwiGLU backward (dg, du, h)
+ *   3 dx: [dg du] W13 (grouped GEMM reading W13 as stored) and the sum over
+ *     a token's slots
+ *   4 transposed operands of the weight-gradient GEMMs
+ *   5 dW2 (grouped GEMM over each expert's rows)
+ *   6 dW13 (same)
  */
-#define MOE_PROFILE_EVENTS_BACKWARD 9
+#define MOE_PROFILE_EVENTS_BACKWARD 8
 int moe_backward_profiled(const void* x, const void* w_router,
                           const float* router_bias, const void* w13,
                           const void* w2, int64_t T, int32_t H, int32_t I,
@@ -547,8 +547,6 @@ typedef struct moe_backward_layout {
     size_t dgdu;         /* [M,2I] bf16: dg then du */
     size_t h;            /* [M,I] bf16: silu(g) u */
     size_t dx_slots;     /* [M,H] bf16: [dg du] W13_e, row t*k+j */
-    size_t w13t;         /* [E,H,2I] bf16 */
-    size_t w2t;          /* [E,I,H] bf16 */
     size_t padded_offsets; /* [E+1] int32: column offsets of the experts in the operands below */
     size_t dyT;          /* [H,ld] bf16 */
     size_t hT;           /* [I,ld] bf16 */

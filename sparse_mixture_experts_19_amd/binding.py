@@ -41,7 +41,7 @@ class SharedLayout(ctypes.Structure):
 
 class BackwardLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "dw", "dlogits", "dx_router", "gu", "dh", "dgdu", "h", "dx_slots", "w13t", "w2t",
+        "dw", "dlogits", "dx_router", "gu", "dh", "dgdu", "h", "dx_slots",
         "padded_offsets", "dyT", "hT", "dgduT", "xT", "ld", "scratch", "total")]
 
 
@@ -470,8 +470,8 @@ def backward_layout(T: int, H: int, I: int, E: int, k: int,
     return L
 
 
-PROFILE_EVENTS_BACKWARD = 9
-PROFILE_STAGES_BACKWARD = ("router_grads", "weight_transpose", "recompute_gate_up", "dgrad_down_swiglu",
+PROFILE_EVENTS_BACKWARD = 8
+PROFILE_STAGES_BACKWARD = ("router_grads", "recompute_gate_up", "dgrad_down_swiglu",
                            "dgrad_gate_up", "wgrad_transpose", "wgrad_down", "wgrad_gate_up")
 
 

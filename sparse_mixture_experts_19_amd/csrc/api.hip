@@ -896,8 +896,6 @@ moe_backward_layout backward_layout(int64_t T, int H, int I, int E, int k, BwdSc
   L.dgdu = c.take(M * 2 * I * 2);
   L.h = c.take(M * I * 2);
   L.dx_slots = c.take(M * H * 2);
-  L.w13t = c.take(static_cast<size_t>(E) * 2 * I * H * 2);
-  L.w2t = c.take(static_cast<size_t>(E) * H * I * 2);
   L.padded_offsets = c.take(static_cast<size_t>(E + 1) * 4);
   L.dyT = c.take(static_cast<size_t>(H) * ld * 2);
   L.hT = c.take(static_cast<size_t>(I) * ld * 2);
@@ -995,11 +993,7 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
   MOE_HIP(moe::launch_bwd_router(ra.logits, ra.meta, ids, dw, T, E, k, renormalize, dl, s));
   MOE_HIP(moe::launch_bwd_router_grads(dl, x, w_router, T, H, E, w + L.dx_router, dwr, dbias,
                                        reinterpret_cast<float*>(w + b.dwr_part), s));
-  // 1: transposed weights
-  MOE_CHECK(mark());
-  MOE_HIP(moe::launch_transpose(w13, w + L.w13t, E, 2 * I, H, s));
-  MOE_HIP(moe::launch_transpose(w2, w + L.w2t, E, H, I, s));
-  // 2: g and u again, unless the training forward kept them
+  // 1: g and u again, unless the training forward kept them
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
   moe::GemmArgs g{};
@@ -1013,19 +1007,21 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
     g.B = w13; g.C = w + L.gu; g.N = 2 * I; g.K = H;
     MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
   }
-  // 3: dh = dout W2_e, then the SwiGLU backward
+  // 2: dh = dout W2_e (W2 read as stored, [E, H, I] = [E, K, N]), then the
+  // SwiGLU backward
   MOE_CHECK(mark());
-  g.A = dout; g.B = w + L.w2t; g.C = w + L.dh; g.N = I; g.K = H;
-  MOE_HIP(moe::launch_gemm_bf16_plain(g, s));
+  g.A = dout; g.B = w2; g.C = w + L.dh; g.N = I; g.K = H;
+  MOE_HIP(moe::launch_gemm_bf16_bt(g, s));
   MOE_HIP(moe::launch_bwd_swiglu(w + L.dh, gu, wts, perm, M, I, w + L.dgdu, w + L.h, s));
-  // 4: dx = sum over a token's slots of [dg du] W13_e, plus dl W_r
+  // 3: dx = sum over a token's slots of [dg du] W13_e (W13 read as stored,
+  // [E, 2I, H] = [E, K, N]), plus dl W_r
   MOE_CHECK(mark());
   g.A = w + L.dgdu; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
-  g.B = w + L.w13t; g.C = w + L.dx_slots; g.N = H; g.K = 2 * I; g.scatter = perm;
-  MOE_HIP(moe::launch_gemm_bf16_down(g, s));
+  g.B = w13; g.C = w + L.dx_slots; g.N = H; g.K = 2 * I; g.scatter = perm;
+  MOE_HIP(moe::launch_gemm_bf16_bt(g, s));
   MOE_HIP(moe::launch_fill(ones, M, 1.f, s));
   MOE_HIP(moe::launch_combine(w + L.dx_slots, nullptr, ones, T, H, k, true, dx, s, w + L.dx_router));
-  // 5: transposed, padded operands of the weight-gradient GEMMs
+  // 4: transposed, padded operands of the weight-gradient GEMMs
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_bwd_tables(counts, E, H, I, poff, goff_h, pre_h, goff_i, pre_i, s));
   MOE_HIP(moe::launch_gather_transpose(dout, H, perm, true, k, wts, offsets, counts, poff, E, ld,
@@ -1036,14 +1032,14 @@ int backward_impl(const void* x, const void* w_router, const float* router_bias,
                                        poff, E, ld, w + L.dgduT, s));
   MOE_HIP(moe::launch_gather_transpose(x, H, perm, true, k, nullptr, offsets, counts, poff, E, ld,
                                        w + L.xT, s));
-  // 6: dW2_e = sum (w dout)^T h over the expert's rows
+  // 5: dW2_e = sum (w dout)^T h over the expert's rows
   MOE_CHECK(mark());
   moe::GemmArgs v{};
   v.E = E; v.koff = poff; v.ld = ld; v.grid = g.grid;
   v.offsets = goff_h; v.prefix = pre_h; v.group_rows = H; v.M = static_cast<int64_t>(E) * H;
   v.A = w + L.dyT; v.B = w + L.hT; v.N = I; v.Cf = dw2; v.a_rows = H;
   MOE_HIP(moe::launch_gemm_bf16_wgrad(v, s));
-  // 7: dW13_e = sum [dg du]^T x over the expert's rows
+  // 6: dW13_e = sum [dg du]^T x over the expert's rows
   MOE_CHECK(mark());
   v.offsets = goff_i; v.prefix = pre_i; v.group_rows = 2 * I; v.M = static_cast<int64_t>(E) * 2 * I;
   v.A = w + L.dgduT; v.B = w + L.xT; v.N = H; v.Cf = dw13; v.a_rows = 2 * I;

@@ -213,36 +213,6 @@ __global__ __launch_bounds__(256) void bwd_dbias_kernel(const float* __restrict_
   if (threadIdx.x == 0) db[e] = red[0];
 }
 
-// dst[b][c][r] = src[b][r][c] for bf16 [R, C] matrices (R, C multiples of
-// 64).  A wave transposes one 64x64 tile without LDS: lane (r8, c8) =
-// (lane / 8, lane % 8) loads 16 bytes (columns 8 c8 .. +7) of each of the
-// rows 8 r8 .. +7, transposes that 8x8 block in registers (v_perm_b32 picks
-// the 16-bit halves) and stores 16 bytes (rows 8 r8 .. +7) of each of the
-// columns 8 c8 .. +7.  Loads and stores move whole 128-byte lines per 8 lanes.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
-                                                        uint16_t* __restrict__ dst, int R, int C) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r8 = lane >> 3, c8 = lane & 7;
-  const int c0 = (blockIdx.x * 4 + wave) * 64, r0 = blockIdx.y * 64;
-  if (c0 >= C) return;
-  const int64_t base = static_cast<int64_t>(blockIdx.z) * R * C;
-  uint4 in[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    in[u] = *reinterpret_cast<const uint4*>(src + base + static_cast<int64_t>(r0 + 8 * r8 + u) * C + c0 + 8 * c8);
-  auto dw = [](const uint4& q, int d) -> uint32_t { return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w; };
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    // column v of the block: dword d holds rows 2d (low half) and 2d + 1
-    const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(dw(in[2 * d + 1], v >> 1), dw(in[2 * d], v >> 1), sel);
-    *reinterpret_cast<uint4*>(dst + base + static_cast<int64_t>(c0 + 8 * c8 + v) * R + r0 + 8 * r8) =
-        make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
 // Padded expert segments of the weight-gradient operands and the tables of
 // the two weight-gradient GEMMs (one block, thread 0 walks the experts).
 __global__ void bwd_tables_kernel(const int32_t* __restrict__ counts, int E, int H, int I,
@@ -405,13 +375,6 @@ hipError_t launch_bwd_router_grads(const float* dl, const void* x, const void* w
   hipLaunchKernelGGL(bwd_dwr_reduce_kernel, dim3(blocks(n, 256)), dim3(256), 0, s, part, S, n, dwr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (db) hipLaunchKernelGGL(bwd_dbias_kernel, dim3(E), dim3(256), 0, s, dl, T, E, db);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const void* src, void* dst, int batch, int R, int C, hipStream_t s) {
-  if (R % 64 || C % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_kernel, dim3((C / 64 + 3) / 4, R / 64, batch), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C);
   return hipGetLastError();
 }
 

@@ -44,6 +44,13 @@
 // output columns of one row: the epilogue applies silu(g)*u in registers,
 // stages bf16 rows in LDS and writes whole 128-byte lines.
 //
+// The data gradients of the backward multiply by W2 and W13 the other way
+// round, K running along the stored weight rows' index: the weight operand
+// is then N-major ([E, K, N] as stored).  In that form (BT) a stage's weight
+// part holds 64 K rows of the tile's 256 columns, fetched by the same DMAs,
+// and its fragments are read with the transposing LDS read, so no transposed
+// copy of a weight is ever written.
+//
 // MXFP8 ([Hunyuan page] §七.1 runs the experts in FP8; the format is OCP
 // MXFP8): the same tiles, stages and DMA plan over e4m3 bytes, so a 128-byte
 // stage row holds 128 K values, multiplied in two K64 steps of the
@@ -180,7 +187,18 @@ __device__ __forceinline__ Split split_work(int total, int G, int nk, int max_pi
   return sp;
 }
 
-template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false>
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// BT: B is N-major (element (k, n) of expert e at B + ((e K + k) N + n) * 2,
+// as the expert weights are stored for the transposed products of the
+// backward).  A stage's B part then holds 64 K rows of 512 bytes (the tile's
+// 256 columns), 16-byte chunk c of K row k in slot c ^ (4 (k & 3)); the B
+// fragments are read with ds_read_b64_tr_b16, which, within each group of 16
+// lanes, hands lane i element i of the four 16-value rows that lanes 4j..4j+3
+// supply: lanes reading 4 K rows x 16 consecutive columns thus receive, per
+// column, 4 consecutive K values, the MFMA operand layout (two reads give the
+// 8 values of a K16 step).
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false, bool BT = false>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // two stage buffers as distinct arrays (each holds the A rows then the B
   // rows of one 128-byte K stage)
@@ -342,6 +360,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       }
       dB0 = Bch + (static_cast<uint64_t>(t.e) * (2 * a.I) + t.n0) * rowbytes;
       dB1 = dB0 + static_cast<uint64_t>(a.I) * rowbytes;
+    } else if constexpr (BT) {
+      // DMA 8 + j of wave w fills K rows 8 j + 2 w and + 1 of the B part (the
+      // lane: row + lane / 32, slot lane % 32, i.e. column chunk
+      // (lane % 32) ^ (4 ((2 w + lane / 32) & 3)), clamped to the last chunk
+      // of the matrix for a tail tile)
+      const int nb = N - t.n0;
+      const int half = lane >> 5;
+      const int cs = (lane & 31) ^ (4 * ((2 * wave + half) & 3));
+      const int cc = cs * 8 < nb ? cs : nb / 8 - 1;
+      const uint32_t rowb = static_cast<uint32_t>(N) * 2u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        voff[8 + j] = static_cast<uint32_t>(8 * j + 2 * wave + half) * rowb + static_cast<uint32_t>(cc) * 16u;
+      dB0 = Bch + (static_cast<uint64_t>(t.e) * K * N + t.n0) * 2;
+      dB1 = dB0;
     } else {
       const int nb = N - t.n0;
 #pragma unroll
@@ -377,8 +410,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // MX: LDS byte address of this wave's token scale words in stage buffer 0
   // (buffer b: + 2048 b; weight scale words: + 1024)
   const uint32_t scb = MX ? __builtin_amdgcn_readfirstlane(lds_addr(SSC) + wave * 256) : 0;
+  // bytes a stage moves the B base: 64 K values of a row, or (BT) 64 rows
+  const uint64_t bstage = BT ? static_cast<uint64_t>(BK) * N * 2 : static_cast<uint64_t>(kStageBytes);
   auto dma1 = [&](int kc, uint32_t sb, int t) {   // t < 8: A rows 32t.., else B rows 32(t-8)..
-    const uint64_t ko = static_cast<uint64_t>(kc) * kStageBytes;
+    const uint64_t ko = static_cast<uint64_t>(kc) * (t < 8 ? static_cast<uint64_t>(kStageBytes) : bstage);
     const char* base = t < 8 ? dA : ((SWIGLU && t >= 12) ? dB1 : dB0);
     dma16s(base + ko, voff[t], sb + (t < 8 ? t * 4 * 64 * 16 : BM * 8 * 16 + (t - 8) * 4 * 64 * 16));
   };
@@ -402,7 +437,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
       const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
       return reinterpret_cast<decltype(p)>(static_cast<uintptr_t>((hi << 32) | lo));
     };
-    StageBase g{pin(dA + ko), pin(dB0 + ko), pin(SWIGLU ? dB1 + ko : dB0 + ko), nullptr, nullptr};
+    const uint64_t kob = static_cast<uint64_t>(kc) * bstage;
+    StageBase g{pin(dA + ko), pin(dB0 + kob), pin(SWIGLU ? dB1 + kob : dB0 + kob), nullptr, nullptr};
     if constexpr (MX) {
       g.sx = pin(dSx + static_cast<uint64_t>(kc) * a.a_srows * 4);
       g.sw = pin(dSw + static_cast<uint64_t>(kc) * a.b_srows * 4);
@@ -470,6 +506,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     xo[st] = static_cast<uint32_t>(((wm * 128 + (lane & 31)) * 8 + slotv) * 16);
     wo[st] = static_cast<uint32_t>((BM * 8 + ((SWIGLU ? wn * 64 : wn * 128) + (lane & 31)) * 8 + slotv) * 16);
   }
+  // BT: byte offset of this lane's first transposing read of w fragment j:
+  // lane 16 g + 4 jr + m reads K row 8 (g / 2) + jr (+ 16 s, + 4 for the
+  // second read) at columns 32 j + 16 (g & 1) + 4 m .. + 3 of the wave's 128
+  uint32_t btr[4];
+  {
+    const int g16 = lane >> 4, jr = (lane >> 2) & 3, mm = lane & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      btr[j] = static_cast<uint32_t>(BM * 128 + (8 * (g16 >> 1) + jr) * 512 + (mm & 1) * 8 +
+                                     (16 * wn + 4 * (j ^ jr) + 2 * (g16 & 1) + (mm >> 1)) * 16);
+  }
   // fragment t (< 4: x[t], else w[t-4]) of K16 step s (0..3) of the stage in
   // Ss; MX: of K64 step s (0..1), the chunks of K16 steps 2 s and 2 s + 1
   auto frag1 = [&](const uint4* Ss, int s, Frag& F, int t) {
@@ -489,6 +536,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     } else {
       if (t < 4) {
         F.x[t] = *reinterpret_cast<const bf16x8_t*>(base + xo[s] + t * 32 * 128);
+      } else if constexpr (BT) {
+        const int j = t - 4;
+        typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + btr[j] + s * 16 * 512));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + btr[j] + s * 16 * 512 + 4 * 512));
+        F.w[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       } else {
         const int j = t - 4;
         const int rowoff = SWIGLU ? ((j < 2) ? j * 32 : 128 + (j - 2) * 32) : j * 32;
@@ -1016,9 +1069,9 @@ __global__ __launch_bounds__(256) void gemm_mx_swiglu_fixup_kernel(GemmArgs a) {
   }
 }
 
-template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false>
+template <bool MX, bool SWIGLU, bool GATHER, bool WG = false, bool SAVE = false, bool BT = false>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER, WG, SAVE>), dim3(a.grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MX, SWIGLU, GATHER, WG, SAVE, BT>), dim3(a.grid), dim3(256), 0, s, a);
   if constexpr (WG) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_pieces < 2 || a.K / stage_k<MX>() < 2 * kMinPiece) return e;
@@ -1085,6 +1138,15 @@ hipError_t launch_gemm_bf16_plain(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   set_gather_magic(a);
   return launch<false, false, true>(a, s);
+}
+
+hipError_t launch_gemm_bf16_bt(const GemmArgs& a0, hipStream_t s) {
+  if (a0.N % 64 || a0.K % BK) return hipErrorInvalidValue;
+  if (!a0.gather) return launch<false, false, false, false, false, true>(a0, s);
+  if (a0.gather_div < 1 || !gemm_gather_fits(a0.a_rows, a0.K, 2)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  set_gather_magic(a);
+  return launch<false, false, true, false, false, true>(a, s);
 }
 
 hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a0, hipStream_t s) {

@@ -135,6 +135,10 @@ hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
 // The down kernel's plain product C = A B^T with A rows gathered (gather != null).
 hipError_t launch_gemm_bf16_plain(const GemmArgs& a, hipStream_t s);
 // Weight gradients: per group g, Cf rows of g = A[rows of g] B^T over K range g.
+// Plain product C = A B^T with B N-major ([E, K, N], the expert weights as
+// stored, read for W^T products without a transposed copy); gathered A rows
+// when gather is set, scattered C rows when scatter is set.  N % 64 == 0.
+hipError_t launch_gemm_bf16_bt(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a, hipStream_t s);
 // MXFP8 operands: K a multiple of 128; SwiGLU: N (= I) a multiple of 128;
 // the down GEMM writes bf16 rows.
@@ -188,8 +192,6 @@ int bwd_dwr_slices(int64_t T);
 hipError_t launch_bwd_router_grads(const float* dl, const void* x, const void* w_router, int64_t T,
                                    int H, int E, void* dxr, float* dwr, float* db, float* part,
                                    hipStream_t s);
-// batch x [R, C] -> batch x [C, R] (bf16; R, C multiples of 64)
-hipError_t launch_transpose(const void* src, void* dst, int batch, int R, int C, hipStream_t s);
 // poff [E+1] padded expert segments; goff/pre [E+1] row offsets and tile
 // prefixes of the two weight-gradient GEMMs (H and 2I rows per expert).
 hipError_t launch_bwd_tables(const int32_t* counts, int E, int H, int I, int32_t* poff,
