@@ -77,6 +77,17 @@ def _compare(inp, dout_bits, res, what):
                          ("dbias", db.cpu().numpy(), ref["dbias"])):
         errs[n] = _tensor_err(got, want)
     errs["dx rows"] = (_row_err(host_f64(dx), ref["dx"]), 0.0)
+    # dh = gather(dout) W2_e before the routing weight, the product that reads
+    # W2 as stored ([E, H, I] taken as [E, K, N]): row by row against the
+    # oracle's permutation (which the GPU's equals bit for bit)
+    fw = ref["fw"]
+    dp = O.gather_rows(W.bf16_bits_to_f32(dout_bits).astype(np.float64), fw["perm"], wl.k)
+    w2 = inp.f32("w2").astype(np.float64)
+    dh_ref = np.zeros((wl.T * wl.k, wl.I))
+    for e in range(wl.E):
+        a, b = int(fw["offsets"][e]), int(fw["offsets"][e + 1])
+        dh_ref[a:b] = dp[a:b] @ w2[e]
+    errs["dh rows"] = (_row_err(host_f64(mid["dh"]), dh_ref), 0.0)
     counts = ref["fw"]["counts"]
     g13, g2 = dw13.cpu().numpy(), dw2.cpu().numpy()
     for n, got, want in (("dw13", g13, ref["dw13"]), ("dw2", g2, ref["dw2"])):
