@@ -605,6 +605,72 @@ def backward(x, w_router, bias, w13, w2, k: int, renormalize: bool, dout) -> Dic
                 dlogits=dl, fw=fw)
 
 
+def backward_sampled(x, w_router, bias, w13, w2, k: int, renormalize: bool, dout,
+                     tokens: Sequence[int], cols: Sequence[int],
+                     to_f32=None) -> Dict[str, np.ndarray]:
+    """Parts of ``backward`` for workloads too large to run it whole: dx,
+    dlogits and dw of the given tokens, and per expert the columns
+    dW2[e][:, i] and the rows dW13[e][i], dW13[e][I + i] for i in ``cols``.
+
+    With the top-k choice fixed a token's input gradient depends only on its
+    own row, routing and dout row (g, u and h recomputed from that row, as
+    [SonicMoE page] 核心差异 §1 recomputes them), and one column or row of a
+    weight gradient only on the expert's rows ([Hunyuan page] §二.2: the
+    tokens that activated it) and one row of each of its matrices.  The
+    algebra is that of ``backward``.  ``to_f32`` widens stored values (bf16
+    bit patterns) expert by expert, as in ``forward_tokens``.
+    """
+    conv = to_f32 if to_f32 is not None else (lambda a: a)
+    tokens = np.asarray([int(t) for t in tokens], dtype=np.int64)
+    cols = np.asarray([int(c) for c in cols], dtype=np.int64)
+    X = _f64(conv(np.asarray(x)))
+    wr = _f64(conv(np.asarray(w_router)))
+    dout = _f64(dout)
+    T, H = X.shape
+    E = np.asarray(w13).shape[0]
+    ids, w, _, p = route(X, wr, bias, k, renormalize)
+    counts, offsets, perm, inv = permute(ids, E)
+    ids64 = ids.astype(np.int64)
+    n = len(tokens)
+    dx = np.zeros((n, H))
+    dw = np.zeros((n, k))
+    dw2_cols = np.zeros((E, H, len(cols)))
+    dw13_rows = np.zeros((E, 2, len(cols), H))
+    for e in range(E):
+        si, sj = np.nonzero(ids64[tokens] == e)     # sampled (token, slot) pairs on e
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if len(si) == 0 and b == a:
+            continue
+        w13_e, w2_e = _f64(conv(w13[e])), _f64(conv(w2[e]))
+        I = w13_e.shape[0] // 2
+        if len(si):
+            ts = tokens[si]
+            xs = X[ts]
+            g, u = xs @ w13_e[:I].T, xs @ w13_e[I:].T
+            y = (silu(g) * u) @ w2_e.T
+            dw[si, sj] = (dout[ts] * y).sum(axis=1)
+            dh = (w[ts, sj][:, None] * dout[ts]) @ w2_e
+            dg, du = dh * u * silu_grad(g), dh * silu(g)
+            np.add.at(dx, si, dg @ w13_e[:I] + du @ w13_e[I:])
+        if b > a:
+            f = perm[a:b].astype(np.int64)            # the expert's rows, flat indices
+            xe = X[f // k]
+            dy = w.reshape(-1)[f][:, None] * dout[f // k]
+            gc, uc = xe @ w13_e[cols].T, xe @ w13_e[I + cols].T
+            dw2_cols[e] = dy.T @ (silu(gc) * uc)
+            dhc = dy @ w2_e[:, cols]
+            dw13_rows[e, 0] = (dhc * uc * silu_grad(gc)).T @ xe
+            dw13_rows[e, 1] = (dhc * silu(gc)).T @ xe
+    ps = p[tokens]
+    dp = np.zeros_like(ps)
+    np.put_along_axis(dp, ids64[tokens], weights_grad(dw, np.take_along_axis(ps, ids64[tokens], axis=1),
+                                                      renormalize), axis=1)
+    dl = softmax_grad(ps, dp)
+    dx = dx + dl @ wr
+    return dict(dx=dx, dlogits=dl, dw=dw, dw2_cols=dw2_cols, dw13_rows=dw13_rows, ids=ids,
+                counts=counts)
+
+
 def forward_tokens(x, ids, weights, w13, w2, tokens: Sequence[int],
                    to_f32=None) -> np.ndarray:
     """Block output for a subset of tokens, one token at a time.

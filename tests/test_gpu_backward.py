@@ -21,7 +21,7 @@ import torch
 from oracle import moe_oracle as O
 from sparse_mixture_experts_19_amd import binding as B
 from sparse_mixture_experts_19_amd import workloads as W
-from moe_test_utils import dev_tensor, host_f64, log, upload
+from moe_test_utils import dev_tensor, host_f64, log, sample_tokens, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +189,47 @@ def test_backward_cached_gate_up(case):
     assert bool(((g_kept - g_rec).abs() <= ulp).all()), "kept g/u differ from the recomputed ones"
     log(f"  kept g/u: {int((g_kept != g_rec).sum())} of {g_kept.numel()} differ by one ulp")
     _compare(inp, dbits, cached, case + " cached")
+
+
+def test_backward_full_size_sampled():
+    """The coarse workload at full size, as the training benchmark runs it
+    (moe_forward_train keeping g and u, then moe_backward reading them):
+    dx, dlogits and dw of sampled tokens, and per expert whole columns of
+    dW2 and whole rows of dW13, against the oracle's one-by-one backward."""
+    wl = W.WORKLOADS["coarse_bf16"]
+    log(f"backward full size: {wl}")
+    inp = W.make_inputs(wl)
+    dbits = _dout(wl.T, wl.H, seed=29)
+    d = upload(inp)
+    _, gu, fws = B.moe_forward_train(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                                     wl.renormalize)
+    dout = dev_tensor(dbits, "bf16")
+    dx, _, _, dw13, dw2, ws = B.moe_backward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"],
+                                             wl.k, wl.renormalize, fws, dout, gate_up=gu)
+    torch.cuda.synchronize()
+    mid = B.backward_intermediates(ws, wl.T, wl.H, wl.I, wl.E, wl.k)
+    ids, _, _, _ = O.route(inp.f32("x"), inp.f32("w_router"), inp.bias, wl.k, wl.renormalize)
+    _, offs, perm, _ = O.permute(ids, wl.E)
+    toks = sample_tokens(wl.T, ids, offs, perm, wl.k)
+    r = np.random.default_rng(31)
+    cols = sorted({0, wl.I - 1} | set(r.choice(wl.I, size=4, replace=False).tolist()))
+    log(f"  oracle on {len(toks)} tokens and columns {cols}")
+    ref = O.backward_sampled(inp.x, inp.w_router, inp.bias, inp.w13, inp.w2, wl.k, wl.renormalize,
+                             W.bf16_bits_to_f32(dbits), toks, cols, to_f32=W.bf16_bits_to_f32)
+    gpu_ids = B.forward_intermediates(fws, wl.T, wl.H, wl.I, wl.E, wl.k, B.MOE_DTYPE_BF16)["ids"]
+    assert np.array_equal(ref["ids"], gpu_ids.cpu().numpy()), "routing differs from the oracle's"
+    ti = torch.tensor(toks, device=dx.device)
+    ci = torch.tensor(cols, device=dx.device)
+    errs = {"dx rows": (_row_err(host_f64(dx[ti]), ref["dx"]), 0.0),
+            "dlogits": _tensor_err(mid["dlogits"][ti].cpu().numpy(), ref["dlogits"]),
+            "dw": _tensor_err(mid["dw"][ti].cpu().numpy(), ref["dw"])}
+    g2 = dw2[:, :, ci].cpu().numpy()
+    g13 = torch.stack([dw13[:, ci, :], dw13[:, ci + wl.I, :]], dim=1).cpu().numpy()
+    per2 = [_tensor_err(g2[e], ref["dw2_cols"][e]) for e in range(wl.E) if ref["counts"][e] > 0]
+    per13 = [_tensor_err(g13[e], ref["dw13_rows"][e]) for e in range(wl.E) if ref["counts"][e] > 0]
+    errs["dw2 columns"] = (max(q[0] for q in per2), max(q[1] for q in per2))
+    errs["dw13 rows"] = (max(q[0] for q in per13), max(q[1] for q in per13))
+    log("  " + " ".join(f"{n} {a:.1e}/{b:.1e}" for n, (a, b) in errs.items()))
+    for n, (a, b) in errs.items():
+        assert a <= TOL_GRAD and b <= TOL_GRAD, (n, a, b)
+

@@ -677,6 +677,28 @@ def pin_backward_special_cases():
         assert np.allclose(g2[n], 2 * g1[n], rtol=1e-12, atol=1e-14), n
 
 
+def pin_backward_sampled_matches_backward():
+    # the one-by-one parts used at full size equal the whole backward (itself
+    # pinned above by finite differences and torch autograd), every token and
+    # a few columns, with and without renormalisation and bias
+    for (T, H, E, k, I, bias, renorm), seed in ((( 9, 6, 4, 2, 5, True, False), 11),
+                                                (( 8, 5, 5, 3, 4, False, True), 12),
+                                                (( 7, 4, 3, 1, 3, True, True), 13)):
+        x, wr, b, w13, w2 = _rand_case(T=T, H=H, E=E, k=k, I=I, seed=seed, bias=bias)
+        dout = np.random.default_rng(seed + 100).standard_normal((T, H))
+        full = O.backward(x, wr, b, w13, w2, k, renorm, dout)
+        cols = [0, I // 2, I - 1]
+        toks = list(range(T))[::-1]
+        sm = O.backward_sampled(x, wr, b, w13, w2, k, renorm, dout, toks, cols)
+        assert np.allclose(sm["dx"], full["dx"][toks], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sm["dlogits"], full["dlogits"][toks], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sm["dw"], full["dw"][toks], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sm["dw2_cols"], full["dw2"][:, :, cols], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sm["dw13_rows"][:, 0], full["dw13"][:, cols, :], rtol=1e-12, atol=1e-14)
+        assert np.allclose(sm["dw13_rows"][:, 1], full["dw13"][:, [I + c for c in cols], :],
+                           rtol=1e-12, atol=1e-14)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_") and callable(v)]
 
 
@@ -862,7 +884,25 @@ def _mut_expert_bwd_swapped(xe, w13_e, w2_e, dy):
     return dxe, np.concatenate([dw13[I:], dw13[:I]]), dw2
 
 
+_orig_backward_sampled = O.backward_sampled
+
+
+def _mut_sampled_no_router(x, w_router, bias, w13, w2, k, renormalize, dout, tokens, cols, to_f32=None):
+    r = _orig_backward_sampled(x, w_router, bias, w13, w2, k, renormalize, dout, tokens, cols, to_f32)
+    r["dx"] = r["dx"] - r["dlogits"] @ np.asarray(w_router, dtype=np.float64)
+    return r
+
+
+def _mut_sampled_up_rows_swapped(x, w_router, bias, w13, w2, k, renormalize, dout, tokens, cols,
+                                 to_f32=None):
+    r = _orig_backward_sampled(x, w_router, bias, w13, w2, k, renormalize, dout, tokens, cols, to_f32)
+    r["dw13_rows"] = r["dw13_rows"][:, ::-1]
+    return r
+
+
 MUTATIONS = {
+    "sampled backward without the router term": ("backward_sampled", _mut_sampled_no_router),
+    "sampled backward gate and up rows swapped": ("backward_sampled", _mut_sampled_up_rows_swapped),
     "topk ties to the highest index": ("topk_ids", _mut_topk_ties_high),
     "topk slots ascending": ("topk_ids", _mut_topk_ascending_slots),
     "router bias dropped": ("router_logits", _mut_no_bias),
