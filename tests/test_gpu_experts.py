@@ -94,3 +94,37 @@ def test_combine_deterministic():
     a = B.moe_combine(y, inv, w)
     b = B.moe_combine(y, inv, w)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_standalone_chain_full_size_coarse():
+    """The four standalone entry points chained at the coarse workload's full
+    size (route, permute with x_perm, grouped GEMM, combine), as the
+    benchmark's standalone_calls times them: sampled output tokens against
+    the oracle, and the fused moe_forward's output equal to the chain's bit
+    for bit."""
+    from moe_test_utils import sample_tokens, upload
+    wl = W.WORKLOADS["coarse_bf16"]
+    log(f"standalone chain full size: {wl}")
+    inp = W.make_inputs(wl)
+    d = upload(inp)
+    ids, wts = B.moe_route(d["x"], d["w_router"], d["bias"], wl.k, wl.renormalize)
+    counts, offsets, perm, inv, x_perm = B.moe_permute(ids, wl.E, x=d["x"])
+    _, y = B.moe_grouped_swiglu_gemm(x_perm, offsets, d["w13"], d["w2"])
+    out = B.moe_combine(y, inv, wts)
+    fused, _ = B.moe_forward(d["x"], d["w_router"], d["bias"], d["w13"], d["w2"], wl.k,
+                             wl.renormalize)
+    torch.cuda.synchronize()
+    oids, ow, _, _ = O.route(inp.f32("x"), inp.f32("w_router"), inp.bias, wl.k, wl.renormalize)
+    assert np.array_equal(ids.cpu().numpy(), oids), "routing differs from the oracle's"
+    _, oo, op, _ = O.permute(oids, wl.E)
+    assert np.array_equal(perm.cpu().numpy(), op) and np.array_equal(offsets.cpu().numpy(), oo)
+    toks = sample_tokens(wl.T, oids, oo, op, wl.k)
+    want = O.forward_tokens(inp.x, oids[toks], ow[toks], inp.w13, inp.w2, toks,
+                            to_f32=W.bf16_bits_to_f32)
+    err = row_rel_err(host_f64(out[torch.tensor(toks, device=out.device)]), want)
+    same = torch.equal(out.view(torch.int16), fused.view(torch.int16))
+    log(f"  sampled out err {err:.3e} on {len(toks)} tokens; fused forward bit-identical: {same}")
+    assert err <= TOL_OUT["bf16"]
+    # same products in the same order: the fused path gathers x and scatters
+    # y while loading and storing, which changes no arithmetic
+    assert same, "the fused forward differs from the standalone chain"
