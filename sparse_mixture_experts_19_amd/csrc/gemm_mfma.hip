@@ -102,6 +102,7 @@ __device__ __forceinline__ float silu_f(float g) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // four floats -> four bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
@@ -802,8 +803,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
             const float4 v = *reinterpret_cast<const float4*>(stg + rr * 32 + ((c ^ (rr & 7)) << 2));
             const int row = wm * 128 + i * 32 + rr;
             const int col = ci.t.n0 + wn * 128 + 32 * j + 4 * c;
+            // streaming stores: the fp32 sums are written once and not read
+            // back here, and kept out of the way of the operand panels in L2
             if (row < ci.t.rows && col < N)
-              *reinterpret_cast<float4*>(a.Cf + static_cast<int64_t>(ci.t.r0 + row) * N + col) = v;
+              __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, v),
+                                          reinterpret_cast<f32x4_t*>(a.Cf + static_cast<int64_t>(ci.t.r0 + row) * N + col));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
