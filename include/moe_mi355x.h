@@ -160,8 +160,11 @@ int moe_combine(const void* y, const int32_t* inv_perm,
                 int32_t dtype, void* out, void* stream);
 
 /*
- * moe_forward -- the whole block: route, permute, grouped SwiGLU, combine.
- * The grouped GEMM reads the rows of x through the permutation directly (no
+ * moe_forward -- the whole block: route, permute, grouped SwiGLU, combine,
+ * in the step order of the optimised forward pseudocode of [Qwen3-MoE page]
+ * §2.2 (route, reorder the tokens by expert, batched expert compute, scatter
+ * the results back and sum them with the routing weights; the block itself
+ * is the forward listing of §1).  The grouped GEMM reads the rows of x through the permutation directly (no
  * x_perm copy), and its down projection writes each output row straight back
  * to token order (row perm[r]), so the combine reads every token's k rows
  * contiguously.  Every intermediate is left in the workspace at the offsets

@@ -308,25 +308,35 @@ def token_round(ids, probs, E: int, B: int, renormalize: bool):
     [SonicMoE page] 核心差异 §3: each expert's assignment count is rounded
     down to a multiple of the tile size and the remaining tokens are given to
     the least-loaded experts, which removes the tile padding of the grouped
-    GEMM.  The page's listing is garbled (``tokens // expert_capacity``); the
-    rule taken here, with every decision on integers:
+    GEMM.  The page's listing of this step is garbled and works on counts
+    only; it does not say which token moves where.  The rule taken here, with
+    every decision on integers:
 
     1. Expert e keeps the first floor(c_e / B) * B rows of its segment of the
        stable expert-sorted permutation (assignments in flat order f = t*k+j);
        the rest of its rows go to a pool.
-    2. The pool is handed out in rounds.  A round with P pooled assignments
-       left opens n = ceil(P / B) tiles of B rows and first decides the owner
-       of every tile by water-filling: tile by tile, the expert with the
-       lowest load (rows kept plus B per tile granted so far in the round;
-       ties to the lowest id) among those that have not come out empty.
-       Then, tile by tile in order, a tile takes up to B of the pooled
-       assignments, in flat order, whose token holds the owner in no other
-       slot, at most one slot per token.  A tile that takes nothing marks its
-       owner as unable to take; whatever a round leaves goes to the next
-       round, with the loads actually reached.
+    2. The pool is handed out in tiles of B rows, each to the least-loaded
+       expert (rows kept plus rows received; ties to the lowest id) that can
+       still take rows.  A tile takes up to B of the pooled assignments, in
+       flat order, whose token holds the owner in no other slot, at most one
+       slot per token.  A tile that takes nothing marks its owner as unable.
+       The owners are planned a round at a time: a round with P pooled
+       assignments left opens ceil(P / B) tiles and gives them out by
+       water-filling (B rows per planned tile), as the page's listing spreads
+       the remainder count over the rounded counts before any token moves;
+       then the tiles are filled in order, and what a round leaves goes to
+       the next one with the loads actually reached.
     3. A moved assignment keeps its slot j; its weight is the token's softmax
        probability of the new expert, renormalised over the token's k weights
        when the workload renormalises (unmoved slots keep the same formula).
+
+    Planning a round ahead gives the same ids as choosing each tile's owner
+    from the loads actually reached so far.  The two differ only after a tile
+    comes out short (fewer than B rows), and such a tile has scanned the whole
+    pool: every pooled slot it skipped belongs to a token that now holds its
+    owner, or that held it in a slot the tile itself took (pooled slots of the
+    owner are always eligible, and taken slots never move again).  So its
+    owner can never take another row, whichever rule offers it more tiles.
 
     ids [T,k] int, probs [T,E] float64 (softmax over all experts).  Returns
     (new ids [T,k] int32, new weights [T,k] float64, moved [T,k] bool).

@@ -134,11 +134,12 @@ hipError_t launch_gemm_bf16_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_down(const GemmArgs& a, hipStream_t s);
 // The down kernel's plain product C = A B^T with A rows gathered (gather != null).
 hipError_t launch_gemm_bf16_plain(const GemmArgs& a, hipStream_t s);
-// Weight gradients: per group g, Cf rows of g = A[rows of g] B^T over K range g.
-// Plain product C = A B^T with B N-major ([E, K, N], the expert weights as
-// stored, read for W^T products without a transposed copy); gathered A rows
-// when gather is set, scattered C rows when scatter is set.  N % 64 == 0.
+// Plain product C = A B_e per expert e with B N-major ([E, K, N]: B_e is
+// [K, N], the expert weights as stored, read for W^T products without a
+// transposed copy); gathered A rows when gather is set, scattered C rows when
+// scatter is set.  N % 64 == 0 and K % 64 == 0.
 hipError_t launch_gemm_bf16_bt(const GemmArgs& a, hipStream_t s);
+// Weight gradients: per group g, Cf rows of g = A[rows of g] B^T over K range g.
 hipError_t launch_gemm_bf16_wgrad(const GemmArgs& a, hipStream_t s);
 // MXFP8 operands: K a multiple of 128; SwiGLU: N (= I) a multiple of 128;
 // the down GEMM writes bf16 rows.

@@ -75,19 +75,38 @@ def compare_ids(gpu_ids: np.ndarray, ora_ids: np.ndarray, ora_logits: np.ndarray
 
 def sample_tokens(T: int, ids: np.ndarray, offsets: np.ndarray, perm: np.ndarray, k: int,
                   n_random: int = 16, seed: int = 1234, cap: int = 320):
-    """Tokens for sampled output checks: both ends, random ones, and the first
-    and last row of every non-empty expert (so every active expert is used,
-    including ragged tails)."""
+    """Tokens for sampled output checks: the first and last row of every
+    non-empty expert (so every active expert is used, including the ragged
+    tail of its last row tile), both ends, and random ones.  When more than
+    ``cap`` tokens are collected, only the random extras are dropped, never
+    an expert's first or last row."""
     r = np.random.default_rng(seed)
-    s = set(range(min(4, T))) | set(range(max(0, T - 4), T))
-    s |= set(r.choice(T, size=min(n_random, T), replace=False).tolist())
+    ends = set()
     E = len(offsets) - 1
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
-            s.add(int(perm[a]) // k)
-            s.add(int(perm[b - 1]) // k)
-    s = sorted(s)
-    if len(s) > cap:
-        s = sorted(r.choice(s, size=cap, replace=False).tolist())
-    return s
+            ends.add(int(perm[a]) // k)
+            ends.add(int(perm[b - 1]) // k)
+    extra = set(range(min(4, T))) | set(range(max(0, T - 4), T))
+    extra |= set(r.choice(T, size=min(n_random, T), replace=False).tolist())
+    extra = sorted(extra - ends)
+    room = max(0, cap - len(ends))
+    if len(extra) > room:
+        extra = r.choice(extra, size=room, replace=False).tolist()
+    return sorted(ends | set(extra))
+
+
+def oracle_outputs_all_tokens(inp: W.Inputs, ids: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """The block output of every token from the oracle's routing ``ids`` /
+    ``weights``, computed expert by expert (the whole output tensor, float64)."""
+    to_f32 = W.bf16_bits_to_f32 if inp.wl.dtype == "bf16" else None
+    from oracle import moe_oracle as O
+    return O.forward_tokens(inp.x, ids, weights, inp.w13, inp.w2, range(inp.wl.T), to_f32=to_f32)
+
+
+def row_errors(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    """Per token row: max_h |got-want| / max_h |want|."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return np.abs(got - want).max(axis=1) / np.maximum(np.abs(want).max(axis=1), 1e-30)

@@ -398,6 +398,83 @@ def pin_token_round_hand_example():
     assert np.allclose(wr[5], [0.5 / 0.7, 0.2 / 0.7])
 
 
+GOLDEN_ROUND = os.path.join(os.path.dirname(__file__), "golden", "token_round_short_tile.json")
+
+
+def pin_token_round_short_tile_golden():
+    """Hand-derived case (tests/golden/token_round_short_tile.json): one round
+    plans three tiles and the second comes out short (2 of 3 rows)."""
+    with open(GOLDEN_ROUND) as f:
+        g = json.load(f)
+    ids = np.array(g["ids"])
+    p = np.array(g["probs"], dtype=np.float64)
+    new, w, moved = O.token_round(ids, p, g["E"], g["B"], False)
+    assert np.array_equal(new, np.array(g["expected_ids"]))
+    assert np.array_equal(moved, np.array(g["expected_moved"]))
+    assert np.array_equal(np.bincount(new.ravel(), minlength=g["E"]), g["expected_counts"])
+    assert np.allclose(w, g["expected_weights"], rtol=0, atol=1e-15)
+    _, wr, _ = O.token_round(ids, p, g["E"], g["B"], True)
+    assert np.allclose(wr, g["expected_weights_renormalised"], rtol=1e-15, atol=0)
+
+
+def _greedy_token_round(ids, E, B):
+    """The plainest reading of the hand-out, written independently of the
+    oracle: every tile goes to the expert with the lowest load reached so far
+    (ties to the lowest id) among those whose last tile was not empty; it
+    takes up to B pooled assignments in flat order, at most one per token,
+    none whose token holds the owner in another slot."""
+    T, k = ids.shape
+    counts = np.bincount(ids.ravel(), minlength=E)
+    keep = counts // B * B
+    rank = _rank_in_expert(ids)
+    pool = [(t, j) for t in range(T) for j in range(k) if rank[t, j] >= keep[ids[t, j]]]
+    load = [int(c) for c in keep]
+    able = [True] * E
+    cur = ids.copy()
+    done = [False] * len(pool)
+    while not all(done):
+        cand = [e for e in range(E) if able[e]]
+        e = min(cand, key=lambda q: (load[q], q))
+        got, toks = 0, set()
+        for i, (t, j) in enumerate(pool):
+            if got == B:
+                break
+            if done[i] or t in toks or any(cur[t, jj] == e for jj in range(k) if jj != j):
+                continue
+            cur[t, j] = e
+            done[i] = True
+            toks.add(t)
+            got += 1
+        load[e] += got
+        if got == 0:
+            able[e] = False
+    return cur
+
+
+def pin_token_round_equals_greedy():
+    """Random cases, about a quarter of them with a tile that comes out short
+    before the last tile of its round (small E, k close to E, B near the pool
+    size): the oracle's
+    ids equal those of choosing each tile's owner from the loads reached so
+    far (``_greedy_token_round``)."""
+    r = np.random.default_rng(77)
+    n_cases = 0
+    for _ in range(600):
+        E = int(r.integers(3, 7))
+        k = int(r.integers(2, E))
+        B = int(r.integers(2, 6))
+        T = int(r.integers(3, 14))
+        ids = np.array([r.choice(E, k, replace=False) for _ in range(T)])
+        p = np.full((T, E), 1.0 / E)
+        try:
+            new, _, _ = O.token_round(ids, p, E, B, False)
+        except RuntimeError:
+            continue
+        assert np.array_equal(new, _greedy_token_round(ids, E, B)), (E, k, B, ids.tolist())
+        n_cases += 1
+    assert n_cases > 400
+
+
 def pin_token_round_k1_closed_form():
     """k = 1 has no eligibility limit: the pool (flat order) is cut into
     consecutive blocks of B, and block i goes to the i-th choice of the
