@@ -22,6 +22,10 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "route.hip", "permute.hip", "round.hip", "gemm_mfma.hip", "gemm_f32.hip", "mxfp8.hip", "backward.hip",
            "combine.hip"]
 
+# Per-source flags.  route.hip: its MFMA results are added on the vector ALU
+# right away, so they are kept in VGPRs (no copies out of AGPRs per MFMA).
+SOURCE_FLAGS = {"route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
@@ -42,7 +46,7 @@ def _run(cmd):
 
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    _run([HIPCC, *CFLAGS, *extra, "-c", os.path.join(SRC, src), "-o", obj])
+    _run([HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(SRC, src), "-o", obj])
     return obj
 
 

@@ -181,15 +181,11 @@ moe_forward_layout rounded_layout(int64_t T, int H, int I, int E, int k, int dty
 }
 
 // Router scratch carved from `base`; returns the bytes used.
-size_t carve_route(char* base, int64_t T, int H, int E, bool bf16, moe::RouteArgs& a) {
+size_t carve_route(char* base, int64_t T, int E, moe::RouteArgs& a) {
   Carver c;
-  const size_t ks = static_cast<size_t>(moe::route_ksplit(T, H, E, bf16));
-  a.ksplit = static_cast<int>(ks);
   a.flag = reinterpret_cast<int32_t*>(base + c.take(static_cast<size_t>(T) * 4));
   a.meta = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * 16));
-  a.logits = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(T) * E * 4));
-  a.xnorm2 = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(T) * 4));
-  a.wnorm2 = reinterpret_cast<float*>(base + c.take(ks * static_cast<size_t>(E) * 4));
+  a.logits = reinterpret_cast<float*>(base + c.take(static_cast<size_t>(T) * E * 4));
   return c.o;
 }
 
@@ -200,7 +196,7 @@ int run_route(const void* x, const void* w_router, const float* bias, int64_t T,
   a.x = x; a.w = w_router; a.bias = bias; a.T = T; a.H = H; a.E = E; a.k = k; a.renorm = renorm;
   a.ids = ids; a.weights = weights; a.keep_all = out_args != nullptr;
   const bool bf16 = dtype == MOE_DTYPE_BF16;
-  if (carve_route(scratch, T, H, E, bf16, a) > moe::route_scratch_bytes(T, H, E, bf16))
+  if (carve_route(scratch, T, E, a) > moe::route_scratch_bytes(T, H, E, bf16))
     return fail(MOE_ERR_WORKSPACE, "internal: router scratch layout exceeds its size");
   MOE_HIP(moe::launch_route(a, bf16, s));
   if (out_args) *out_args = a;

@@ -47,17 +47,12 @@ struct RouteArgs {
   int H, E, k, renorm;
   int32_t* ids;           // [T,k]
   float* weights;         // [T,k]
-  int32_t* flag;          // [T]     1 = needs the float64 re-rank
-  float* meta;            // [T,4]   max, sum, delta, unused
-  float* logits;          // [ksplit,T,E] fp32 logits (bf16 path: partial sums over K ranges
-                          //              of every token; slot 0 then holds flagged tokens' totals)
-  float* xnorm2;          // [ksplit,T]   ||x_t||^2 (bf16 path, partial over K ranges)
-  float* wnorm2;          // [ksplit,E]   ||W_e||^2 (bf16 path, partial over K ranges)
-  int ksplit;             // K ranges of the bf16 logits kernel (1 for fp32)
+  int32_t* flag;          // [T]     fp32 path: 1 = needs the float64 re-rank
+  float* meta;            // [T,4]   softmax max and sum, band, k-th logit
+  float* logits;          // [T,E]   fp32 logits with bias (fp32 path: of flagged tokens;
+                          //         every token's when keep_all)
   int keep_all;           // 1: meta and total logits are written for every token
 };
-// K ranges the bf16 router splits H into so that its grid fills the chip.
-int route_ksplit(int64_t T, int H, int E, bool bf16);
 size_t route_scratch_bytes(int64_t T, int H, int E, bool bf16);
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
 

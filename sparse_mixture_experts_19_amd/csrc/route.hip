@@ -13,14 +13,16 @@
 //   delta_t = D * 2^-23 * (1 + D*2^-23) * S_t,
 //   S_t = ||x_t||_2 * max_e ||W_e||_2 + max_e |b_e|   (bounds sum_h |x_th W_eh| + |b_e|),
 // where D is the longest chain of roundings any product passes through in the
-// summation structure below (each MFMA is treated as a chain of 16 rounded
-// additions, each rounding worth at most 2^-23 relative, i.e. even a
-// truncating adder is covered).  A token is flagged when its fp32 top-k is not
-// provably the exact one: some expert outside the top-k is within 2*delta of
-// the k-th logit, or two adjacent top-k logits are within 2*delta.  Flagged
-// tokens are re-ranked by route_refine with float64 dot products (exact
-// products, float64 sums) over the candidate set {e : L_k - L_e <= 2*delta},
-// which provably contains the exact top-k.
+// summation structure of the kernel (an MFMA that starts from zero is
+// counted as a chain of as many rounded additions as it has products, each
+// rounding worth at most 2^-23 relative, so even a truncating adder is
+// covered).  A token is flagged when its fp32 top-k is not provably the exact
+// one: some expert outside the top-k is within 2*delta of the k-th logit, or
+// two adjacent top-k logits are within 2*delta.  Flagged tokens are re-ranked
+// with float64 dot products (exact products, float64 sums) over the
+// candidate set {e : L_k - L_e <= 2*delta}, which provably contains the exact
+// top-k: in the same workgroup on the bf16 path, by route_refine_kernel on
+// the fp32 path.
 #include "moe_internal.h"
 #include "cdna4.h"
 
@@ -149,231 +151,6 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
   }
 }
 
-// ---------------------------------------------------------------- bf16 path
-// Logits: a workgroup owns 128 tokens x 64 (E > 64: 128) experts; wave w
-// multiplies tokens 32w..32w+31 by every 32-expert part (MFMA 32x32x16,
-// router rows as A, tokens as B).  K moves in 64-wide stages through four LDS buffers, loaded
-// by direct-to-LDS DMA three stages ahead.  Each stage's four MFMAs start
-// from zero and are then added to the running sum (the summation structure
-// the error bound counts).  Squared norms of the token rows and router rows
-// are summed from the very operand fragments the MFMAs consume.
-constexpr int LT = 128;               // tokens per workgroup
-constexpr int LBK = 64;               // K per stage
-// experts per workgroup: 64 (two 32-expert MFMA halves per wave) or, for
-// E > 64, 128 (four), which halves the re-reads of x across expert blocks
-__host__ __device__ constexpr int route_ne(int E) { return E > 64 ? 4 : 2; }
-
-// s_waitcnt immediate for vmcnt(n), n < 64 (expcnt / lgkmcnt at their maxima)
-constexpr int vmcnt_code(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// sum of squares of 8 bf16 by packed dot products (v_dot2c_f32_bf16); every
-// term is non-negative, and a square the instruction might flush (below
-// 2^-126) is covered by the slack the norm gets before use
-__device__ __forceinline__ float sumsq8_dot(const bf16x8_t& v, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_t p = {v[2 * i], v[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
-  }
-  return acc;
-}
-
-__device__ __forceinline__ float sumsq8(const bf16x8_t& v) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float f = static_cast<float>(v[i]);
-    s = fmaf(f, f, s);
-  }
-  return s;
-}
-
-template <int NE>
-__global__ __launch_bounds__(256) void route_logits_bf16_kernel(RouteArgs a) {
-  constexpr int LE = 32 * NE;
-  constexpr int LSTAGE = (LT + LE) * 8;   // uint4 per stage buffer
-  constexpr int ND = 4 + NE;              // DMAs per lane per stage
-  __shared__ uint4 R[4][LSTAGE];       // ring of 4 stage buffers
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
-  const int e0 = blockIdx.y * LE;
-  const int H = a.H, E = a.E;
-  // K range z of ksplit: stages [kb, kb + nk) of the H / 64
-  const int z = blockIdx.z, nch = H / LBK;
-  const int kb = z * nch / a.ksplit;
-  const int nk = (z + 1) * nch / a.ksplit - kb;
-  const uint16_t* X = static_cast<const uint16_t*>(a.x) + kb * LBK;
-  const uint16_t* W = static_cast<const uint16_t*>(a.w) + kb * LBK;
-
-  // DMA rows of this lane (clamped in bounds; clamped rows are never
-  // stored): scalar tile bases plus 32-bit lane offsets, no per-DMA ALU work
-  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-  const int lrow = 8 * wave + (lane >> 3);
-  const char* xbase = reinterpret_cast<const char*>(X + t0 * H);
-  const char* wbase = reinterpret_cast<const char*>(W + static_cast<int64_t>(e0) * H);
-  uint32_t xo[4], wo[NE];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int64_t t = t0 + lrow + 32 * j;
-    t = t < a.T ? t : a.T - 1;
-    xo[j] = static_cast<uint32_t>((t - t0) * H * 2 + lchunk * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    int e = e0 + lrow + 32 * j;
-    e = e < E ? e : E - 1;
-    wo[j] = static_cast<uint32_t>((e - e0) * H * 2 + lchunk * 16);
-  }
-  const uint32_t wofs = static_cast<uint32_t>(wave) * 64 * 16;
-  const uint32_t rb = __builtin_amdgcn_readfirstlane(lds_addr(&R[0][0]) + wofs);
-  auto issue = [&](int kc) {
-    const int ko = kc * LBK * 2;
-    const uint32_t dst = rb + (kc & 3) * LSTAGE * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16s(xbase + ko, xo[j], dst + j * 4 * 64 * 16);
-#pragma unroll
-    for (int j = 0; j < NE; ++j) dma16s(wbase + ko, wo[j], dst + LT * 8 * 16 + j * 4 * 64 * 16);
-  };
-
-  f32x16_t acc[NE];
-#pragma unroll
-  for (int n = 0; n < NE; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
-  float xsq = 0.f, wsq[NE];
-#pragma unroll
-  for (int n = 0; n < NE; ++n) wsq[n] = 0.f;
-
-  // router-row norms: only wave 0 of the first token block stores them (a
-  // wave-uniform choice, taken once per stage outside the MFMA sequence)
-  const bool wnorms = blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(wave) == 0;
-  auto multiply = [&](const uint4* Rs, f32x16_t* part, auto with_w) {
-    // all fragments of the stage first, so their LDS latencies overlap
-    bf16x8_t bx[4], aw[4][NE];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      bx[s] = *reinterpret_cast<const bf16x8_t*>(&Rs[swz128(wave * 32 + (lane & 31), c)]);
-#pragma unroll
-      for (int n = 0; n < NE; ++n)
-        aw[s][n] = *reinterpret_cast<const bf16x8_t*>(&Rs[LT * 8 + swz128(n * 32 + (lane & 31), c)]);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      xsq = sumsq8_dot(bx[s], xsq);
-#pragma unroll
-      for (int n = 0; n < NE; ++n) {
-        if constexpr (decltype(with_w)::value) wsq[n] += sumsq8(aw[s][n]);
-        part[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[s][n], bx[s], part[n], 0, 0, 0);
-      }
-    }
-  };
-  issue(0);
-  if (1 < nk) issue(1);
-  if (2 < nk) issue(2);
-  for (int kc = 0; kc < nk; ++kc) {
-    const int after = nk - 1 - kc;          // stages issued after kc (at most 2)
-    // loads of a wave complete in order: keep the newer stages' ND DMAs each
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_code(2 * ND));
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_code(ND));
-    else wait_vmcnt0();
-    lds_barrier();
-    if (kc + 3 < nk) issue(kc + 3);
-    const uint4* Rs = R[kc & 3];
-    f32x16_t part[NE];
-#pragma unroll
-    for (int n = 0; n < NE; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part[n][r] = 0.f;
-    if (wnorms) multiply(Rs, part, std::true_type{});
-    else multiply(Rs, part, std::false_type{});
-#pragma unroll
-    for (int n = 0; n < NE; ++n) acc[n] += part[n];
-  }
-
-  // norms: lanes l and l+32 hold the two K halves of the same row
-  xsq += __shfl_xor(xsq, 32);
-#pragma unroll
-  for (int n = 0; n < NE; ++n) wsq[n] += __shfl_xor(wsq[n], 32);
-  const int64_t t = t0 + wave * 32 + (lane & 31);
-  if (blockIdx.y == 0 && lane < 32 && t < a.T) a.xnorm2[z * a.T + t] = xsq;
-  if (wnorms && lane < 32) {
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      const int e = e0 + n * 32 + lane;
-      if (e < E) a.wnorm2[z * E + e] = wsq[n];
-    }
-  }
-  // logits: lane holds token t and experts 8(r/4) + 4(lane/32) + (r%4) of each half
-  if (t < a.T) {
-    float* row = a.logits + (z * a.T + t) * E;
-#pragma unroll
-    for (int n = 0; n < NE; ++n)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int e = e0 + n * 32 + 8 * g + 4 * (lane >> 5);
-        if ((E & 3) == 0) {
-          if (e < E)
-            *reinterpret_cast<float4*>(row + e) =
-                make_float4(acc[n][4 * g], acc[n][4 * g + 1], acc[n][4 * g + 2], acc[n][4 * g + 3]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (e + q < E) row[e + q] = acc[n][4 * g + q];
-        }
-      }
-  }
-}
-
-// Softmax + top-k + near-tie flag from the fp32 logits, with delta from the
-// squared norms (see the file comment).  max(8, EP / 8) lanes per token, so
-// every lane holds at most 8 logits.
-template <int EP>
-__global__ __launch_bounds__(256) void route_select_bf16_kernel(RouteArgs a) {
-  constexpr int LPT = EP / 8 > 8 ? EP / 8 : 8;
-  constexpr int NT = 256 / LPT;           // tokens per workgroup
-  __shared__ float lg[NT][EP + 1];
-  __shared__ float delta_s[NT];
-  __shared__ unsigned wmax_bits, bmax_bits;
-  const int tid = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * NT;
-  const int E = a.E;
-  const int ks = a.ksplit;
-  if (tid == 0) { wmax_bits = 0u; bmax_bits = 0u; }
-  __syncthreads();
-  if (tid < E) {
-    float w2 = 0.f;
-    for (int z = 0; z < ks; ++z) w2 += a.wnorm2[z * E + tid];
-    atomicMax(&wmax_bits, __float_as_uint(w2));
-    if (a.bias) atomicMax(&bmax_bits, __float_as_uint(fabsf(a.bias[tid])));
-  }
-  // logits = the K ranges' partial sums added in range order
-  for (int i = tid; i < NT * E; i += 256) {
-    const int tk = i / E, e = i - tk * E;
-    const int64_t t = t0 + tk;
-    float v = 0.f;
-    if (t < a.T)
-      for (int z = 0; z < ks; ++z) v += a.logits[(z * a.T + t) * E + e];
-    lg[tk][e] = v;
-  }
-  __syncthreads();
-  if (tid < NT) {
-    const int64_t t = t0 + tid;
-    float x2 = 0.f;
-    if (t < a.T)
-      for (int z = 0; z < ks; ++z) x2 += a.xnorm2[z * a.T + t];
-    x2 += static_cast<float>(a.H) * 1.1754943508222875e-38f;   // H * 2^-126: flushed squares
-    const int nch = a.H / LBK;
-    // 4 chained MFMAs per stage, stage sums within a range, range sums, bias
-    const int depth = 64 + (nch + ks - 1) / ks + ks + 2;
-    delta_s[tid] = route_delta(x2, __uint_as_float(wmax_bits), __uint_as_float(bmax_bits), depth);
-  }
-  __syncthreads();
-  route_select<EP, LPT>(a, t0, lg, delta_s);
-}
-
 // ----------------------------------------------------------------- f32 path
 // Plain fp32 FMA chains (no reduced-precision matrix path).  Thread = one
 // token (tid % 32) x experts tid/32 + 8 i.  K is summed in chunks of 64 from
@@ -475,19 +252,17 @@ __device__ __forceinline__ int nth_set_bit(unsigned long long m, int i) {
 // by (logit desc, id asc) is then taken over C with exact logits for the
 // ambiguous candidates and fp32 ones for the rest.  Weights come from the
 // stored fp32 softmax.
+// The wave's token t: fp32 logits (bias included) at row[0..E), softmax max,
+// sum, band and k-th logit at meta[0..3]; cv / ce / cd are the wave's own
+// kMaxE-entry scratch arrays.  Writes the token's ids and weights.
 template <typename ELEM>
-__global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
-  __shared__ float cv[4][kMaxE];     // candidate fp32 logits, in candidate order
-  __shared__ int ce[4][kMaxE];       // candidate expert ids
-  __shared__ double cd[4][kMaxE];    // candidate logits used for the final ranking
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
-  if (t >= a.T) return;
-  if (a.flag[t] == 0) return;
+__device__ void rerank_token(const RouteArgs& a, int64_t t, const float* row, const float* meta,
+                             float* cv, int* ce, double* cd) {
+  const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k, H = a.H;
   constexpr int VEC = 16 / sizeof(ELEM);
-  const float mx = a.meta[t * 4 + 0], s = a.meta[t * 4 + 1], band = a.meta[t * 4 + 2];
-  const float vk = a.meta[t * 4 + 3];
+  const float mx = meta[0], s = meta[1], band = meta[2];
+  const float vk = meta[3];
   const unsigned long long below = (1ull << lane) - 1ull;
 
   // candidate list (expert order), fp32 logits
@@ -496,17 +271,17 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    v[q] = (e < E) ? a.logits[t * E + e] : -INFINITY;
+    v[q] = (e < E) ? row[e] : -INFINITY;
     const bool cand = e < E && (vk - v[q]) <= band;
     const unsigned long long m = __ballot(cand);
     if (cand) {
       const int i = nc + __popcll(m & below);
-      cv[wave][i] = v[q];
-      ce[wave][i] = e;
+      cv[i] = v[q];
+      ce[i] = e;
     }
     nc += __popcll(m);
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_s_waitcnt(0);   // the wave's scratch writes (LDS or flat) are done
   __builtin_amdgcn_wave_barrier();
 
   // ambiguity and default (fp32) ranking logits; amb[q] of candidate lane + 64 q
@@ -517,10 +292,10 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
     const int i = lane + 64 * q;
     bool amb = false;
     if (i < nc) {
-      const float vi = cv[wave][i];
+      const float vi = cv[i];
       for (int j = 0; j < nc; ++j)
-        if (j != i && fabsf(vi - cv[wave][j]) <= band) amb = true;
-      cd[wave][i] = static_cast<double>(vi);
+        if (j != i && fabsf(vi - cv[j]) <= band) amb = true;
+      cd[i] = static_cast<double>(vi);
     }
     am[q] = __ballot(amb);
     na += __popcll(am[q]);
@@ -537,8 +312,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
 
   const ELEM* xrow = static_cast<const ELEM*>(a.x) + t * H;
   // P ambiguous candidates at a time (a power of two >= na, at most 8), G =
-  // 64 / P lanes each; a lane sums chunks sub, sub + G, ... with 4 loads of x
-  // and of W in flight
+  // 64 / P lanes each; a lane sums chunks sub, sub + G, ...
   const int P = na <= 1 ? 1 : na <= 2 ? 2 : na <= 4 ? 4 : 8;
   const int G = 64 / P;
   const int slot = lane / G, sub = lane % G;
@@ -560,98 +334,566 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
     }
     return acc;
   };
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   for (int r0 = 0; r0 < na; r0 += P) {
     const int r = r0 + slot;
     const bool live = r < na;
     const int ci = live ? amb_index(r) : 0;
-    const int ec = live ? ce[wave][ci] : 0;
+    const int ec = live ? ce[ci] : 0;
     const ELEM* wrow = static_cast<const ELEM*>(a.w) + static_cast<int64_t>(ec) * H;
+    // batches of NB chunks per lane, all their loads issued before any is
+    // used (one memory round trip per batch; H = 4096 with two candidates at
+    // a time is one batch)
+    constexpr int NB = 16;
     double accd = 0.0;
-    int c = sub;
-    for (; c + 3 * G < nchunk; c += 4 * G) {
-      uint4 xv[4], wv[4];
+    for (int c0 = sub; c0 < nchunk; c0 += NB * G) {
+      uint4 xv[NB], wv[NB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xv[u] = *reinterpret_cast<const uint4*>(xrow + (c + u * G) * VEC);
-        wv[u] = *reinterpret_cast<const uint4*>(wrow + (c + u * G) * VEC);
+      for (int u = 0; u < NB; ++u) {
+        const int c = c0 + u * G;
+        const int cc = c < nchunk ? c : sub;          // in-range address; its data is not used
+        xv[u] = *reinterpret_cast<const uint4*>(xrow + cc * VEC);
+        wv[u] = *reinterpret_cast<const uint4*>(wrow + cc * VEC);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) accd = dot_chunk(xv[u], wv[u], accd);
-    }
-    for (; c < nchunk; c += G) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + c * VEC);
-      const uint4 wv = *reinterpret_cast<const uint4*>(wrow + c * VEC);
-      accd = dot_chunk(xv, wv, accd);
+      for (int u = 0; u < NB; ++u)
+        if (c0 + u * G < nchunk) accd = dot_chunk(xv[u], wv[u], accd);
     }
     for (int off = 1; off < G; off <<= 1) accd += __shfl_xor(accd, off);
     if (a.bias) accd += static_cast<double>(a.bias[ec]);
-    if (live && sub == 0) cd[wave][ci] = accd;
+    if (live && sub == 0) cd[ci] = accd;
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
 
-  // exact top-k over the candidates, lane owns candidates lane + 64 q
-  double d[4];
-  int de[4];
+  // exact top-k over the candidates by rank: candidate i (lane + 64 q) is
+  // beaten by every candidate with a larger logit, or an equal logit and a
+  // lower id; those of rank < k take slot rank (no cross-lane reductions)
+  int rank[4], myid[4];
+  float myp[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int i = lane + 64 * q;
-    d[q] = i < nc ? cd[wave][i] : -INFINITY;
-    de[q] = i < nc ? ce[wave][i] : 0x7fffffff;
-  }
-  uint32_t taken = 0;
-  float p[kMaxK];
-  int ids[kMaxK];
-  float ps = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      double bv = -INFINITY;
-      int be = 0x7fffffff, bq = -1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (lane + 64 * q < nc && !((taken >> q) & 1u) && (d[q] > bv || (d[q] == bv && de[q] < be))) {
-          bv = d[q];
-          be = de[q];
-          bq = q;
-        }
+    rank[q] = kMaxE;
+    myid[q] = 0;
+    myp[q] = 0.f;
+    if (i < nc) {
+      const double di = cd[i];
+      const int ei = ce[i];
+      int r = 0;
+      for (int j = 0; j < nc; ++j) {
+        const double dj = cd[j];
+        r += (dj > di || (dj == di && ce[j] < ei)) ? 1 : 0;
       }
-      int bl = bq >= 0 ? lane + 64 * bq : 0x7fffffff;   // candidate index of the best
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        const int ol = __shfl_xor(bl, off);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bl = ol; }
-      }
-      if ((bl & 63) == lane) taken |= 1u << (bl >> 6);
-      // fp32 logit of the chosen expert from the lane that loaded it
-      const int q = be >> 6;
-      float lv = (q == 0) ? v[0] : (q == 1) ? v[1] : (q == 2) ? v[2] : v[3];
-      lv = __shfl(lv, be & 63);
-      ids[j] = be;
-      p[j] = __expf(lv - mx) / s;
-      ps += p[j];
+      rank[q] = r;
+      myid[q] = ei;
+      myp[q] = __expf(cv[i] - mx) / s;   // weights from the stored fp32 softmax
     }
   }
-  if (lane < k) {
-    float pj = 0.f;
-    int ej = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j == lane) { pj = p[j]; ej = ids[j]; }
-    a.ids[t * k + lane] = ej;
+  for (int q = 0; q < 4; ++q)
+    if (rank[q] < k) { ce[rank[q]] = myid[q]; cv[rank[q]] = myp[q]; }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) {
+    float ps = 0.f;
+    for (int j = 0; j < k; ++j) ps += cv[j];   // slot order, as the unflagged path sums
+    const float pj = cv[lane];
+    a.ids[t * k + lane] = ce[lane];
     a.weights[t * k + lane] = a.renorm ? pj / ps : pj;
   }
 }
 
-template <int EP>
-hipError_t launch_select_bf16(const RouteArgs& a, hipStream_t s) {
-  constexpr int NT = 256 / (EP / 8 > 8 ? EP / 8 : 8);
-  const unsigned grid = static_cast<unsigned>((a.T + NT - 1) / NT);
-  hipLaunchKernelGGL((route_select_bf16_kernel<EP>), dim3(grid), dim3(256), 0, s, a);
+template <typename ELEM>
+__global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
+  __shared__ float cv[4][kMaxE];     // candidate fp32 logits, in candidate order
+  __shared__ int ce[4][kMaxE];       // candidate expert ids
+  __shared__ double cd[4][kMaxE];    // candidate logits used for the final ranking
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  if (t >= a.T) return;
+  if (a.flag[t] == 0) return;
+  rerank_token<ELEM>(a, t, a.logits + t * a.E, a.meta + t * 4, cv[wave], ce[wave], cd[wave]);
+}
+
+// ---------------------------------------------------------- fused bf16 path
+// One workgroup owns BT tokens and every expert over the whole of H, and
+// does the whole router for them in one pass: logits (MFMA 16x16x32, rows
+// of x as A, router rows as B), bias, softmax, top-k, the exactness check,
+// and the float64 re-rank of the few tokens that fail it.  Nothing but ids
+// and weights leaves the workgroup (plus the logits and softmax statistics
+// when the caller keeps them).
+//
+// Waves: WE expert groups x WK K ranges (WE * WK = 4).  Wave w owns experts
+// [eg*EPW, (eg+1)*EPW), eg = w % WE, and the K32 steps
+// [kq*S/WK, (kq+1)*S/WK), kq = w / WE, S = H / 32.  Operands are loaded
+// straight into registers, PF steps ahead, four lanes per 64-byte row
+// segment, and moved into the MFMA operand layout (lane l: row l % 16, K
+// values 8*(l/16) .. 8*(l/16)+7 of the step) by a lane permutation; no LDS
+// memory and no barrier until the logits are complete.
+//
+// Summation (the structure the error bound counts): every MFMA starts from
+// zero (a chain of at most 32 roundings), the results of PF consecutive steps
+// are added into a group sum, group sums into the wave's sum, the WK wave
+// sums in K order, then the bias:
+//   D = 32 + PF + ceil(n / PF) + WK + 1,  n = K32 steps per wave.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// rounding depth D of a logit summed over n K32 steps per wave, groups of
+// g steps, wk wave sums
+__host__ __device__ constexpr int fused_depth(int n, int g, int wk) {
+  return 32 + g + (n + g - 1) / g + wk + 1;
+}
+
+// sum of squares of 8 bf16 by packed dot products (v_dot2_f32_bf16); every
+// term is non-negative, and a square the instruction might flush (below
+// 2^-126) is covered by the slack the norm gets before use
+__device__ __forceinline__ float sumsq8_dot(const bf16x8_t& v, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t p = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
+// v of the lane whose index differs from this one's in bit OFF (OFF < 32):
+// quad permutes by DPP, wider distances by ds_swizzle (xor mode within 32
+// lanes); neither needs an address register or LDS storage
+template <int OFF>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (OFF == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (OFF == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else return __builtin_amdgcn_ds_swizzle(v, (OFF << 10) | 0x1F);
+}
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __int_as_float(xor_lane<OFF>(__float_as_int(v)));
+}
+
+// (value, id) maximum over the LPT-lane group, ties to the lower id
+template <int LPT, int OFF = 1>
+__device__ __forceinline__ void group_argmax(float& bv, int& be) {
+  if constexpr (OFF < LPT) {
+    const float ov = xor_lane<OFF>(bv);
+    const int oe = xor_lane<OFF>(be);
+    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    group_argmax<LPT, OFF * 2>(bv, be);
+  }
+}
+template <int LPT, int OFF = 1>
+__device__ __forceinline__ float group_add(float v) {
+  if constexpr (OFF < LPT) return group_add<LPT, OFF * 2>(v + xor_lane<OFF>(v));
+  else return v;
+}
+
+// delta of the fused kernel.  The norms are fp32 sums of exact squares, each
+// within a relative (number of terms) * 2^-24 <= 2^-10 of its value (H <=
+// 16384); kSafety^3 covers both norms, their square roots and the product.
+__device__ __forceinline__ float fused_delta(float xsq, float wsq_max, float bmax, int depth) {
+  const float S = sqrtf(xsq) * sqrtf(wsq_max) * kSafety * kSafety * kSafety + bmax;
+  const float d = static_cast<float>(depth) * kUlp2;
+  return d * (1.f + d) * S * kSafety;
+}
+
+template <int BT, int EPW, int WE, int WK, int PF>
+__global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
+  static_assert(WE * WK == 4 && BT % 16 == 0 && EPW % 16 == 0 && 256 % BT == 0, "shape");
+  constexpr int NT = BT / 16, NJ = EPW / 16, EP = EPW * WE;
+  constexpr int LPT = 256 / BT;                 // select: lanes per token
+  constexpr int PER = EP / LPT;                 // select: logits per lane
+  static_assert(PER >= 1 && PER <= 32, "select layout");
+  __shared__ float lg[WK][BT][EP + 1];          // wave sums; lg[0] then holds the totals
+  __shared__ float xsq_s[WK][BT];
+  __shared__ float wsq_s[WK][EP];
+  __shared__ float fmeta[BT][4];                // flagged tokens: max, sum, band, k-th logit
+  __shared__ int flagged[BT];
+  __shared__ int nflag;
+  __shared__ unsigned wmax_bits, bmax_bits;
+  __shared__ float cv[4][kMaxE];                // re-rank: candidate fp32 logits (per wave)
+  __shared__ int ce[4][kMaxE];                  //          candidate expert ids
+  __shared__ double cd[4][kMaxE];               //          logits used for the final ranking
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int eg = wave % WE, kq = wave / WE;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  const int H = a.H, E = a.E, k = a.k;
+  const int64_t T = a.T;
+  const int S = H / 32;
+  const int sb = kq * S / WK, n = (kq + 1) * S / WK - sb;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  if (tid == 0) { nflag = 0; wmax_bits = 0u; bmax_bits = 0u; }
+
+  // ---- logits
+  // Loads are coalesced (four or sixteen lanes per row segment); the MFMA
+  // wants row l % 16 and the 16-byte chunk l / 16 of the step in lane l.
+  const int lrow = lane >> 2, lchk = lane & 3;
+  const char* wp[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int e = eg * EPW + 16 * j + lrow;
+    e = e < E ? e : E - 1;
+    wp[j] = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(e) * H +
+                                          sb * 32 + 8 * lchk);
+  }
+  // lane permutation into the MFMA layout: lane l takes the 16 bytes of the
+  // lane that loaded (row l % 16, chunk l / 16)
+  const int src_lane4 = 4 * (4 * r16 + g4);
+  auto to_mfma = [&](const bf16x8_t& v) {
+    const i32x4_t q = __builtin_bit_cast(i32x4_t, v);
+    i32x4_t o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_ds_bpermute(src_lane4, q[d]);
+    return __builtin_bit_cast(bf16x8_t, o);
+  };
+  // every load is unconditional (steps past the wave's range reload its last
+  // step, whose data is then not used), so that the loop body is straight-line
+  // code and the compiler's waits count exactly the loads in flight
+  const int slast = n > 0 ? n - 1 : 0;
+  auto clamp_step = [&](int s) { return s < slast ? s : slast; };
+  bf16x8_t wb[PF][NJ];
+  auto wload = [&](int s, bf16x8_t* wr) {
+    s = clamp_step(s);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wr[j] = *reinterpret_cast<const bf16x8_t*>(wp[j] + s * 64);
+  };
+
+  f32x4_t acc[NT][NJ], grp[NT][NJ];
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) { acc[i][j] = zero4; grp[i][j] = zero4; }
+  float wsq[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) wsq[j] = 0.f;
+  auto close_group = [&]() {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) { acc[i][j] += grp[i][j]; grp[i][j] = zero4; }
+  };
+  auto mfmas = [&](const bf16x8_t* xf, const bf16x8_t* wr) {
+    bf16x8_t wf[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wf[j] = to_mfma(wr[j]);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        grp[i][j] += __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], wf[j], zero4, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wsq[j] = sumsq8_dot(wr[j], wsq[j]);
+  };
+
+  if constexpr (WK == 1) {
+    // The four waves share x through LDS.  An iteration covers PF = 4 steps
+    // (256 bytes of each row): every wave loads BT / 4 rows of the next
+    // iteration (16 lanes per row), writes them to one of two LDS buffers
+    // (16-byte chunk c of row r in slot c ^ (r % 16): conflict-free both for
+    // the row-wise writes and for the MFMA reads of 16 rows at one chunk),
+    // and the waves meet at one barrier per iteration.
+    static_assert(PF == 4, "one iteration is 256 bytes of a row");
+    constexpr int XR = BT / 16;                   // 64-lane loads per wave per iteration
+    __shared__ uint4 xs[2][BT * 16];
+    const int xchk = lane & 15;
+    const char* xq[XR];
+    int xrow[XR];
+    float xsq[XR];
+#pragma unroll
+    for (int q = 0; q < XR; ++q) {
+      xrow[q] = 4 * (wave * XR + q) + (lane >> 4);
+      int64_t t = t0 + xrow[q];
+      t = t < T ? t : T - 1;
+      xq[q] = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.x) + t * H) + (xchk & 3) * 16;
+      xsq[q] = 0.f;
+    }
+    uint4 xr[XR];
+    auto xload = [&](int it) {
+      const int s = clamp_step(4 * it + (xchk >> 2));
+#pragma unroll
+      for (int q = 0; q < XR; ++q) xr[q] = *reinterpret_cast<const uint4*>(xq[q] + s * 64);
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < XR; ++q) {
+        xs[buf][xrow[q] * 16 + (xchk ^ (xrow[q] & 15))] = xr[q];
+        // token norms, one wave per row; a last partial iteration re-reads
+        // its last step, which only enlarges the norm (the bound stays valid)
+        xsq[q] = sumsq8_dot(__builtin_bit_cast(bf16x8_t, xr[q]), xsq[q]);
+      }
+    };
+    auto xfrags = [&](int buf, int u, bf16x8_t* xf) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        xf[i] = __builtin_bit_cast(bf16x8_t, xs[buf][(16 * i + r16) * 16 + ((4 * u + g4) ^ r16)]);
+    };
+    // prologue: x of iteration 0 in LDS, x of iteration 1 and W of iteration 0 in flight
+    xload(0);
+    xstore(0);
+    __builtin_amdgcn_sched_barrier(0);
+    xload(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      wload(u, wb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+    const int nfull = n / PF;
+    for (int it = 0; it < nfull; ++it) {
+      const int buf = it & 1;
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        bf16x8_t xf[NT];
+        xfrags(buf, u, xf);
+        mfmas(xf, wb[u]);
+        wload((it + 1) * PF + u, wb[u]);
+        if (u == 0) {
+          xstore(buf ^ 1);                        // x of iteration it + 1
+          xload(it + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      close_group();
+      lds_barrier();
+    }
+    const int rem = n - nfull * PF;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      if (u < rem) {
+        bf16x8_t xf[NT];
+        xfrags(nfull & 1, u, xf);
+        mfmas(xf, wb[u]);
+      }
+    }
+    close_group();
+    // norms of the rows this wave loaded: the 16 lanes of a row hold its chunks
+#pragma unroll
+    for (int q = 0; q < XR; ++q) {
+      float v = xsq[q] + xor_lane<1>(xsq[q]);
+      v += xor_lane<2>(v);
+      v += xor_lane<4>(v);
+      v += xor_lane<8>(v);
+      if (xchk == 0) xsq_s[0][xrow[q]] = v;
+    }
+  } else {
+    // WK K ranges: every wave has its own x columns, loaded to registers
+    const char* xp[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      int64_t t = t0 + 16 * i + lrow;
+      t = t < T ? t : T - 1;          // clamped rows are computed, never stored
+      xp[i] = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.x) + t * H + sb * 32 + 8 * lchk);
+    }
+    bf16x8_t xb[PF][NT];
+    float xsq[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) xsq[i] = 0.f;
+    auto load = [&](int s, int u) {
+      const int sc = clamp_step(s);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) xb[u][i] = *reinterpret_cast<const bf16x8_t*>(xp[i] + sc * 64);
+      wload(s, wb[u]);
+    };
+    auto step = [&](int u) {
+      bf16x8_t xf[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) xf[i] = to_mfma(xb[u][i]);
+      mfmas(xf, wb[u]);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) xsq[i] = sumsq8_dot(xb[u][i], xsq[i]);
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      load(u, u);
+      // issue order = step order here as in the loop, so that the count of
+      // newer loads is the same at every use (entry and back edge alike)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // PF steps per iteration, each iteration's sum closed into the wave's
+    // sum; the loop body is branch-free, the last n % PF steps run after it
+    const int nfull = n / PF;
+    for (int it = 0; it < nfull; ++it) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        step(u);
+        load((it + 1) * PF + u, u);
+        // keep this order: the loads of step s + PF go out right after step
+        // s, so each step's data has PF - 1 steps of work to arrive in
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      close_group();
+    }
+    const int rem = n - nfull * PF;
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < rem) step(u);
+    close_group();
+    // norms: the four lanes 4r .. 4r+3 of a quad hold the four chunks of row r
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      float v = xsq[i] + xor_lane<1>(xsq[i]);
+      v += xor_lane<2>(v);
+      if (lchk == 0) xsq_s[kq][16 * i + lrow] = v;
+    }
+  }
+
+  // wave sums to LDS: lane holds tokens 16 i + 4 g4 + v of expert column 16 j + r16
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lg[kq][16 * i + 4 * g4 + v][eg * EPW + 16 * j + r16] = acc[i][j][v];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float v = wsq[j] + xor_lane<1>(wsq[j]);
+    v += xor_lane<2>(v);
+    if (lchk == 0) wsq_s[kq][eg * EPW + 16 * j + lrow] = v;
+  }
+  __syncthreads();
+
+  // ---- totals (wave sums in K order), norm maxima
+  if constexpr (WK > 1) {
+    for (int c = tid; c < BT * EP; c += 256) {
+      const int tk = c / EP, e = c - tk * EP;
+      float v = lg[0][tk][e];
+#pragma unroll
+      for (int q = 1; q < WK; ++q) v += lg[q][tk][e];
+      lg[0][tk][e] = v;
+    }
+  }
+  if (tid < E) {
+    float w2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < WK; ++q) w2 += wsq_s[q][tid];
+    atomicMax(&wmax_bits, __float_as_uint(w2));
+    if (a.bias) atomicMax(&bmax_bits, __float_as_uint(fabsf(a.bias[tid])));
+  }
+  __syncthreads();
+
+  // ---- softmax, top-k, exactness check: LPT lanes per token
+  {
+    const int tok = tid / LPT, sub = tid % LPT;
+    const int64_t t = t0 + tok;
+    float x2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < WK; ++q) x2 += xsq_s[q][tok];
+    x2 += static_cast<float>(H) * 1.1754943508222875e-38f;   // H * 2^-126: flushed squares
+    const int nmax = (S + WK - 1) / WK;
+    const float delta = fused_delta(x2, __uint_as_float(wmax_bits), __uint_as_float(bmax_bits),
+                                    fused_depth(nmax, PF, WK));
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = sub + LPT * i;
+      v[i] = (e < E) ? lg[0][tok][e] + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float sel_v[kMaxK];
+    int sel_e[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int e = sub + LPT * i;
+          const bool free_ = !((taken >> i) & 1u) && e < E;
+          if (free_ && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+        }
+        group_argmax<LPT>(bv, be);
+        sel_v[j] = bv;
+        sel_e[j] = be;
+        if ((be % LPT) == sub) taken |= 1u << (be / LPT);
+      }
+    }
+    const float mx = sel_v[0];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (sub + LPT * i < E) sum += __expf(v[i] - mx);
+    sum = group_add<LPT>(sum);
+    const float band = 2.f * delta * kSafety;
+    const float vk = sel_v[k - 1];
+    float cnt = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (sub + LPT * i < E && (vk - v[i]) <= band) cnt += 1.f;
+    cnt = group_add<LPT>(cnt);
+    bool flag = cnt > static_cast<float>(k);
+#pragma unroll
+    for (int j = 0; j + 1 < kMaxK; ++j)
+      if (j + 1 < k && (sel_v[j] - sel_v[j + 1]) <= band) flag = true;
+
+    if (t < T) {
+      if (flag) {
+        if (sub == 0) {
+          const int slot = atomicAdd(&nflag, 1);
+          flagged[slot] = tok;
+          fmeta[tok][0] = mx; fmeta[tok][1] = sum; fmeta[tok][2] = band; fmeta[tok][3] = vk;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int e = sub + LPT * i;
+          if (e < E) lg[0][tok][e] = v[i];          // the re-rank reads logits with bias
+        }
+      } else {
+        float p[kMaxK];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+          if (j < k) { p[j] = __expf(sel_v[j] - mx) / sum; ps += p[j]; }
+        // slot j is written by lane j % LPT of the token's group (LPT may be < k)
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          if (j < k && j % LPT == sub) {
+            a.ids[t * k + j] = sel_e[j];
+            a.weights[t * k + j] = a.renorm ? p[j] / ps : p[j];
+          }
+        }
+      }
+      if (a.keep_all) {
+        if (sub == 0) {
+          a.meta[t * 4 + 0] = mx;
+          a.meta[t * 4 + 1] = sum;
+          a.meta[t * 4 + 2] = band;
+          a.meta[t * 4 + 3] = vk;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int e = sub + LPT * i;
+          if (e < E) a.logits[t * E + e] = v[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- float64 re-rank of the flagged tokens, one wave per token
+  const int nf = nflag;
+  for (int f = wave; f < nf; f += 4) {
+    const int tok = flagged[f];
+    rerank_token<uint16_t>(a, t0 + tok, &lg[0][tok][0], fmeta[tok], cv[wave], ce[wave], cd[wave]);
+  }
+}
+
+template <int BT, int EPW, int WE, int WK>
+hipError_t launch_fused(const RouteArgs& a, hipStream_t s) {
+  // shared x: iterations of 4 steps; K ranges: about 24 16-byte loads per
+  // lane in flight (96 registers)
+  constexpr int L = BT / 16 + EPW / 16;
+  constexpr int PF = WK == 1 ? 4 : (24 / L > 8 ? 8 : (24 / L < 3 ? 3 : 24 / L));
+  const unsigned grid = static_cast<unsigned>((a.T + BT - 1) / BT);
+  hipLaunchKernelGGL((route_fused_bf16_kernel<BT, EPW, WE, WK, PF>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -664,54 +906,44 @@ hipError_t launch_f32(const RouteArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int route_ksplit(int64_t T, int H, int E, bool bf16) {
-  if (!bf16) return 1;
-  // about 256 workgroups: split H when tokens x expert blocks are fewer
-  const int le = 32 * route_ne(E);
-  const int64_t wg = ((T + LT - 1) / LT) * ((E + le - 1) / le);
-  int64_t ks = wg > 0 ? 256 / wg : 1;
-  const int nch = H / LBK;
-  if (ks > nch) ks = nch;
-  if (ks > 16) ks = 16;
-  return ks < 1 ? 1 : static_cast<int>(ks);
-}
-
 size_t route_scratch_bytes(int64_t T, int H, int E, bool bf16) {
-  const size_t ks = static_cast<size_t>(route_ksplit(T, H, E, bf16));
+  (void)H;
+  (void)bf16;
   return align_up(static_cast<size_t>(T) * 4, 256) + align_up(static_cast<size_t>(T) * 16, 256) +
-         align_up(ks * static_cast<size_t>(T) * E * 4, 256) + align_up(ks * static_cast<size_t>(T) * 4, 256) +
-         align_up(ks * static_cast<size_t>(E) * 4, 256);
+         align_up(static_cast<size_t>(T) * E * 4, 256);
 }
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
   // every scratch region must have been carved before anything is launched
-  if (!a.x || !a.w || !a.ids || !a.weights || !a.flag || !a.meta || !a.logits ||
-      (bf16 && (!a.xnorm2 || !a.wnorm2)))
+  if (!a.x || !a.w || !a.ids || !a.weights || !a.flag || !a.meta || !a.logits)
     return hipErrorInvalidValue;
-  hipError_t err;
+  if (a.H % 64 || a.E < 1 || a.E > kMaxE || a.k < 1 || a.k > kMaxK || a.k > a.E) return hipErrorInvalidValue;
   if (bf16) {
-    if (a.ksplit < 1 || a.ksplit > a.H / LBK) return hipErrorInvalidValue;
-    const int le = 32 * route_ne(a.E);
-    const dim3 grid(static_cast<unsigned>((a.T + LT - 1) / LT), static_cast<unsigned>((a.E + le - 1) / le),
-                    static_cast<unsigned>(a.ksplit));
-    if (route_ne(a.E) == 4) hipLaunchKernelGGL(route_logits_bf16_kernel<4>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(route_logits_bf16_kernel<2>, grid, dim3(256), 0, s, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (a.E <= 32) err = launch_select_bf16<32>(a, s);
-    else if (a.E <= 64) err = launch_select_bf16<64>(a, s);
-    else if (a.E <= 128) err = launch_select_bf16<128>(a, s);
-    else err = launch_select_bf16<256>(a, s);
-  } else {
-    if (a.E <= 32) err = launch_f32<32>(a, s);
-    else if (a.E <= 64) err = launch_f32<64>(a, s);
-    else if (a.E <= 128) err = launch_f32<128>(a, s);
-    else err = launch_f32<256>(a, s);
+    const int64_t T = a.T;
+    // token blocks: about 512 workgroups (two per CU) up to 128 experts,
+    // 256 beyond (every workgroup reads all of W_r; measured on the
+    // fine, very fine and skewed workloads)
+    if (a.E <= 16) return launch_fused<16, 16, 1, 4>(a, s);
+    if (a.E <= 64) {
+      if (T >= 512 * 128) return launch_fused<128, 16, 4, 1>(a, s);
+      if (T >= 512 * 64) return launch_fused<64, 16, 4, 1>(a, s);
+      return launch_fused<32, 16, 4, 1>(a, s);
+    }
+    if (a.E <= 128) {
+      if (T >= 512 * 64) return launch_fused<64, 32, 4, 1>(a, s);
+      return launch_fused<32, 32, 4, 1>(a, s);
+    }
+    if (T >= 256 * 32) return launch_fused<32, 64, 4, 1>(a, s);
+    return launch_fused<16, 64, 4, 1>(a, s);
   }
+  hipError_t err;
+  if (a.E <= 32) err = launch_f32<32>(a, s);
+  else if (a.E <= 64) err = launch_f32<64>(a, s);
+  else if (a.E <= 128) err = launch_f32<128>(a, s);
+  else err = launch_f32<256>(a, s);
   if (err != hipSuccess) return err;
   const unsigned grid = static_cast<unsigned>((a.T + 3) / 4);
-  if (bf16) hipLaunchKernelGGL((route_refine_kernel<uint16_t>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((route_refine_kernel<float>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((route_refine_kernel<float>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -33,6 +33,16 @@ CASES = [
     (50, 64, 5, 5, "bf16", False, "zero"),
     (77, 512, 256, 1, "bf16", False, "zero"),
     (129, 2048, 64, 4, "bf16", False, "zipf1.2"),
+    # token counts that select every token-block shape of the one-pass bf16
+    # router (16 to 128 tokens per workgroup, 2 to 16 lanes per token, k up
+    # to 8 slots over fewer lanes than slots)
+    (16384 + 77, 64, 40, 8, "bf16", False, "zero"),
+    (65536 + 9, 64, 64, 8, "bf16", False, "zero"),
+    (32768 + 7, 64, 128, 8, "bf16", False, "zero"),
+    (32768 + 5, 64, 64, 8, "bf16", True, "zero"),
+    (16384 + 3, 64, 128, 8, "bf16", True, "zero"),
+    (8192 + 33, 64, 256, 8, "bf16", False, "zero"),
+    (8192 + 31, 128, 200, 6, "bf16", False, "zipf1.2"),
     (100, 64, 8, 2, "f32", False, "zero"),
     (257, 256, 64, 4, "f32", True, "zero"),
     (65, 128, 256, 8, "f32", False, "zipf1.2"),
