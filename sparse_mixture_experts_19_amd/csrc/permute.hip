@@ -126,20 +126,29 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a) {
   }
 }
 
-// x_perm[r] = x[perm[r] / k], 16-byte chunks.
+// x_perm[r] = x[perm[r] / k]: one workgroup per row, thread i copying the
+// 16-byte chunks i, i + 256, ... (the source row index is workgroup-uniform,
+// read once; no per-chunk division).
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
-                                                          int64_t M, int64_t T, int chunks,
-                                                          int k, uint4* __restrict__ xp) {
-  const int64_t total = M * chunks;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t r = i / chunks;
-    const int c = static_cast<int>(i - r * chunks);
-    int64_t src = perm[r] / k;
-    src = src < 0 ? 0 : (src >= T ? T - 1 : src);   // malformed perm stays in bounds
-    xp[i] = x[src * chunks + c];
+                                                          int64_t T, int chunks, int k,
+                                                          uint4* __restrict__ xp) {
+  const int64_t r = blockIdx.x;
+  int64_t src = perm[r] / k;
+  src = src < 0 ? 0 : (src >= T ? T - 1 : src);   // malformed perm stays in bounds
+  const uint4* in = x + src * chunks;
+  uint4* o = xp + r * chunks;
+  // x_perm is written once and read later by another kernel: nontemporal
+  // stores keep it from evicting the rows of x, which k slots re-read
+  typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+  u32x4_nt* on = reinterpret_cast<u32x4_nt*>(o);
+  int c = threadIdx.x;
+  for (; c + 256 < chunks; c += 512) {
+    const uint4 a = in[c], b = in[c + 256];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, a), on + c);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, b), on + c + 256);
   }
+  if (c < chunks) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, in[c]), on + c);
 }
 
 __global__ void dense_offsets_kernel(int32_t* offsets, int64_t M) {
@@ -184,15 +193,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
 
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
                               int elem_bytes, void* x_perm, hipStream_t s) {
+  if (M > 0x7fffffff || k < 1) return hipErrorInvalidValue;
   const int chunks = H * elem_bytes / 16;
-  const int64_t total = M * chunks;
-  int64_t grid = (total + 255) / 256;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), perm, M, M / k, chunks, k,
-                     static_cast<uint4*>(x_perm));
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), perm, M / k, chunks, k, static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 
