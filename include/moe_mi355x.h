@@ -125,6 +125,28 @@ int moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int32_t H,
                 void* stream);
 
 /*
+ * moe_permute_static -- moe_permute for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * kernels as moe_permute without the workspace; the per-chunk expert
+ * histograms live in a 4 MiB device array the library owns (one per GPU,
+ * held until the process ends, its address looked up on the first call on
+ * each device).  Nothing is allocated or freed, and every entry of that
+ * array a call reads was written by the same call (no zeroing needed).
+ *
+ * Limit: ceil(T*k / 1024) * E <= 1048576 histogram entries (for E = 256,
+ * T*k <= 4194304); larger problems return MOE_ERR_UNSUPPORTED before any
+ * launch.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (different streams or host threads without ordering)
+ * race and give undefined results.
+ */
+int moe_permute_static(const int32_t* topk_ids, const void* x, int64_t T,
+                       int32_t H, int32_t E, int32_t k, int32_t dtype,
+                       int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* perm, int32_t* inv_perm, void* x_perm,
+                       void* stream);
+
+/*
  * moe_grouped_swiglu_gemm -- steps 5-6: every expert's SwiGLU MLP over its
  * rows, in one grouped compute ([Qwen3-MoE page] §2.1: stacked expert
  * weights, one batched launch scheduled over the compute units).

@@ -55,6 +55,7 @@ class Mxfp8Layout(ctypes.Structure):
 _SIGS = {
     "moe_route": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
     "moe_permute": [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+    "moe_permute_static": [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_grouped_swiglu_gemm": [_vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_sz, _vp],
     "moe_combine": [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _vp, _vp],
     "moe_forward": [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_sz, _vp],
@@ -190,6 +191,27 @@ def moe_permute(topk_ids, E: int, x=None, workspace=None):
     _check(lib().moe_permute(_ptr(topk_ids), _ptr(x), T, H, E, k, dt, _ptr(counts), _ptr(offsets),
                              _ptr(perm), _ptr(inv), _ptr(x_perm), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(dev)))
+    return counts, offsets, perm, inv, x_perm
+
+
+def moe_permute_static(topk_ids, E: int, x=None, out=None):
+    """moe_permute without a workspace (the library's own device scratch).
+    ``out``: optional (counts, offsets, perm, inv, x_perm) tensors to write.
+    Returns (counts, offsets, perm, inv, x_perm)."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    H = x.shape[1] if x is not None else 64
+    dt = _dtype_code(x.dtype) if x is not None else MOE_DTYPE_BF16
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty((T * k, H), dtype=x.dtype, device=dev) if x is not None else None)
+    counts, offsets, perm, inv, x_perm = out
+    _check(lib().moe_permute_static(_ptr(topk_ids), _ptr(x), T, H, E, k, dt, _ptr(counts),
+                                    _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(x_perm),
+                                    _stream(dev)))
     return counts, offsets, perm, inv, x_perm
 
 

@@ -353,6 +353,40 @@ int moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int32_t H, in
   return ok();
 }
 
+int moe_permute_static(const int32_t* topk_ids, const void* x, int64_t T, int32_t H, int32_t E,
+                       int32_t k, int32_t dtype, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* perm, int32_t* inv_perm, void* x_perm, void* stream) {
+  MOE_CHECK(check_sizes(T, H, 64, E, k, dtype, false));
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x and x_perm must both be set or both be NULL");
+  if (T == 0) return ok();
+  MOE_CHECK(need_ptr(topk_ids, "topk_ids", 4));
+  MOE_CHECK(need_ptr(expert_counts, "expert_counts", 4));
+  MOE_CHECK(need_ptr(expert_offsets, "expert_offsets", 4));
+  MOE_CHECK(need_ptr(perm, "perm", 4));
+  MOE_CHECK(need_ptr(inv_perm, "inv_perm", 4));
+  if (x) {
+    MOE_CHECK(need_ptr(x, "x", 16));
+    MOE_CHECK(need_ptr(x_perm, "x_perm", 16));
+  }
+  const int64_t M = T * k;
+  const size_t need = moe::permute_scratch_bytes(M, E);
+  if (need > moe::kPermStaticScratchInts * sizeof(int32_t))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_permute_static: ceil(T*k/%d)*E = %zu histogram entries exceed the library's "
+                "static scratch of %zu; use moe_permute with a workspace",
+                moe::kPermChunk, need / sizeof(int32_t), moe::kPermStaticScratchInts);
+  int dev = -1;
+  MOE_CHECK(current_device(&dev, nullptr));
+  int32_t* scratch = nullptr;
+  MOE_HIP(moe::permute_static_scratch(dev, &scratch));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_CHECK(run_permute(topk_ids, M, E, k, expert_counts, expert_offsets, perm, inv_perm,
+                        reinterpret_cast<char*>(scratch), s));
+  if (x) MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, elem_bytes(dtype), x_perm, s));
+  return ok();
+}
+
 int moe_grouped_swiglu_gemm(const void* x_perm, const int32_t* expert_offsets, const void* w13,
                             const void* w2, int64_t M, int32_t H, int32_t I, int32_t E,
                             int32_t dtype, void* h, void* y, void* workspace,

@@ -69,6 +69,11 @@ struct PermuteArgs {
 };
 size_t permute_scratch_bytes(int64_t M, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Allocation-free permutation: int32 entries of the library's own device
+// array for the chunk histograms (4 MiB per GPU), and its address on
+// `device`, which must be the current device (looked up once per device).
+constexpr size_t kPermStaticScratchInts = size_t(1) << 20;
+hipError_t permute_static_scratch(int device, int32_t** ptr);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
                               int elem_bytes, void* x_perm, hipStream_t s);
 

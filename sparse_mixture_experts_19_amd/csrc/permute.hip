@@ -18,6 +18,8 @@
 //      elements in order (wave match + LDS prefix) and writes perm / inv.
 #include "moe_internal.h"
 
+#include <mutex>
+
 namespace moe {
 namespace {
 
@@ -177,6 +179,34 @@ __global__ __launch_bounds__(256) void tile_schedule_kernel(const int32_t* offse
 }
 
 }  // namespace
+
+// ------------------------------------------- allocation-free permutation
+// The per-chunk expert histograms of moe_permute_static live in this
+// file-scope device array (each GPU holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel: the name is
+// a host-side stand-in, and the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) int32_t scratch[kPermStaticScratchInts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t permute_static_scratch(int device, int32_t** ptr) {
+  if (device < 0 || device >= kMaxDevices || !ptr) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = static_cast<int32_t*>(p);
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 size_t permute_scratch_bytes(int64_t M, int E) {
   const int64_t nb = (M + CH - 1) / CH;
