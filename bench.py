@@ -368,6 +368,8 @@ def main():
         d = {"ms": round(stage_ms[s], 5)}
         if alg[s]["bytes"]:
             d["GB/s"] = round(alg[s]["bytes"] / t / 1e9, 1)
+            if not alg[s]["flops"]:
+                d["frac_hbm"] = round(alg[s]["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
         if alg[s]["flops"]:
             d["TFLOP/s"] = round(alg[s]["flops"] / t / 1e12, 1)
         detail[s] = d
@@ -380,6 +382,21 @@ def main():
     g_flops = sum(alg[s]["flops"] for s in gemm_stages)
     peak = PEAK_FP8_TFLOPS if MX else PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     grouped_tflops = g_flops / g_t / 1e12
+    # attainable rate of the two forward GEMMs: min(MFMA peak, intensity x HBM peak)
+    fw_bytes = sum(alg[s]["bytes"] for s in ("gemm_gate_up_swiglu", "gemm_down"))
+    fw_flops = sum(alg[s]["flops"] for s in ("gemm_gate_up_swiglu", "gemm_down"))
+    attainable = min(peak, fw_flops / fw_bytes * PEAK_HBM_GBS / 1e3) if fw_bytes else peak
+
+    # expert loads ([Qwen3-MoE page] §3 suggests watching their spread) and
+    # the router's share of the step ([Hunyuan page] §六.2 puts routing at
+    # about 15% extra compute)
+    cnt = np.asarray(counts, dtype=np.float64)
+    load = {"counts": [int(c) for c in counts], "mean": round(float(cnt.mean()), 2),
+            "std": round(float(cnt.std()), 2),
+            "std_over_mean": round(float(cnt.std() / cnt.mean()), 4) if cnt.mean() else None,
+            "max": int(cnt.max()), "max_over_mean": round(float(cnt.max() / cnt.mean()), 3) if cnt.mean() else None,
+            "empty_experts": int((cnt == 0).sum())}
+    step_stage_ms = sum(stage_ms.values())
 
     # dominant kernel roofline
     dom = max(stages, key=lambda s: stage_ms[s])
@@ -428,7 +445,11 @@ def main():
                    "router_bias": wl.bias, "parallelism": "single GPU"},
         "grouped_gemm": {"TFLOP/s": round(grouped_tflops, 1),
                          "frac_of_peak": round(grouped_tflops / peak, 4),
+                         "attainable_TFLOP/s": round(attainable, 1),
+                         "frac_of_attainable": round(grouped_tflops / attainable, 4),
                          "padding_waste_bm256": round(padding_waste(counts), 4)},
+        "expert_load": load,
+        "router_time_share": round(stage_ms.get("route", 0.0) / step_stage_ms, 4) if step_stage_ms else None,
         "stages": detail,
         "roofline": roof,
     }
