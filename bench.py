@@ -58,7 +58,6 @@ def algorithmic(wl, counts, Is: int = 0, mx: bool = False):
     st = {}
     st["route"] = dict(bytes=T * H * b + E * H * b + 8 * M, flops=2 * T * H * E)
     st["permute"] = dict(bytes=4 * M + 4 * M + 4 * M + 8 * E, flops=0)
-    st["schedule"] = dict(bytes=8 * E, flops=0)
     st["quantize_x"] = dict(bytes=T * H * b + T * H * (1 + 1 / 32), flops=0)
     st["gemm_gate_up_swiglu"] = dict(flops=4 * M * H * I,
                                      bytes=2 * active * I * H * q + M * H * q + M * I * q + 4 * M)
@@ -155,8 +154,12 @@ def standalone_calls(B, x, wr, bias, w13, w2, wl, iters: int = 10):
     def route():
         B.moe_route(x, wr, bias, k, wl.renormalize, ids, wts, ws_r)
 
+    pout = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+            torch.empty(T * k, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev),
+            torch.empty((T * k, H), dtype=x.dtype, device=dev))
+
     def permute():
-        state["p"] = B.moe_permute(ids, E, x, ws_p)
+        state["p"] = B.moe_permute(ids, E, x, ws_p, out=pout)
 
     def gemm():
         B.moe_grouped_swiglu_gemm(state["p"][4], state["p"][1], w13, w2, h, y, ws_g)

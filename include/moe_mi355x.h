@@ -209,14 +209,14 @@ int moe_forward(const void* x, const void* w_router, const float* router_bias,
  * (passed as void*), n_events == MOE_PROFILE_EVENTS.  events[i] is recorded
  * before stage i and events[MOE_PROFILE_EVENTS-1] after the last stage:
  *   0 router (logits, softmax, top-k, float64 re-rank)
- *   1 permutation (histogram, scan, stable scatter)
- *   2 tile schedule of the grouped GEMMs
- *   3 gate/up grouped GEMM with the SiLU(gate)*up epilogue
- *   4 down grouped GEMM
- *   5 combine
+ *   1 permutation (histogram, scan, stable scatter; also the grouped GEMMs'
+ *     tile schedule)
+ *   2 gate/up grouped GEMM with the SiLU(gate)*up epilogue
+ *   3 down grouped GEMM
+ *   4 combine
  * Arguments and results are otherwise those of moe_forward.
  */
-#define MOE_PROFILE_EVENTS 7
+#define MOE_PROFILE_EVENTS 6
 int moe_forward_profiled(const void* x, const void* w_router,
                          const float* router_bias, const void* w13,
                          const void* w2, int64_t T, int32_t H, int32_t I,
@@ -294,11 +294,11 @@ int moe_forward_shared(const void* x, const void* w_router,
 /*
  * moe_forward_shared_profiled -- moe_forward_shared recording caller-created
  * HIP events around its stages (as moe_forward_profiled), n_events ==
- * MOE_PROFILE_EVENTS_SHARED: stages 0..4 as moe_forward_profiled, then
- *   5 shared expert (gate/up and down GEMMs over every token)
- *   6 combine (routed slots plus the shared output)
+ * MOE_PROFILE_EVENTS_SHARED: stages 0..3 as moe_forward_profiled, then
+ *   4 shared expert (gate/up and down GEMMs over every token)
+ *   5 combine (routed slots plus the shared output)
  */
-#define MOE_PROFILE_EVENTS_SHARED 8
+#define MOE_PROFILE_EVENTS_SHARED 7
 int moe_forward_shared_profiled(const void* x, const void* w_router,
                                 const float* router_bias, const void* w13,
                                 const void* w2, const void* ws13,
@@ -369,10 +369,10 @@ int moe_forward_rounded(const void* x, const void* w_router,
  *   0 router (also keeps every token's logits, softmax max and sum)
  *   1 token rounding (permutation of the routed ids, pooled slots, tile
  *     hand-out, new weights)
- *   2 permutation of the rounded ids
- *   3..6 tile schedule, gate/up GEMM, down GEMM, combine
+ *   2 permutation of the rounded ids (and the GEMMs' tile schedule)
+ *   3..5 gate/up GEMM, down GEMM, combine
  */
-#define MOE_PROFILE_EVENTS_ROUNDED 8
+#define MOE_PROFILE_EVENTS_ROUNDED 7
 int moe_forward_rounded_profiled(const void* x, const void* w_router,
                                  const float* router_bias, const void* w13,
                                  const void* w2, int64_t T, int32_t H,
@@ -451,11 +451,11 @@ int moe_forward_mxfp8(const void* x, const void* w_router,
 /*
  * moe_forward_mxfp8_profiled -- moe_forward_mxfp8 recording caller-created
  * HIP events around its stages (as moe_forward_profiled), n_events ==
- * MOE_PROFILE_EVENTS_MXFP8: 0 router, 1 permutation, 2 quantization of x
- * and the stage-major scale words, 3 tile schedule, 4 gate/up GEMM (with the quantization of h), 5 down GEMM,
- * 6 combine.
+ * MOE_PROFILE_EVENTS_MXFP8: 0 router, 1 permutation (and the GEMMs' tile
+ * schedule), 2 quantization of x and the stage-major scale words, 3 gate/up
+ * GEMM (with the quantization of h), 4 down GEMM, 5 combine.
  */
-#define MOE_PROFILE_EVENTS_MXFP8 8
+#define MOE_PROFILE_EVENTS_MXFP8 7
 int moe_forward_mxfp8_profiled(const void* x, const void* w_router,
                                const float* router_bias, const uint8_t* w13q,
                                const uint8_t* w13s, const uint8_t* w2q,

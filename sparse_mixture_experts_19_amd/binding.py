@@ -175,18 +175,21 @@ def moe_route(x, w_router, router_bias, k: int, renormalize: bool, topk_ids=None
     return topk_ids, topk_weights
 
 
-def moe_permute(topk_ids, E: int, x=None, workspace=None):
+def moe_permute(topk_ids, E: int, x=None, workspace=None, out=None):
     """Expert histogram, offsets, stable expert-sorted permutation and its inverse;
-    with ``x`` also the reordered rows.  Returns (counts, offsets, perm, inv, x_perm)."""
+    with ``x`` also the reordered rows.  ``out``: optional (counts, offsets, perm,
+    inv, x_perm) tensors to write.  Returns (counts, offsets, perm, inv, x_perm)."""
     T, k = topk_ids.shape
     dev = topk_ids.device
     H = x.shape[1] if x is not None else 64
     dt = _dtype_code(x.dtype) if x is not None else MOE_DTYPE_BF16
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev) if x is not None else None
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty((T * k, H), dtype=x.dtype, device=dev) if x is not None else None)
+    counts, offsets, perm, inv, x_perm = out
     ws = _workspace(workspace_size(ENTRY_PERMUTE, T, H, 64, E, k, dt), dev, workspace)
     _check(lib().moe_permute(_ptr(topk_ids), _ptr(x), T, H, E, k, dt, _ptr(counts), _ptr(offsets),
                              _ptr(perm), _ptr(inv), _ptr(x_perm), _ptr(ws),
@@ -263,8 +266,8 @@ def moe_forward(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, ou
     return out, ws
 
 
-PROFILE_EVENTS = 7
-PROFILE_STAGES = ("route", "permute", "schedule", "gemm_gate_up_swiglu", "gemm_down", "combine")
+PROFILE_EVENTS = 6
+PROFILE_STAGES = ("route", "permute", "gemm_gate_up_swiglu", "gemm_down", "combine")
 
 
 def moe_forward_profiled(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, out,
@@ -292,8 +295,8 @@ def shared_layout(T: int, H: int, I: int, Is: int, E: int, k: int, dtype: int) -
     return L
 
 
-PROFILE_EVENTS_SHARED = 8
-PROFILE_STAGES_SHARED = ("route", "permute", "schedule", "gemm_gate_up_swiglu", "gemm_down",
+PROFILE_EVENTS_SHARED = 7
+PROFILE_STAGES_SHARED = ("route", "permute", "gemm_gate_up_swiglu", "gemm_down",
                          "shared_expert", "combine")
 
 
@@ -350,8 +353,8 @@ def gemm_tile_rows(dtype: int) -> int:
     return n
 
 
-PROFILE_EVENTS_ROUNDED = 8
-PROFILE_STAGES_ROUNDED = ("route", "token_round", "permute", "schedule", "gemm_gate_up_swiglu",
+PROFILE_EVENTS_ROUNDED = 7
+PROFILE_STAGES_ROUNDED = ("route", "token_round", "permute", "gemm_gate_up_swiglu",
                           "gemm_down", "combine")
 
 
@@ -427,8 +430,8 @@ def mxfp8_layout(T: int, H: int, I: int, E: int, k: int,
     return L
 
 
-PROFILE_EVENTS_MXFP8 = 8
-PROFILE_STAGES_MXFP8 = ("route", "permute", "quantize_x", "schedule", "gemm_gate_up_swiglu",
+PROFILE_EVENTS_MXFP8 = 7
+PROFILE_STAGES_MXFP8 = ("route", "permute", "quantize_x", "gemm_gate_up_swiglu",
                         "gemm_down", "combine")
 
 

@@ -203,11 +203,15 @@ int run_route(const void* x, const void* w_router, const float* bias, int64_t T,
   return MOE_OK;
 }
 
+// tile_prefix (optional): also write the grouped GEMM's m-tile prefix for
+// tiles of tile_bm rows (the permutation's last pass does it in passing).
 int run_permute(const int32_t* ids, int64_t M, int E, int k, int32_t* counts, int32_t* offsets,
-                int32_t* perm, int32_t* inv, char* scratch, hipStream_t s) {
+                int32_t* perm, int32_t* inv, char* scratch, hipStream_t s,
+                int32_t* tile_prefix = nullptr, int tile_bm = 0) {
   moe::PermuteArgs a{};
   a.ids = ids; a.M = M; a.E = E; a.k = k; a.counts = counts; a.offsets = offsets;
   a.perm = perm; a.inv = inv; a.block_hist = reinterpret_cast<int32_t*>(scratch);
+  a.tile_prefix = tile_prefix; a.tile_bm = tile_bm;
   MOE_HIP(moe::launch_permute(a, s));
   return MOE_OK;
 }
@@ -251,7 +255,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int moe_version(void) { return 105; }
+int moe_version(void) { return 106; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -349,7 +353,7 @@ int moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int32_t H, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_CHECK(run_permute(topk_ids, M, E, k, expert_counts, expert_offsets, perm, inv_perm,
                         static_cast<char*>(workspace), s));
-  if (x) MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, elem_bytes(dtype), x_perm, s));
+  if (x) MOE_HIP(moe::launch_gather_rows(x, inv_perm, T, H, k, elem_bytes(dtype), x_perm, s));
   return ok();
 }
 
@@ -383,7 +387,7 @@ int moe_permute_static(const int32_t* topk_ids, const void* x, int64_t T, int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_CHECK(run_permute(topk_ids, M, E, k, expert_counts, expert_offsets, perm, inv_perm,
                         reinterpret_cast<char*>(scratch), s));
-  if (x) MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, elem_bytes(dtype), x_perm, s));
+  if (x) MOE_HIP(moe::launch_gather_rows(x, inv_perm, T, H, k, elem_bytes(dtype), x_perm, s));
   return ok();
 }
 
@@ -493,6 +497,7 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   const int64_t M = T * k;
   char* shared = w + L.scratch + gemm_scratch(M, H, I, E, dtype);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
+  const int bm = bf16 ? moe::kGemmBM : moe::kF32BM;
   int next_event = 0;
   auto mark = [&]() -> int {
     if (events) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(events[next_event]), s));
@@ -519,15 +524,14 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
     moe::carve_round(xs, r);
     MOE_HIP(moe::launch_token_round(r, s));
     MOE_CHECK(mark());
-    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, ps, s));
+    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, ps, s, prefix, bm));
   } else {
     MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared,
                         s));
     MOE_CHECK(mark());
-    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
+    MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s, prefix, bm));
   }
-  MOE_CHECK(mark());
-  MOE_HIP(moe::launch_tile_schedule(offsets, E, bf16 ? moe::kGemmBM : moe::kF32BM, M, prefix, s));
+  // (the permutation's last pass also wrote the GEMMs' tile prefix)
   MOE_CHECK(mark());
   moe::GemmArgs g{};
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M; g.a_rows = T;
@@ -540,7 +544,7 @@ int forward_impl(const void* x, const void* w_router, const float* router_bias, 
   if (bf16 && !moe::gemm_gather_fits(T, H, 2)) {
     // x spans more than 2^32 bytes: gather its rows into the (not yet used)
     // down-projection output buffer, which has the same [M, H] shape
-    MOE_HIP(moe::launch_gather_rows(x, perm, M, H, k, 2, w + L.y, s));
+    MOE_HIP(moe::launch_gather_rows(x, inv, T, H, k, 2, w + L.y, s));
     g.A = w + L.y; g.gather = nullptr; g.gather_div = 1; g.a_rows = M;
   }
   g.B = w13; g.b_stride = static_cast<int64_t>(2) * I * H;
@@ -812,7 +816,8 @@ int forward_mxfp8_impl(const void* x, const void* w_router, const float* router_
   MOE_CHECK(mark());
   MOE_CHECK(run_route(x, w_router, router_bias, T, H, E, k, dtype, renormalize, ids, wts, shared, s));
   MOE_CHECK(mark());
-  MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s));
+  MOE_CHECK(run_permute(ids, M, E, k, counts, offsets, perm, inv, shared, s, prefix,
+                        moe::kGemmBM));
   MOE_CHECK(mark());
   MOE_HIP(moe::launch_mx_quantize(x, true, T, H, xq, xs, s));
   // stage-major scale words for the GEMMs: x's in the expert-sorted row order
@@ -823,8 +828,6 @@ int forward_mxfp8_impl(const void* x, const void* w_router, const float* router_
   MOE_HIP(moe::launch_mx_scale_words(xs, M, H, perm, k, xsw, s));
   MOE_HIP(moe::launch_mx_scale_words(w13s, static_cast<int64_t>(E) * 2 * I, H, nullptr, 1, w13sw, s));
   MOE_HIP(moe::launch_mx_scale_words(w2s, static_cast<int64_t>(E) * H, I, nullptr, 1, w2sw, s));
-  MOE_CHECK(mark());
-  MOE_HIP(moe::launch_tile_schedule(offsets, E, moe::kGemmBM, M, prefix, s));
   MOE_CHECK(mark());
   moe::GemmArgs g{};
   g.E = E; g.offsets = offsets; g.prefix = prefix; g.I = I; g.M = M;

@@ -66,7 +66,12 @@ struct PermuteArgs {
   int32_t* perm;          // [M]
   int32_t* inv;           // [M]
   int32_t* block_hist;    // [nblocks, E] scratch
+  int32_t* tile_prefix;   // [E+1] or NULL: m-tiles of tile_bm rows per expert, exclusive prefix
+  int tile_bm;
 };
+// chunks x experts up to which each scatter workgroup sums the chunk
+// histograms itself (no separate scan pass)
+constexpr int64_t kPermInlineScan = 32768;
 size_t permute_scratch_bytes(int64_t M, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 // Allocation-free permutation: int32 entries of the library's own device
@@ -74,7 +79,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 // `device`, which must be the current device (looked up once per device).
 constexpr size_t kPermStaticScratchInts = size_t(1) << 20;
 hipError_t permute_static_scratch(int device, int32_t** ptr);
-hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
+// x_perm[inv[t*k + j]] = x[t]: T tokens of H elements of elem_bytes each.
+hipError_t launch_gather_rows(const void* x, const int32_t* inv, int64_t T, int H, int k,
                               int elem_bytes, void* x_perm, hipStream_t s);
 
 // offsets[0] = 0, offsets[1] = M: one dense group of M rows.

@@ -10,12 +10,17 @@
 //   offsets    = exclusive prefix sum of counts (E+1 entries)
 //   perm[r]    = f of row r, rows in (expert, f) order (stable)
 //   inv[f]     = r with perm[r] == f
-// Three passes, all deterministic and free of order-deciding atomics:
-//   1. per-chunk expert histograms (LDS integer counters),
-//   2. one workgroup per expert scans its chunk counts into chunk-local row
-//      bases and the expert's count,
-//   3. each chunk derives the expert offsets from the counts, ranks its
-//      elements in order (wave match + LDS prefix) and writes perm / inv.
+// Deterministic passes, free of order-deciding atomics:
+//   1. per-chunk expert histograms (LDS integer counters);
+//   2. each chunk sums the histograms of the chunks before it (its row base
+//      inside each expert) and of all chunks (the expert counts), derives
+//      the expert offsets, ranks its elements in order (wave match + LDS
+//      prefix) and writes perm / inv; the first chunk also writes counts,
+//      offsets and, when asked, the grouped GEMM's tile prefix.
+// When the histogram table is large (chunks x experts above 32768 entries)
+// those sums would cost each chunk too many loads: a separate pass with one
+// workgroup per expert then turns the table into chunk bases and counts
+// first, and pass 2 reads them from there.
 #include "moe_internal.h"
 
 #include <mutex>
@@ -75,22 +80,75 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(PermuteArgs a, int nbloc
   if (tid == 0) a.counts[e] = carry;
 }
 
-__global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a) {
+// INLINE_SCAN: block_hist holds the raw chunk histograms (chunk-major) and
+// this kernel sums them; otherwise perm_scan_kernel has already turned them
+// into chunk bases and written the counts.
+template <bool INLINE_SCAN>
+__global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a, int nb) {
   __shared__ int base[kMaxE];
   __shared__ int wc[4][kMaxE];
   __shared__ int buf[256];
+  __shared__ int red[2][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
+  const int bx = blockIdx.x;
+  int cnt = 0, before = 0;   // expert tid: rows in all chunks / in chunks before this one
+  if constexpr (INLINE_SCAN) {
+    // thread (g, e) sums chunks g, g + G, ... of column e; eight loads in
+    // flight per thread
+    const int G = 256 / E;
+    int tot = 0, bef = 0;
+    if (tid < G * E) {
+      const int g = tid / E, e = tid - g * E;
+      const int32_t* h = a.block_hist + e;
+      int b = g;
+      for (; b + 7 * G < nb; b += 8 * G) {
+        int v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = h[static_cast<int64_t>(b + q * G) * E];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          tot += v[q];
+          if (b + q * G < bx) bef += v[q];
+        }
+      }
+      for (; b < nb; b += G) {
+        const int v = h[static_cast<int64_t>(b) * E];
+        tot += v;
+        if (b < bx) bef += v;
+      }
+    }
+    red[0][tid] = tot;
+    red[1][tid] = bef;
+    __syncthreads();
+    if (tid < E)
+      for (int g = 0; g < G; ++g) {
+        cnt += red[0][g * E + tid];
+        before += red[1][g * E + tid];
+      }
+    if (bx == 0 && tid < E) a.counts[tid] = cnt;
+  } else {
+    if (tid < E) {
+      cnt = a.counts[tid];
+      before = a.block_hist[static_cast<int64_t>(bx) * E + tid];
+    }
+  }
   // expert offsets = exclusive prefix of the counts (every workgroup derives
-  // them; the first one also writes them out)
-  const int cnt = tid < E ? a.counts[tid] : 0;
+  // them; the first one also writes them out, and the tile prefix)
   const int all = block_exclusive_scan(cnt, buf);
-  if (blockIdx.x == 0) {
+  if (bx == 0) {
     if (tid < E) a.offsets[tid] = buf[tid];
     if (tid == 0) a.offsets[E] = all;
   }
-  if (tid < E) base[tid] = buf[tid] + a.block_hist[static_cast<int64_t>(blockIdx.x) * E + tid];
+  if (tid < E) base[tid] = buf[tid] + before;
   for (int i = tid; i < 4 * kMaxE; i += 256) (&wc[0][0])[i] = 0;
+  if (bx == 0 && a.tile_prefix) {
+    // m-tiles of tile_bm rows per expert, exclusive prefix over experts
+    const int mt = tid < E ? (cnt + a.tile_bm - 1) / a.tile_bm : 0;
+    const int tiles = block_exclusive_scan(mt, red[0]);
+    if (tid < E) a.tile_prefix[tid] = red[0][tid];
+    if (tid == 0) a.tile_prefix[E] = tiles;
+  }
   __syncthreads();
 
   const int64_t f0 = static_cast<int64_t>(blockIdx.x) * CH;
@@ -128,29 +186,36 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a) {
   }
 }
 
-// x_perm[r] = x[perm[r] / k]: one workgroup per row, thread i copying the
-// 16-byte chunks i, i + 256, ... (the source row index is workgroup-uniform,
-// read once; no per-chunk division).
+// x_perm[inv[t*k + j]] = x[t] for j < k: one workgroup per token.  Each
+// thread loads up to four of the row's 16-byte chunks (i, i + 256, ...) into
+// registers and stores each of them k times, so x is read once in all (the
+// loads are nontemporal: nothing here reads a row twice) and every row of
+// x_perm is written once, by whole 4 KB lines per store instruction.  A
+// destination outside [0, M) (a malformed inv) is skipped.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
-                                                          const int32_t* __restrict__ perm,
-                                                          int64_t T, int chunks, int k,
+                                                          const int32_t* __restrict__ inv,
+                                                          int64_t M, int chunks, int k,
                                                           uint4* __restrict__ xp) {
-  const int64_t r = blockIdx.x;
-  int64_t src = perm[r] / k;
-  src = src < 0 ? 0 : (src >= T ? T - 1 : src);   // malformed perm stays in bounds
-  const uint4* in = x + src * chunks;
-  uint4* o = xp + r * chunks;
-  // x_perm is written once and read later by another kernel: nontemporal
-  // stores keep it from evicting the rows of x, which k slots re-read
-  typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-  u32x4_nt* on = reinterpret_cast<u32x4_nt*>(o);
-  int c = threadIdx.x;
-  for (; c + 256 < chunks; c += 512) {
-    const uint4 a = in[c], b = in[c + 256];
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, a), on + c);
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, b), on + c + 256);
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t t = blockIdx.x;
+  const u32x4* in = reinterpret_cast<const u32x4*>(x) + t * chunks;
+  u32x4* out = reinterpret_cast<u32x4*>(xp);
+  const int32_t* dst = inv + t * k;
+  for (int c0 = 0; c0 < chunks; c0 += 4 * 256) {
+    const int c = c0 + static_cast<int>(threadIdx.x);
+    u32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (c + q * 256 < chunks) v[q] = __builtin_nontemporal_load(in + c + q * 256);
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = dst[j];
+      if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(M)) continue;
+      u32x4* o = out + r * chunks;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c + q * 256 < chunks) __builtin_nontemporal_store(v[q], o + c + q * 256);
+    }
   }
-  if (c < chunks) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, in[c]), on + c);
 }
 
 __global__ void dense_offsets_kernel(int32_t* offsets, int64_t M) {
@@ -214,19 +279,24 @@ size_t permute_scratch_bytes(int64_t M, int E) {
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.tile_prefix && a.tile_bm < 1) return hipErrorInvalidValue;
   const int nb = static_cast<int>((a.M + CH - 1) / CH);
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(a.E), dim3(256), 0, s, a, nb);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, a);
+  if (static_cast<int64_t>(nb) * a.E <= kPermInlineScan) {
+    hipLaunchKernelGGL(perm_scatter_kernel<true>, dim3(nb), dim3(256), 0, s, a, nb);
+  } else {
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(a.E), dim3(256), 0, s, a, nb);
+    hipLaunchKernelGGL(perm_scatter_kernel<false>, dim3(nb), dim3(256), 0, s, a, nb);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void* x, const int32_t* perm, int64_t M, int H, int k,
+hipError_t launch_gather_rows(const void* x, const int32_t* inv, int64_t T, int H, int k,
                               int elem_bytes, void* x_perm, hipStream_t s) {
-  if (M > 0x7fffffff || k < 1) return hipErrorInvalidValue;
+  if (T > 0x7fffffff || k < 1) return hipErrorInvalidValue;
   const int chunks = H * elem_bytes / 16;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), perm, M / k, chunks, k, static_cast<uint4*>(x_perm));
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), inv, T * k, chunks, k, static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = B.lib()
-    assert L.moe_version() == 105
+    assert L.moe_version() == 106
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -179,7 +179,7 @@ def test_rounded_layout_and_argument_errors():
     assert L.moe_forward_rounded(*args(T=0, x=None, out=None, ws=None, wsb=0)) == B.MOE_OK
     assert L.moe_forward_rounded_profiled(*args()[:-1], None, 0, None) == B.MOE_ERR_INVALID_ARG
     ev = (ctypes.c_void_p * 8)(*([FAKE] * 8))
-    assert L.moe_forward_rounded_profiled(*args()[:-1], ev, 7, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_rounded_profiled(*args()[:-1], ev, B.PROFILE_EVENTS_ROUNDED - 1, None) == B.MOE_ERR_INVALID_ARG
     lay = B.ForwardLayout()
     assert L.moe_forward_rounded_layout(8, 64, 100, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_forward_rounded_layout(8, 64, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
@@ -216,7 +216,7 @@ def test_mxfp8_layout_and_argument_errors():
     assert L.moe_forward_mxfp8(*args(T=0, x=None, out=None, ws=None, wsb=0)) == B.MOE_OK
     assert L.moe_forward_mxfp8_profiled(*args()[:-1], None, 0, None) == B.MOE_ERR_INVALID_ARG
     ev = (ctypes.c_void_p * 8)(*([FAKE] * 8))
-    assert L.moe_forward_mxfp8_profiled(*args()[:-1], ev, 7, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_mxfp8_profiled(*args()[:-1], ev, B.PROFILE_EVENTS_MXFP8 - 1, None) == B.MOE_ERR_INVALID_ARG
     lay = B.Mxfp8Layout()
     assert L.moe_forward_mxfp8_layout(8, 128, 100, 4, 2, 1, ctypes.byref(lay)) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_forward_mxfp8_layout(8, 128, 128, 4, 2, 1, None) == B.MOE_ERR_INVALID_ARG
@@ -263,7 +263,8 @@ def test_backward_layout_and_argument_errors():
         ("ws", FAKE), ("wsb", 1 << 30), ("ev", None), ("nev", 0), ("s", None))]
     assert L.moe_forward_train(*targs(dt=0)) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_forward_train(*targs(gu=None)) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_forward_train(*targs(ev=(ctypes.c_void_p * 7)(*([FAKE] * 7)), nev=6)) == B.MOE_ERR_INVALID_ARG
+    nev = B.PROFILE_EVENTS
+    assert L.moe_forward_train(*targs(ev=(ctypes.c_void_p * nev)(*([FAKE] * nev)), nev=nev - 1)) == B.MOE_ERR_INVALID_ARG
     assert L.moe_forward_train(*targs(wsb=64)) == B.MOE_ERR_WORKSPACE
     assert L.moe_backward(*args(wsb=1024)) == B.MOE_ERR_WORKSPACE
     assert L.moe_backward(*args(T=0, x=None, dout=None, dx=None, fws=None, fwsb=0, ws=None,

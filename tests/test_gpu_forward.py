@@ -56,6 +56,10 @@ SMALL = {
     "k3_bf16": ("fine_bf16", dict(T=301, H=256, I=192, E=16, k=3)),
     "k6_bf16": ("fine_bf16", dict(T=150, H=256, I=128, E=12, k=6, renormalize=False)),
     "k7_bf16": ("vfine_bf16", dict(T=129, H=128, I=256, E=32, k=7)),
+    # 313 permutation chunks x 128 experts: histograms too many for each chunk
+    # to sum itself, so the permutation takes its separate scan pass (and
+    # still writes the GEMM's tile prefix)
+    "many_chunks": ("fine_bf16", dict(T=40000, H=128, I=128)),
 }
 
 

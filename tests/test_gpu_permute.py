@@ -38,7 +38,9 @@ def _check(ids, E, x=None, dt="bf16"):
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 2), (100, 8, 2), (513, 8, 2), (1000, 64, 4),
                                    (777, 128, 8), (300, 256, 8), (4096, 1, 1), (2048, 5, 5),
-                                   (1025, 256, 1)])
+                                   (1025, 256, 1),
+                                   # 293 chunks x 128 experts: the separate scan pass
+                                   (37500, 128, 8)])
 def test_permute_parity(T, E, k):
     log(f"permute T={T} E={E} k={k}")
     _check(_random_ids(T, E, k, seed=T * 7 + E), E)
