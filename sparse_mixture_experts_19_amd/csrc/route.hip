@@ -54,7 +54,7 @@ __device__ __forceinline__ float route_delta(float xsq, float wsq_max, float bma
 // whose fp32 logits (without bias) sit in lg[256 / LPT][EP + 1].  LPT lanes
 // per token, each holding EP / LPT logits (experts sub + LPT i).
 template <int EP, int LPT>
-__device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1],
+__device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1],
                              const float* delta) {
   constexpr int PER = EP / LPT;
   const int tid = threadIdx.x;
@@ -78,6 +78,7 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
   uint32_t taken = 0;
   float sel_v[kMaxK];
   int sel_e[kMaxK];
+  float vk = 0.f;        // the k-th largest logit (kept without a runtime index)
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
@@ -97,6 +98,7 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
       }
       sel_v[j] = bv;
       sel_e[j] = be;
+      if (j == k - 1) vk = bv;
       if ((be % LPT) == sub) taken |= 1u << (be / LPT);
     }
   }
@@ -109,7 +111,6 @@ __device__ void route_select(const RouteArgs& a, int64_t t0, float (*lg)[EP + 1]
   s = group_sum(s);
 
   const float band = 2.f * delta[tok] * kSafety;
-  const float vk = sel_v[k - 1];
   float cnt = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
