@@ -272,7 +272,7 @@ PROFILE_STAGES = ("route", "permute", "gemm_gate_up_swiglu", "gemm_down", "combi
 
 def moe_forward_profiled(x, w_router, router_bias, w13, w2, k: int, renormalize: bool, out,
                          workspace, events):
-    """moe_forward recording ``events`` (7 torch.cuda.Event, timing enabled) on the
+    """moe_forward recording ``events`` (PROFILE_EVENTS torch.cuda.Event, timing enabled) on the
     current stream before each stage and after the last; see PROFILE_STAGES."""
     T, H = x.shape
     E, I2, _ = w13.shape
