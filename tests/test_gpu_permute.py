@@ -68,6 +68,15 @@ def test_permute_with_gather(dt):
     _check(_random_ids(T, E, k, seed=12), E, x=inp.x, dt=dt)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_permute_with_gather_widest_rows(dt):
+    # H = 16384: 2048 (bf16) or 4096 (fp32) 16-byte chunks per row, several
+    # passes of the gather's four-chunks-per-thread loop
+    T, H, E, k = 96, 16384, 8, 3
+    inp = W.random_small(T, H, E, k, 64, dt, seed=21)
+    _check(_random_ids(T, E, k, seed=22), E, x=inp.x, dt=dt)
+
+
 def test_permute_full_size_shapes():
     for name in ("fine_bf16", "skewed_bf16"):
         wl = W.WORKLOADS[name]
