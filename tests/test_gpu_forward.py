@@ -60,6 +60,11 @@ SMALL = {
     # to sum itself, so the permutation takes its separate scan pass (and
     # still writes the GEMM's tile prefix)
     "many_chunks": ("fine_bf16", dict(T=40000, H=128, I=128)),
+    # the largest hidden and intermediate sizes the library accepts: 256
+    # K stages in the gate/up GEMM; 512 gate/up n-tiles and 1024 K stages
+    # (cut into K pieces) in the down GEMM
+    "h_max": ("coarse_bf16", dict(T=65, H=16384, I=128, E=4, k=2)),
+    "i_max": ("coarse_bf16", dict(T=70, H=64, I=65536, E=4, k=2)),
 }
 
 
