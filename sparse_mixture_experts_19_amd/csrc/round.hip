@@ -100,11 +100,11 @@ __device__ __forceinline__ int id_byte(uint64_t w, int j) {
 __device__ __forceinline__ int take_slot(uint32_t m, uint64_t w, uint64_t ob, uint64_t kbytes) {
   const uint64_t x = w ^ ob;
   const uint64_t z = (x - 0x0101010101010101ull) & ~x & kbytes;
-  const uint32_t zlo = static_cast<uint32_t>(z), zhi = static_cast<uint32_t>(z >> 32);
-  const int pos = (zlo ? __builtin_ctz(zlo) : 32 + __builtin_ctz(zhi | 0x80000000u)) >> 3;
+  // bit 63 keeps the count defined for z == 0 (that result is not used)
+  const int pos = __builtin_ctzll(z | (1ull << 63)) >> 3;
   const int held = ((m >> pos) & 1u) ? pos : -1;
-  const int firstp = m ? __builtin_ctz(m) : -1;
-  return z ? held : firstp;
+  const int firstp = __builtin_ctz(m | 0x100u);      // 8: no pooled slot
+  return z ? held : (firstp < 8 ? firstp : -1);
 }
 
 constexpr int kRoundMaxTiles = kMaxE;        // tiles per round: ceil(pooled / B) <= E
@@ -228,8 +228,10 @@ __device__ void round_tile(SID* sid, SMASK* smask, int Q, int i, RoundShared& sh
     need -= took;
     got += took;
     front = front && __ballot(ma != 0) == 0;
-    if (front && lane == 0) atomicMax(&sh.first, b + 1);
     lds_release(&sh.prog[i], b + 1);
+    // a hint only (later tiles start there; an older value makes them walk
+    // exhausted blocks), so it leaves the hand-over path
+    if (front && lane == 0) atomicMax(&sh.first, b + 1);
   }
   if (lane == 0) sh.got[i] = got;
   lds_release(&sh.prog[i], INT_MAX);
