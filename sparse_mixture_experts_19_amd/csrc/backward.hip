@@ -162,29 +162,69 @@ __global__ __launch_bounds__(256) void bwd_dxr_kernel(const float* __restrict__ 
 }
 
 // dW_r partial sums over token slices: part[s,e,h] = sum_{t in slice s}
-// dl[t,e] x[t,h]; 16 experts x 256 columns per block.
-constexpr int kDwrExp = 16;
+// dl[t,e] x[t,h], tokens in order; NE experts x 1024 columns per block, a
+// thread owning 4 consecutive columns (one 8-byte load of x per token, the
+// loads of 16 tokens issued before their sums).  The block's dl values come
+// through LDS, 256 tokens at a time (one cooperative load instead of a
+// round trip per token).
+constexpr int kDwrExp = 16;      // experts per block (8 when E <= 8)
+constexpr int kDwrCols = 4;
+constexpr int kDwrChunk = 256;
+constexpr int kDwrBatch = 16;    // tokens whose x loads are in flight together
+template <int NE>
 __global__ __launch_bounds__(256) void bwd_dwr_partial_kernel(const float* __restrict__ dl,
                                                               const uint16_t* __restrict__ x,
                                                               int64_t T, int H, int E, int64_t slice,
                                                               float* __restrict__ part) {
-  const int h = blockIdx.y * 256 + threadIdx.x;
-  const int e0 = blockIdx.x * kDwrExp;
+  __shared__ float sdl[kDwrChunk * NE];
+  const int tid = threadIdx.x;
+  const int h = (blockIdx.y * 256 + tid) * kDwrCols;
+  const bool live = h < H;
+  const int e0 = blockIdx.x * NE;
   const int s = blockIdx.z;
   const int64_t ta = s * slice, tb = ta + slice < T ? ta + slice : T;
-  if (h >= H) return;
-  float acc[kDwrExp];
+  float acc[NE][kDwrCols];
 #pragma unroll
-  for (int i = 0; i < kDwrExp; ++i) acc[i] = 0.f;
-  for (int64_t t = ta; t < tb; ++t) {
-    const float xv = bf16_to_f32(x[t * H + h]);
+  for (int i = 0; i < NE; ++i)
 #pragma unroll
-    for (int i = 0; i < kDwrExp; ++i)
-      if (e0 + i < E) acc[i] += dl[t * E + e0 + i] * xv;
+    for (int c = 0; c < kDwrCols; ++c) acc[i][c] = 0.f;
+  const uint16_t* xc = x + (live ? h : 0);
+  auto add = [&](const float* d, uint2 xr) {
+    const float xv[kDwrCols] = {bf16_to_f32(static_cast<uint16_t>(xr.x)), bf16_to_f32(static_cast<uint16_t>(xr.x >> 16)),
+                                bf16_to_f32(static_cast<uint16_t>(xr.y)), bf16_to_f32(static_cast<uint16_t>(xr.y >> 16))};
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+#pragma unroll
+      for (int c = 0; c < kDwrCols; ++c) acc[i][c] += d[i] * xv[c];
+  };
+  for (int64_t c0 = ta; c0 < tb; c0 += kDwrChunk) {
+    const int n = static_cast<int>(tb - c0 < kDwrChunk ? tb - c0 : kDwrChunk);
+    __syncthreads();                       // the previous chunk's dl is no longer read
+    for (int idx = tid; idx < n * NE; idx += 256) {
+      const int tt = idx / NE, i = idx % NE;
+      sdl[idx] = e0 + i < E ? dl[(c0 + tt) * E + e0 + i] : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+      int u0 = 0;
+      for (; u0 + kDwrBatch <= n; u0 += kDwrBatch) {
+        uint2 xr[kDwrBatch];
+#pragma unroll
+        for (int u = 0; u < kDwrBatch; ++u) xr[u] = *reinterpret_cast<const uint2*>(xc + (c0 + u0 + u) * H);
+#pragma unroll
+        for (int u = 0; u < kDwrBatch; ++u) add(sdl + (u0 + u) * NE, xr[u]);
+      }
+      for (; u0 < n; ++u0) add(sdl + u0 * NE, *reinterpret_cast<const uint2*>(xc + (c0 + u0) * H));
+    }
   }
+  if (!live) return;
 #pragma unroll
-  for (int i = 0; i < kDwrExp; ++i)
-    if (e0 + i < E) part[(static_cast<int64_t>(s) * E + e0 + i) * H + h] = acc[i];
+  for (int i = 0; i < NE; ++i)
+    if (e0 + i < E) {
+      float4 v;
+      v.x = acc[i][0]; v.y = acc[i][1]; v.z = acc[i][2]; v.w = acc[i][3];
+      *reinterpret_cast<float4*>(part + (static_cast<int64_t>(s) * E + e0 + i) * H + h) = v;
+    }
 }
 
 // dW_r = sum over slices in slice order
@@ -368,8 +408,12 @@ hipError_t launch_bwd_router_grads(const float* dl, const void* x, const void* w
   if (e != hipSuccess) return e;
   const int S = bwd_dwr_slices(T);
   const int64_t slice = (T + S - 1) / S;
-  hipLaunchKernelGGL(bwd_dwr_partial_kernel, dim3(blocks(E, kDwrExp), blocks(H, 256), S), dim3(256),
-                     0, s, dl, static_cast<const uint16_t*>(x), T, H, E, slice, part);
+  if (E <= 8)
+    hipLaunchKernelGGL(bwd_dwr_partial_kernel<8>, dim3(1, blocks(H / kDwrCols, 256), S), dim3(256), 0, s,
+                       dl, static_cast<const uint16_t*>(x), T, H, E, slice, part);
+  else
+    hipLaunchKernelGGL(bwd_dwr_partial_kernel<kDwrExp>, dim3(blocks(E, kDwrExp), blocks(H / kDwrCols, 256), S),
+                       dim3(256), 0, s, dl, static_cast<const uint16_t*>(x), T, H, E, slice, part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n = static_cast<int64_t>(E) * H;
   hipLaunchKernelGGL(bwd_dwr_reduce_kernel, dim3(blocks(n, 256)), dim3(256), 0, s, part, S, n, dwr);
