@@ -214,8 +214,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(every box has one MI355X; see the sharding notes in the design document)",
+        print(f"bench.py: the benchmark measures one GPU; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,6 +1,6 @@
 """CPU oracle of the sparse top-k MoE FFN forward (test infrastructure).
 
-This is the plain, slow, obviously-correct reference the HIP path is judged
+This is the plain, slow, obviously-correct reference the HIP path is checked
 against.  It is *test infrastructure*: only ``tests/``, the smoke check in
 ``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import or
 run it.  The product library never calls it and shares no code with it.
