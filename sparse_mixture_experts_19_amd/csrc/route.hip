@@ -503,8 +503,12 @@ __device__ __forceinline__ float fused_delta(float xsq, float wsq_max, float bma
 }
 
 template <int BT, int EPW, int WE, int WK, int PF>
-__global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
-  static_assert(WE * WK == 4 && BT % 16 == 0 && EPW % 16 == 0 && 256 % BT == 0, "shape");
+__global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArgs a) {
+  // NW waves: 4, or 8 when they split the experts (more loads in flight per
+  // CU for a workgroup that streams a large router matrix)
+  constexpr int NW = WE * WK, NTH = 64 * NW;
+  static_assert((NW == 4 || (NW == 8 && WK == 1)) && BT % 16 == 0 && EPW % 16 == 0 && 256 % BT == 0,
+                "shape");
   constexpr int NT = BT / 16, NJ = EPW / 16, EP = EPW * WE;
   constexpr int LPT = 256 / BT;                 // select: lanes per token
   constexpr int PER = EP / LPT;                 // select: logits per lane
@@ -516,9 +520,9 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
   __shared__ int flagged[BT];
   __shared__ int nflag;
   __shared__ unsigned wmax_bits, bmax_bits;
-  __shared__ float cv[4][kMaxE];                // re-rank: candidate fp32 logits (per wave)
-  __shared__ int ce[4][kMaxE];                  //          candidate expert ids
-  __shared__ double cd[4][kMaxE];               //          logits used for the final ranking
+  __shared__ float cv[NW][kMaxE];               // re-rank: candidate fp32 logits (per wave)
+  __shared__ int ce[NW][kMaxE];                 //          candidate expert ids
+  __shared__ double cd[NW][kMaxE];              //          logits used for the final ranking
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -595,13 +599,14 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
 
   if constexpr (WK == 1) {
     // The four waves share x through LDS.  An iteration covers PF = 4 steps
-    // (256 bytes of each row): every wave loads BT / 4 rows of the next
+    // (256 bytes of each row): every wave loads BT / NW rows of the next
     // iteration (16 lanes per row), writes them to one of two LDS buffers
     // (16-byte chunk c of row r in slot c ^ (r % 16): conflict-free both for
     // the row-wise writes and for the MFMA reads of 16 rows at one chunk),
     // and the waves meet at one barrier per iteration.
     static_assert(PF == 4, "one iteration is 256 bytes of a row");
-    constexpr int XR = BT / 16;                   // 64-lane loads per wave per iteration
+    static_assert(BT % (4 * NW) == 0, "whole rows per wave");
+    constexpr int XR = BT / (4 * NW);             // 64-lane loads per wave per iteration
     __shared__ uint4 xs[2][BT * 16];
     const int xchk = lane & 15;
     const char* xq[XR];
@@ -763,7 +768,7 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
 
   // ---- totals (wave sums in K order), norm maxima
   if constexpr (WK > 1) {
-    for (int c = tid; c < BT * EP; c += 256) {
+    for (int c = tid; c < BT * EP; c += NTH) {
       const int tk = c / EP, e = c - tk * EP;
       float v = lg[0][tk][e];
 #pragma unroll
@@ -780,8 +785,9 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // ---- softmax, top-k, exactness check: LPT lanes per token
-  {
+  // ---- softmax, top-k, exactness check: LPT lanes per token (the first
+  // 256 threads; whole waves)
+  if (tid < 256) {
     const int tok = tid / LPT, sub = tid % LPT;
     const int64_t t = t0 + tok;
     float x2 = 0.f;
@@ -881,7 +887,7 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(RouteArgs a) {
 
   // ---- float64 re-rank of the flagged tokens, one wave per token
   const int nf = nflag;
-  for (int f = wave; f < nf; f += 4) {
+  for (int f = wave; f < nf; f += NW) {
     const int tok = flagged[f];
     rerank_token<uint16_t>(a, t0 + tok, &lg[0][tok][0], fmeta[tok], cv[wave], ce[wave], cd[wave]);
   }
@@ -894,7 +900,7 @@ hipError_t launch_fused(const RouteArgs& a, hipStream_t s) {
   constexpr int L = BT / 16 + EPW / 16;
   constexpr int PF = WK == 1 ? 4 : (24 / L > 8 ? 8 : (24 / L < 3 ? 3 : 24 / L));
   const unsigned grid = static_cast<unsigned>((a.T + BT - 1) / BT);
-  hipLaunchKernelGGL((route_fused_bf16_kernel<BT, EPW, WE, WK, PF>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((route_fused_bf16_kernel<BT, EPW, WE, WK, PF>), dim3(grid), dim3(64 * WE * WK), 0, s, a);
   return hipGetLastError();
 }
 
@@ -934,7 +940,11 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
       if (T >= 512 * 64) return launch_fused<64, 32, 4, 1>(a, s);
       return launch_fused<32, 32, 4, 1>(a, s);
     }
-    if (T >= 256 * 32) return launch_fused<32, 64, 4, 1>(a, s);
+    // beyond 128 experts the workgroup streams 2 MB of router rows per 32
+    // tokens: eight waves (32 experts each) keep twice the loads in flight
+    // (measured on the very fine workload: 0.134 -> 0.118-0.121 ms; with 128
+    // experts the eight-wave form was slower, 0.071 -> 0.094 ms)
+    if (T >= 256 * 32) return launch_fused<32, 32, 8, 1>(a, s);
     return launch_fused<16, 64, 4, 1>(a, s);
   }
   hipError_t err;
