@@ -426,6 +426,9 @@ def main():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
         pass
+    roof["algorithmic_bytes"] = int(a["bytes"])
+    roof["traffic_over_algorithmic"] = (round(roof["traffic"] / a["bytes"], 3)
+                                        if roof["traffic"] and a["bytes"] else None)
 
     rec = {
         "metric": METRIC,
