@@ -420,8 +420,11 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(rec_key := wl.name + ("+mxfp8" if MX else "") +
-                      ((("+train" if CACHE else "+train_recompute")) if TR else ""), {}).get(dom)
+        # keyed by the workload string of the record's config (shared expert,
+        # rounding, MXFP8 and training variants have their own entries)
+        rec = tr.get(wl.name + (f"+shared{Is}" if Is else "") + (f"+round{RB}" if RB else "") +
+                     ("+mxfp8" if MX else "") +
+                     (("+train" if CACHE else "+train_recompute") if TR else ""), {}).get(dom)
         if rec and rec.get("source_sha256") == gemm_source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
