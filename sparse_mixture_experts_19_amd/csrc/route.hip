@@ -438,9 +438,13 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
 //
 // Summation (the structure the error bound counts): every MFMA starts from
 // zero (a chain of at most 32 roundings), the results of PF consecutive steps
-// are added into a group sum, group sums into the wave's sum, the WK wave
-// sums in K order, then the bias:
+// form a group sum (the first assigned, the others added), group sums are
+// added into the wave's sum, the WK wave sums in K order, then the bias:
 //   D = 32 + PF + ceil(n / PF) + WK + 1,  n = K32 steps per wave.
+// The squared norms of the router rows, which the bound needs, come from one
+// more MFMA per step on the matrix cores (the row block times itself,
+// accumulated over the steps; the diagonal holds them), so the vector ALU
+// only adds the MFMA results.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -493,11 +497,16 @@ __device__ __forceinline__ float group_add(float v) {
   else return v;
 }
 
-// delta of the fused kernel.  The norms are fp32 sums of exact squares, each
-// within a relative (number of terms) * 2^-24 <= 2^-10 of its value (H <=
-// 16384); kSafety^3 covers both norms, their square roots and the product.
+// delta of the fused kernel.  The norms are fp32 sums of exact squares
+// (token norms by v_dot2, router-row norms by MFMA accumulation), at most H
+// non-negative terms added in some order, each addition within 2^-23 of its
+// result even if the adder truncates: a computed norm is at least
+// (1 - H * 2^-23) >= (1 - 2^-9) of the exact one (H <= 16384).  The product of
+// the two square roots is then at least (1 - 2^-8 - 2^-20) of the exact
+// product, which kNormSafety (with the roundings of the products) covers.
+constexpr float kNormSafety = 1.0078125f;   // 1 + 2^-7
 __device__ __forceinline__ float fused_delta(float xsq, float wsq_max, float bmax, int depth) {
-  const float S = sqrtf(xsq) * sqrtf(wsq_max) * kSafety * kSafety * kSafety + bmax;
+  const float S = sqrtf(xsq) * sqrtf(wsq_max) * kNormSafety + bmax;
   const float d = static_cast<float>(depth) * kUlp2;
   return d * (1.f + d) * S * kSafety;
 }
@@ -575,46 +584,52 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) { acc[i][j] = zero4; grp[i][j] = zero4; }
-  float wsq[NJ];
+  // router-row norms: W times itself on the matrix cores, accumulated over
+  // all steps; the diagonal holds the squared norms
+  f32x4_t wsqm[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) wsq[j] = 0.f;
+  for (int j = 0; j < NJ; ++j) wsqm[j] = zero4;
+  // a group's first step assigns its MFMA results, later steps add them
   auto close_group = [&]() {
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) { acc[i][j] += grp[i][j]; grp[i][j] = zero4; }
+      for (int j = 0; j < NJ; ++j) acc[i][j] += grp[i][j];
   };
-  auto mfmas = [&](const bf16x8_t* xf, const bf16x8_t* wr) {
+  auto mfmas = [&](const bf16x8_t* xf, const bf16x8_t* wr, bool first) {
     bf16x8_t wf[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) wf[j] = to_mfma(wr[j]);
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        grp[i][j] += __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], wf[j], zero4, 0, 0, 0);
+      for (int j = 0; j < NJ; ++j) {
+        const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[i], wf[j], zero4, 0, 0, 0);
+        grp[i][j] = first ? p : grp[i][j] + p;
+      }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) wsq[j] = sumsq8_dot(wr[j], wsq[j]);
+    for (int j = 0; j < NJ; ++j) wsqm[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], wf[j], wsqm[j], 0, 0, 0);
   };
 
   if constexpr (WK == 1) {
-    // The four waves share x through LDS.  An iteration covers PF = 4 steps
-    // (256 bytes of each row): every wave loads BT / NW rows of the next
-    // iteration (16 lanes per row), writes them to one of two LDS buffers
-    // (16-byte chunk c of row r in slot c ^ (r % 16): conflict-free both for
-    // the row-wise writes and for the MFMA reads of 16 rows at one chunk),
-    // and the waves meet at one barrier per iteration.
-    static_assert(PF == 4, "one iteration is 256 bytes of a row");
-    static_assert(BT % (4 * NW) == 0, "whole rows per wave");
-    constexpr int XR = BT / (4 * NW);             // 64-lane loads per wave per iteration
-    __shared__ uint4 xs[2][BT * 16];
-    const int xchk = lane & 15;
+    // The waves share x through LDS.  An iteration covers PF steps (64·PF
+    // bytes of each row): every wave loads BT / NW rows of the next iteration
+    // (4·PF lanes per row), writes them to one of two LDS buffers (16-byte
+    // chunk c of row r in slot c ^ (r % 16): conflict-free both for the
+    // row-wise writes and for the MFMA reads of 16 rows at one chunk), and the
+    // waves meet at one barrier per iteration.
+    constexpr int CPR = 4 * PF;                   // 16-byte chunks of a row per iteration
+    constexpr int RPI = 64 / CPR;                 // rows per 64-lane load
+    static_assert((PF == 4 || PF == 8) && BT % (RPI * NW) == 0, "whole rows per wave");
+    constexpr int XR = BT / (RPI * NW);           // 64-lane loads per wave per iteration
+    __shared__ uint4 xs[2][BT * CPR];
+    const int xchk = lane % CPR;
     const char* xq[XR];
     int xrow[XR];
     float xsq[XR];
 #pragma unroll
     for (int q = 0; q < XR; ++q) {
-      xrow[q] = 4 * (wave * XR + q) + (lane >> 4);
+      xrow[q] = RPI * (wave * XR + q) + lane / CPR;
       int64_t t = t0 + xrow[q];
       t = t < T ? t : T - 1;
       xq[q] = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.x) + t * H) + (xchk & 3) * 16;
@@ -622,14 +637,14 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
     }
     uint4 xr[XR];
     auto xload = [&](int it) {
-      const int s = clamp_step(4 * it + (xchk >> 2));
+      const int s = clamp_step(PF * it + (xchk >> 2));
 #pragma unroll
       for (int q = 0; q < XR; ++q) xr[q] = *reinterpret_cast<const uint4*>(xq[q] + s * 64);
     };
     auto xstore = [&](int buf) {
 #pragma unroll
       for (int q = 0; q < XR; ++q) {
-        xs[buf][xrow[q] * 16 + (xchk ^ (xrow[q] & 15))] = xr[q];
+        xs[buf][xrow[q] * CPR + (xchk ^ (xrow[q] & 15))] = xr[q];
         // token norms, one wave per row; a last partial iteration re-reads
         // its last step, which only enlarges the norm (the bound stays valid)
         xsq[q] = sumsq8_dot(__builtin_bit_cast(bf16x8_t, xr[q]), xsq[q]);
@@ -638,7 +653,7 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
     auto xfrags = [&](int buf, int u, bf16x8_t* xf) {
 #pragma unroll
       for (int i = 0; i < NT; ++i)
-        xf[i] = __builtin_bit_cast(bf16x8_t, xs[buf][(16 * i + r16) * 16 + ((4 * u + g4) ^ r16)]);
+        xf[i] = __builtin_bit_cast(bf16x8_t, xs[buf][(16 * i + r16) * CPR + ((4 * u + g4) ^ r16)]);
     };
     // prologue: x of iteration 0 in LDS, x of iteration 1 and W of iteration 0 in flight
     xload(0);
@@ -659,7 +674,7 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       for (int u = 0; u < PF; ++u) {
         bf16x8_t xf[NT];
         xfrags(buf, u, xf);
-        mfmas(xf, wb[u]);
+        mfmas(xf, wb[u], u == 0);
         wload((it + 1) * PF + u, wb[u]);
         if (u == 0) {
           xstore(buf ^ 1);                        // x of iteration it + 1
@@ -671,15 +686,17 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       lds_barrier();
     }
     const int rem = n - nfull * PF;
+    if (rem > 0) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      if (u < rem) {
-        bf16x8_t xf[NT];
-        xfrags(nfull & 1, u, xf);
-        mfmas(xf, wb[u]);
+      for (int u = 0; u < PF; ++u) {
+        if (u < rem) {
+          bf16x8_t xf[NT];
+          xfrags(nfull & 1, u, xf);
+          mfmas(xf, wb[u], u == 0);
+        }
       }
+      close_group();
     }
-    close_group();
     // norms of the rows this wave loaded: the 16 lanes of a row hold its chunks
 #pragma unroll
     for (int q = 0; q < XR; ++q) {
@@ -712,7 +729,7 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       bf16x8_t xf[NT];
 #pragma unroll
       for (int i = 0; i < NT; ++i) xf[i] = to_mfma(xb[u][i]);
-      mfmas(xf, wb[u]);
+      mfmas(xf, wb[u], u == 0);
 #pragma unroll
       for (int i = 0; i < NT; ++i) xsq[i] = sumsq8_dot(xb[u][i], xsq[i]);
     };
@@ -738,10 +755,12 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       close_group();
     }
     const int rem = n - nfull * PF;
+    if (rem > 0) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (u < rem) step(u);
-    close_group();
+      for (int u = 0; u < PF; ++u)
+        if (u < rem) step(u);
+      close_group();
+    }
     // norms: the four lanes 4r .. 4r+3 of a quad hold the four chunks of row r
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -758,11 +777,9 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) lg[kq][16 * i + 4 * g4 + v][eg * EPW + 16 * j + r16] = acc[i][j][v];
+  if ((r16 >> 2) == g4) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    float v = wsq[j] + xor_lane<1>(wsq[j]);
-    v += xor_lane<2>(v);
-    if (lchk == 0) wsq_s[kq][eg * EPW + 16 * j + lrow] = v;
+    for (int j = 0; j < NJ; ++j) wsq_s[kq][eg * EPW + 16 * j + r16] = wsqm[j][r16 & 3];
   }
   __syncthreads();
 
@@ -895,10 +912,14 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
 
 template <int BT, int EPW, int WE, int WK>
 hipError_t launch_fused(const RouteArgs& a, hipStream_t s) {
-  // shared x: iterations of 4 steps; K ranges: about 24 16-byte loads per
-  // lane in flight (96 registers)
+  // shared x: iterations of 8 steps where the x buffers leave room (half the
+  // barriers of 4-step iterations: fine 62 -> 57.5 us, very fine 95 -> 86 us;
+  // with 16 experts per wave the larger x buffers halve the workgroups per CU
+  // and 8 steps were slower, 52 -> 80 us on the skewed workload, and 128
+  // tokens do not fit); K ranges: about 24 16-byte loads per lane in flight
+  // (96 registers)
   constexpr int L = BT / 16 + EPW / 16;
-  constexpr int PF = WK == 1 ? 4 : (24 / L > 8 ? 8 : (24 / L < 3 ? 3 : 24 / L));
+  constexpr int PF = WK == 1 ? (EPW >= 32 && BT <= 64 ? 8 : 4) : (24 / L > 8 ? 8 : (24 / L < 3 ? 3 : 24 / L));
   const unsigned grid = static_cast<unsigned>((a.T + BT - 1) / BT);
   hipLaunchKernelGGL((route_fused_bf16_kernel<BT, EPW, WE, WK, PF>), dim3(grid), dim3(64 * WE * WK), 0, s, a);
   return hipGetLastError();
