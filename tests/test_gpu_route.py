@@ -43,6 +43,12 @@ CASES = [
     (16384 + 3, 64, 128, 8, "bf16", True, "zero"),
     (8192 + 33, 64, 256, 8, "bf16", False, "zero"),
     (8192 + 31, 128, 200, 6, "bf16", False, "zipf1.2"),
+    # the layouts with 32 or 64 experts per wave walk K in iterations of 8
+    # steps of 32: whole iterations plus a remainder of 2 or 6 steps, the
+    # remainder in either LDS buffer
+    (1000, 320, 128, 8, "bf16", True, "zero"),
+    (8192 + 8, 704, 256, 8, "bf16", False, "zero"),
+    (40, 448, 160, 4, "bf16", False, "zipf1.2"),
     (100, 64, 8, 2, "f32", False, "zero"),
     (257, 256, 64, 4, "f32", True, "zero"),
     (65, 128, 256, 8, "f32", False, "zipf1.2"),
