@@ -428,13 +428,15 @@ __global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
 // and weights leaves the workgroup (plus the logits and softmax statistics
 // when the caller keeps them).
 //
-// Waves: WE expert groups x WK K ranges (WE * WK = 4).  Wave w owns experts
+// Waves: WE expert groups x WK K ranges (WE * WK = 4, or WE = 8 with one K
+// range when a workgroup streams a large router matrix).  Wave w owns experts
 // [eg*EPW, (eg+1)*EPW), eg = w % WE, and the K32 steps
-// [kq*S/WK, (kq+1)*S/WK), kq = w / WE, S = H / 32.  Operands are loaded
+// [kq*S/WK, (kq+1)*S/WK), kq = w / WE, S = H / 32.  Router rows are loaded
 // straight into registers, PF steps ahead, four lanes per 64-byte row
 // segment, and moved into the MFMA operand layout (lane l: row l % 16, K
-// values 8*(l/16) .. 8*(l/16)+7 of the step) by a lane permutation; no LDS
-// memory and no barrier until the logits are complete.
+// values 8*(l/16) .. 8*(l/16)+7 of the step) by a lane permutation.  Rows
+// of x take the same path when the waves split K; when they split only the
+// experts, the waves share x through LDS, one barrier per PF steps.
 //
 // Summation (the structure the error bound counts): every MFMA starts from
 // zero (a chain of at most 32 roundings), the results of PF consecutive steps
