@@ -87,6 +87,17 @@ def algorithmic(wl, counts, Is: int = 0, mx: bool = False):
     return st
 
 
+def workload_key(name: str, Is: int = 0, round_tile: int = 0, mx: bool = False,
+                 train: bool = False, cache: bool = True) -> str:
+    """The record's config.workload: the workload's name plus its variant
+    (shared expert of intermediate size Is, token rounding with tile
+    round_tile, MXFP8 experts, forward + backward with or without the cached
+    gate/up sums).  Also the key of the workload's HBM counters in
+    profiles/traffic.json."""
+    return (name + (f"+shared{Is}" if Is else "") + (f"+round{round_tile}" if round_tile else "") +
+            ("+mxfp8" if mx else "") + (("+train" if cache else "+train_recompute") if train else ""))
+
+
 def padding_waste(counts, bm=BM):
     tiles = sum((c + bm - 1) // bm for c in counts)
     return 1.0 - sum(counts) / (tiles * bm) if tiles else 0.0
@@ -422,9 +433,7 @@ def main():
             tr = json.load(f)
         # keyed by the workload string of the record's config (shared expert,
         # rounding, MXFP8 and training variants have their own entries)
-        rec = tr.get(wl.name + (f"+shared{Is}" if Is else "") + (f"+round{RB}" if RB else "") +
-                     ("+mxfp8" if MX else "") +
-                     (("+train" if CACHE else "+train_recompute") if TR else ""), {}).get(dom)
+        rec = tr.get(workload_key(wl.name, Is, RB, MX, TR, CACHE), {}).get(dom)
         if rec and rec.get("source_sha256") == gemm_source_hash():
             roof["traffic"] = rec["bytes_per_launch"]
     except (OSError, ValueError):
@@ -446,9 +455,7 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8" if MX else "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) weights)",
-        "config": {"workload": wl.name + (f"+shared{Is}" if Is else "") +
-                   (f"+round{RB}" if RB else "") + ("+mxfp8" if MX else "") +
-                   (("+train" if CACHE else "+train_recompute") if TR else ""), "tokens": wl.T,
+        "config": {"workload": workload_key(wl.name, Is, RB, MX, TR, CACHE), "tokens": wl.T,
                    "hidden": wl.H, "experts": wl.E, "top_k": wl.k, "intermediate": wl.I,
                    "shared_intermediate": Is, "round_tile": RB, "renormalize": wl.renormalize,
                    "router_bias": wl.bias, "parallelism": "single GPU"},
