@@ -196,6 +196,64 @@ def standalone_calls(B, x, wr, bias, w13, w2, wl, iters: int = 10):
     return res
 
 
+def library_reference(torch, B, wl, x, w13, w2, iters: int = 10):
+    """The vendor library on the expert GEMM shapes of the workload, for
+    context: torch.matmul (hipBLASLt) of M = T*k rows against one expert's
+    weights (dense: all rows in one GEMM) and against each expert's weights in
+    turn (M/E rows each: the per-expert loop without gather, ragged tails or
+    fused epilogue).  Operands as the library stores them (weights [N, K]
+    row-major, read through a transposed view, K contiguous on both sides);
+    two-dimensional products only.  Beside them, this library's grouped GEMM
+    (both GEMMs of moe_grouped_swiglu_gemm) on the same dense problem: one
+    expert holding all M rows."""
+    M, H, I, E = wl.T * wl.k, wl.H, wl.I, wl.E
+    if wl.dtype != "bf16" or M % E:
+        raise SystemExit("bench.py: --library-reference needs a bf16 workload with T*k a multiple of E")
+    g = torch.Generator(device=x.device).manual_seed(0)
+    a = torch.randn(M, H, device=x.device, generator=g).to(torch.bfloat16)
+    h = torch.randn(M, I, device=x.device, generator=g).to(torch.bfloat16)
+    m = M // E
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    def per_expert(src, w):
+        for e in range(E):
+            torch.matmul(src[e * m:(e + 1) * m], w[e].t())
+
+    off = torch.tensor([0, M], dtype=torch.int32, device=x.device)
+    h_out = torch.empty(M, I, dtype=torch.bfloat16, device=x.device)
+    y_out = torch.empty(M, H, dtype=torch.bfloat16, device=x.device)
+    runs = {
+        "this_library_dense_gate_up_and_down": (
+            lambda: B.moe_grouped_swiglu_gemm(a, off, w13[0:1], w2[0:1], h_out, y_out), 6 * M * H * I,
+            f"{M}x{2 * I}x{H} + {M}x{H}x{I}"),
+        "dense_gate_up": (lambda: torch.matmul(a, w13[0].t()), 4 * M * H * I, f"{M}x{2 * I}x{H}"),
+        "dense_down": (lambda: torch.matmul(h, w2[0].t()), 2 * M * I * H, f"{M}x{H}x{I}"),
+        "per_expert_gate_up": (lambda: per_expert(a, w13), 4 * M * H * I, f"{E} x {m}x{2 * I}x{H}"),
+        "per_expert_down": (lambda: per_expert(h, w2), 2 * M * I * H, f"{E} x {m}x{H}x{I}"),
+    }
+    out = {}
+    for name, (fn, flops, shape) in runs.items():
+        ms = timed(fn)
+        tf = flops / ms / 1e9
+        out[name] = {"shape (MxNxK)": shape, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return {"library_reference": out, "workload": wl.name, "library": "torch.matmul (hipBLASLt)",
+            "torch": torch.__version__, "iterations": iters, "statistic": "median"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +280,10 @@ def main():
     ap.add_argument("--mxfp8", action="store_true",
                     help="MXFP8 expert GEMMs (moe_forward_mxfp8; weights quantized once, "
                          "before the timed steps)")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="instead of the MoE block: time the vendor library (torch.matmul, "
+                         "hipBLASLt) on dense and per-expert equivalents of the workload's two "
+                         "expert GEMM shapes, for context")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -260,6 +322,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     x, wr, w13, w2 = up(inp.x), up(inp.w_router), up(inp.w13), up(inp.w2)
+    if args.library_reference:
+        print(json.dumps(library_reference(torch, B, wl, x, w13, w2)))
+        return
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
     dt_code = B.MOE_DTYPE_BF16 if wl.dtype == "bf16" else B.MOE_DTYPE_F32
     out = torch.empty((wl.T, wl.H), dtype=x.dtype, device=dev)
