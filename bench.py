@@ -147,7 +147,8 @@ def standalone_calls(B, x, wr, bias, w13, w2, wl, iters: int = 10):
     with the gathered rows, grouped SwiGLU GEMM, combine) over ``iters`` runs
     after one warm-up, buffers and workspaces allocated beforehand; and their
     sum.  The fused moe_forward gathers rows while loading instead of writing
-    x_perm, so the sum is expected to exceed its time."""
+    x_perm, so the sum is expected to exceed its time.  Also the median time
+    of torch device copies of x-sized and y-sized buffers (not in the sum)."""
     import torch
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     dev = x.device
@@ -193,6 +194,24 @@ def standalone_calls(B, x, wr, bias, w13, w2, wl, iters: int = 10):
             times.append(e0.elapsed_time(e1))
         res[name + "_ms"] = round(sorted(times)[len(times) // 2], 5)
     res["sum_ms"] = round(sum(v for n, v in res.items()), 5)
+    # Context for the memory-bound entry points: torch's own device copies
+    # of an x-sized buffer (the router reads x once) and of a y-sized one
+    # (the combine reads y once), timed the same way.
+    xa, xb = torch.empty_like(x), torch.empty_like(x)
+    ya = torch.empty_like(y)
+    ya.zero_()
+    for name, fn in (("copy_x", lambda: xb.copy_(xa)), ("copy_y", lambda: y.copy_(ya))):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        res[name + "_ms"] = round(sorted(times)[len(times) // 2], 5)
     return res
 
 
