@@ -795,12 +795,34 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       lg[0][tk][e] = v;
     }
   }
-  if (tid < E) {
-    float w2 = 0.f;
+  {
+    // largest squared router-row norm and |bias|: the values are
+    // non-negative, so their bit patterns order as they do; a maximum over
+    // the wave first, then one LDS atomic per wave (one per expert cost
+    // 3-5 us per call with 64-256 experts)
+    float w2 = 0.f, bm = 0.f;
+    if (tid < E) {
 #pragma unroll
-    for (int q = 0; q < WK; ++q) w2 += wsq_s[q][tid];
-    atomicMax(&wmax_bits, __float_as_uint(w2));
-    if (a.bias) atomicMax(&bmax_bits, __float_as_uint(fabsf(a.bias[tid])));
+      for (int q = 0; q < WK; ++q) w2 += wsq_s[q][tid];
+      if (a.bias) bm = fabsf(a.bias[tid]);
+    }
+    unsigned wb = __float_as_uint(w2), bb = __float_as_uint(bm);
+    wb = max(wb, static_cast<unsigned>(xor_lane<1>(static_cast<int>(wb))));
+    bb = max(bb, static_cast<unsigned>(xor_lane<1>(static_cast<int>(bb))));
+    wb = max(wb, static_cast<unsigned>(xor_lane<2>(static_cast<int>(wb))));
+    bb = max(bb, static_cast<unsigned>(xor_lane<2>(static_cast<int>(bb))));
+    wb = max(wb, static_cast<unsigned>(xor_lane<4>(static_cast<int>(wb))));
+    bb = max(bb, static_cast<unsigned>(xor_lane<4>(static_cast<int>(bb))));
+    wb = max(wb, static_cast<unsigned>(xor_lane<8>(static_cast<int>(wb))));
+    bb = max(bb, static_cast<unsigned>(xor_lane<8>(static_cast<int>(bb))));
+    wb = max(wb, static_cast<unsigned>(xor_lane<16>(static_cast<int>(wb))));
+    bb = max(bb, static_cast<unsigned>(xor_lane<16>(static_cast<int>(bb))));
+    wb = max(wb, static_cast<unsigned>(__shfl_xor(static_cast<int>(wb), 32)));
+    bb = max(bb, static_cast<unsigned>(__shfl_xor(static_cast<int>(bb), 32)));
+    if (lane == 0 && wave * 64 < E) {
+      atomicMax(&wmax_bits, wb);
+      if (a.bias) atomicMax(&bmax_bits, bb);
+    }
   }
   __syncthreads();
 

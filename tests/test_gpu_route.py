@@ -49,6 +49,15 @@ CASES = [
     (1000, 320, 128, 8, "bf16", True, "zero"),
     (8192 + 8, 704, 256, 8, "bf16", False, "zero"),
     (40, 448, 160, 4, "bf16", False, "zipf1.2"),
+    # the DMA-fed router (more than 16 experts): 32 to 128 tokens per
+    # workgroup with 3 or 4 stage buffers, K in 64-wide stages (S = H / 64)
+    # grouped by 4; stage counts below, at and past the pipeline depth, with
+    # and without a partial last group
+    (32768 + 100, 256, 64, 4, "bf16", False, "zipf1.2"),
+    (16384 + 50, 320, 128, 8, "bf16", True, "zero"),
+    (20000, 192, 48, 6, "bf16", False, "zero"),
+    (600, 1088, 96, 3, "bf16", False, "zipf1.2"),
+    (8192 + 3, 128, 256, 2, "bf16", True, "zipf1.2"),
     (100, 64, 8, 2, "f32", False, "zero"),
     (257, 256, 64, 4, "f32", True, "zero"),
     (65, 128, 256, 8, "f32", False, "zipf1.2"),
