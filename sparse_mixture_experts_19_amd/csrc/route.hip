@@ -43,6 +43,43 @@ __device__ __forceinline__ float xor_sum8(float v) {   // sum over an 8-lane gro
   return v;
 }
 
+// Top-k scan keys.  logit_key orders as the logits do (larger value,
+// larger key; -0 and +0, which compare equal, share a key), so a lane's best
+// element is one signed integer compare per element and the scan compiles
+// to selects rather than branches; a NaN logit, which no comparison selects,
+// gets kNoKey, the key of elements out of range or already taken.
+constexpr int kNoKey = -2147483647 - 1;
+__device__ __forceinline__ int logit_key(float v) {
+  const int b = __float_as_int(v + 0.f);
+  return v != v ? kNoKey : (b ^ ((b >> 31) & 0x7fffffff));
+}
+__device__ __forceinline__ float key_logit(int key) {   // inverse, for keys other than kNoKey
+  return __int_as_float(key ^ ((key >> 31) & 0x7fffffff));
+}
+
+// One round of the per-lane scan: the lane's largest remaining logit and
+// its expert (elements e = sub + LPT i, ties to the lowest e, i.e. the first
+// in scan order); -inf and 0x7fffffff when none is left.
+template <int PER, int LPT>
+__device__ __forceinline__ void lane_best(const int (&key)[PER], int sub, float& bv, int& be) {
+  int bk = kNoKey;
+  be = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool better = key[i] > bk;
+    bk = better ? key[i] : bk;
+    be = better ? sub + LPT * i : be;
+  }
+  bv = bk == kNoKey ? -INFINITY : key_logit(bk);
+}
+
+// The round's winner (group-wide) leaves the scan: its owner lane drops it.
+template <int PER, int LPT>
+__device__ __forceinline__ void drop_taken(int (&key)[PER], int sub, int be) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = be == sub + LPT * i ? kNoKey : key[i];
+}
+
 // delta from the squared norms (see file comment).
 __device__ __forceinline__ float route_delta(float xsq, float wsq_max, float bmax, int depth) {
   float S = sqrtf(xsq) * sqrtf(wsq_max) * kSafety * kSafety + bmax;
@@ -75,21 +112,18 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t0, flo
   }
 
   // k rounds of (max value, lowest id) selection over the LPT-lane group.
-  uint32_t taken = 0;
+  int key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = sub + LPT * i < E ? logit_key(v[i]) : kNoKey;
   float sel_v[kMaxK];
   int sel_e[kMaxK];
   float vk = 0.f;        // the k-th largest logit (kept without a runtime index)
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int e = sub + LPT * i;
-        bool free_ = !((taken >> i) & 1u) && e < E;
-        if (free_ && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-      }
+      float bv;
+      int be;
+      lane_best<PER, LPT>(key, sub, bv, be);
 #pragma unroll
       for (int off = 1; off < LPT; off <<= 1) {
         float ov = __shfl_xor(bv, off);
@@ -99,7 +133,7 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t0, flo
       sel_v[j] = bv;
       sel_e[j] = be;
       if (j == k - 1) vk = bv;
-      if ((be % LPT) == sub) taken |= 1u << (be / LPT);
+      drop_taken<PER, LPT>(key, sub, be);
     }
   }
 
@@ -844,24 +878,21 @@ __global__ __launch_bounds__(64 * WE * WK) void route_fused_bf16_kernel(RouteArg
       const int e = sub + LPT * i;
       v[i] = (e < E) ? lg[0][tok][e] + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
     }
-    uint32_t taken = 0;
+    int key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = sub + LPT * i < E ? logit_key(v[i]) : kNoKey;
     float sel_v[kMaxK];
     int sel_e[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j < k) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int e = sub + LPT * i;
-          const bool free_ = !((taken >> i) & 1u) && e < E;
-          if (free_ && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-        }
+        float bv;
+        int be;
+        lane_best<PER, LPT>(key, sub, bv, be);
         group_argmax<LPT>(bv, be);
         sel_v[j] = bv;
         sel_e[j] = be;
-        if ((be % LPT) == sub) taken |= 1u << (be / LPT);
+        drop_taken<PER, LPT>(key, sub, be);
       }
     }
     const float mx = sel_v[0];
