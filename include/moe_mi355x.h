@@ -95,6 +95,10 @@ typedef enum moe_entry {
  *                the token's k probabilities.
  *   workspace    device scratch of moe_workspace_size(MOE_ENTRY_ROUTE, ...)
  *                bytes; contents on entry are ignored.
+ * x, w_router and router_bias must hold finite values (the error bound that
+ * decides which tokens are re-ranked is built from their norms); with an
+ * infinity or NaN among them the ids and weights are unspecified.  The same
+ * holds for every entry point that routes.
  */
 int moe_route(const void* x, const void* w_router, const float* router_bias,
               int64_t T, int32_t H, int32_t E, int32_t k, int32_t dtype,
