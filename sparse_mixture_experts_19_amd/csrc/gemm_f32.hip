@@ -7,8 +7,10 @@
 // one launch, [Qwen3-MoE page] §2.1), for fp32 workloads: fp32 fused
 // multiply-adds on the vector ALUs, summed in K order, so no reduced-precision
 // matrix path touches the data.  64x64 output tiles, 16-wide K stages through
-// LDS, 4x4 outputs per thread (the swiglu kernel keeps 4x4 gate and 4x4 up
-// sums and applies silu(g)*u before storing).
+// two LDS buffers (the next stage's loads are issued before the current one
+// is multiplied, one barrier per stage), 4x4 outputs per thread (the swiglu
+// kernel keeps 4x4 gate and 4x4 up sums and applies silu(g)*u before
+// storing).
 #include "moe_internal.h"
 
 namespace moe {
@@ -19,8 +21,8 @@ constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BR = SWIGLU ? 2 * BN : BN;   // weight rows per tile
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BR + 4];
+  __shared__ float As[2][BK][BM + 4];
+  __shared__ float Bs[2][BK][BR + 4];
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_pre[kMaxE + 1];
 
@@ -80,27 +82,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) { acc[i][j] = 0.f; accu[i][j] = 0.f; }
 
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      __syncthreads();
-      const float4 av = *reinterpret_cast<const float4*>(ap + k0);
-      As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
+    // stage loads go to registers first, so that the next stage's global
+    // loads are in flight while the current one is multiplied
+    float4 av, bv[BR / 64];
+    auto load = [&](int k0) {
+      av = *reinterpret_cast<const float4*>(ap + k0);
+#pragma unroll
+      for (int h = 0; h < BR / 64; ++h) bv[h] = *reinterpret_cast<const float4*>(bp[h] + k0);
+    };
+    auto store = [&](int buf) {
+      As[buf][lk + 0][lr] = av.x; As[buf][lk + 1][lr] = av.y; As[buf][lk + 2][lr] = av.z;
+      As[buf][lk + 3][lr] = av.w;
 #pragma unroll
       for (int h = 0; h < BR / 64; ++h) {
-        const float4 bv = *reinterpret_cast<const float4*>(bp[h] + k0);
         const int c = h * 64 + lr;
-        Bs[lk + 0][c] = bv.x; Bs[lk + 1][c] = bv.y; Bs[lk + 2][c] = bv.z; Bs[lk + 3][c] = bv.w;
+        Bs[buf][lk + 0][c] = bv[h].x; Bs[buf][lk + 1][c] = bv[h].y; Bs[buf][lk + 2][c] = bv[h].z;
+        Bs[buf][lk + 3][c] = bv[h].w;
       }
-      __syncthreads();
+    };
+    __syncthreads();                 // the previous tile's reads of both buffers are done
+    load(0);
+    store(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      const bool more = k0 + BK < K;
+      if (more) load(k0 + BK);
 #pragma unroll
       for (int kk = 0; kk < BK; ++kk) {
         float av4[4], bv4[4], uv4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av4[i] = As[kk][ty * 4 + i];
+        for (int i = 0; i < 4; ++i) av4[i] = As[buf][kk][ty * 4 + i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv4[j] = Bs[kk][tx * 4 + j];
+        for (int j = 0; j < 4; ++j) bv4[j] = Bs[buf][kk][tx * 4 + j];
         if constexpr (SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) uv4[j] = Bs[kk][BN + tx * 4 + j];
+          for (int j = 0; j < 4; ++j) uv4[j] = Bs[buf][kk][BN + tx * 4 + j];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -110,6 +127,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
             if constexpr (SWIGLU) accu[i][j] = fmaf(av4[i], uv4[j], accu[i][j]);
           }
       }
+      // the other buffer was last read before the previous barrier
+      if (more) store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
 
 #pragma unroll
