@@ -6,10 +6,11 @@
 // Same two operations and tile schedule as the bf16 kernels (all experts in
 // one launch, [Qwen3-MoE page] §2.1), for fp32 workloads: fp32 fused
 // multiply-adds on the vector ALUs, summed in K order, so no reduced-precision
-// matrix path touches the data.  64x64 output tiles, 16-wide K stages through
-// two LDS buffers (the next stage's loads are issued before the current one
-// is multiplied, one barrier per stage), 4x4 outputs per thread (the swiglu
-// kernel keeps 4x4 gate and 4x4 up sums and applies silu(g)*u before
+// matrix path touches the data.  64x32 output tiles (so that the small
+// fp32 problems still give most CUs a tile), 16-wide K stages through two
+// LDS buffers (the next stage's loads are issued before the current one is
+// multiplied, one barrier per stage), 4x2 outputs per thread (the swiglu
+// kernel keeps 4x2 gate and 4x2 up sums and applies silu(g)*u before
 // storing).
 #include "moe_internal.h"
 
@@ -21,6 +22,8 @@ constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BR = SWIGLU ? 2 * BN : BN;   // weight rows per tile
+  constexpr int TN = BN / 16;                // output columns per thread
+  static_assert(BM == 64 && BR <= 64 && BN % 16 == 0, "one 64-row load group per operand");
   __shared__ float As[2][BK][BM + 4];
   __shared__ float Bs[2][BK][BR + 4];
   __shared__ int s_off[kMaxE + 1];
@@ -62,42 +65,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       src = src < 0 ? 0 : (src >= a.a_rows ? a.a_rows - 1 : src);
     }
     const float* ap = Ab + src * K + lk;
-    const float* bp[BR / 64];
-#pragma unroll
-    for (int h = 0; h < BR / 64; ++h) {
+    // weight row of tile column lr (swiglu: gate rows, then up rows); lanes
+    // past BR load a clamped row and store nothing
+    const bool bl = lr < BR;
+    const float* bp;
+    {
       int64_t wr;
       if constexpr (SWIGLU) {
-        const int n = n0 + lr;
-        wr = (n < a.I ? n : a.I - 1) + (h == 1 ? a.I : 0);
+        const int c = lr < BN ? lr : lr - BN;
+        const int n = n0 + c;
+        wr = (n < a.I ? n : a.I - 1) + (lr < BN ? 0 : a.I);
       } else {
-        const int n = n0 + lr;
+        const int n = n0 + (bl ? lr : 0);
         wr = n < N ? n : N - 1;
       }
-      bp[h] = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lk;
+      bp = Bb + static_cast<int64_t>(e) * a.b_stride + wr * K + lk;
     }
 
-    float acc[4][4], accu[4][4];
+    float acc[4][TN], accu[4][TN];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { acc[i][j] = 0.f; accu[i][j] = 0.f; }
+      for (int j = 0; j < TN; ++j) { acc[i][j] = 0.f; accu[i][j] = 0.f; }
 
     // stage loads go to registers first, so that the next stage's global
     // loads are in flight while the current one is multiplied
-    float4 av, bv[BR / 64];
+    float4 av, bv;
     auto load = [&](int k0) {
       av = *reinterpret_cast<const float4*>(ap + k0);
-#pragma unroll
-      for (int h = 0; h < BR / 64; ++h) bv[h] = *reinterpret_cast<const float4*>(bp[h] + k0);
+      bv = *reinterpret_cast<const float4*>(bp + k0);
     };
     auto store = [&](int buf) {
       As[buf][lk + 0][lr] = av.x; As[buf][lk + 1][lr] = av.y; As[buf][lk + 2][lr] = av.z;
       As[buf][lk + 3][lr] = av.w;
-#pragma unroll
-      for (int h = 0; h < BR / 64; ++h) {
-        const int c = h * 64 + lr;
-        Bs[buf][lk + 0][c] = bv[h].x; Bs[buf][lk + 1][c] = bv[h].y; Bs[buf][lk + 2][c] = bv[h].z;
-        Bs[buf][lk + 3][c] = bv[h].w;
+      if (bl) {
+        Bs[buf][lk + 0][lr] = bv.x; Bs[buf][lk + 1][lr] = bv.y; Bs[buf][lk + 2][lr] = bv.z;
+        Bs[buf][lk + 3][lr] = bv.w;
       }
     };
     __syncthreads();                 // the previous tile's reads of both buffers are done
@@ -110,19 +113,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       if (more) load(k0 + BK);
 #pragma unroll
       for (int kk = 0; kk < BK; ++kk) {
-        float av4[4], bv4[4], uv4[4];
+        float av4[4], bv4[TN], uv4[TN];
 #pragma unroll
         for (int i = 0; i < 4; ++i) av4[i] = As[buf][kk][ty * 4 + i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv4[j] = Bs[buf][kk][tx * 4 + j];
+        for (int j = 0; j < TN; ++j) bv4[j] = Bs[buf][kk][tx * TN + j];
         if constexpr (SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) uv4[j] = Bs[buf][kk][BN + tx * 4 + j];
+          for (int j = 0; j < TN; ++j) uv4[j] = Bs[buf][kk][BN + tx * TN + j];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < TN; ++j) {
             acc[i][j] = fmaf(av4[i], bv4[j], acc[i][j]);
             if constexpr (SWIGLU) accu[i][j] = fmaf(av4[i], uv4[j], accu[i][j]);
           }
@@ -139,8 +142,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       if (m >= rows) continue;
       float* crow = Cb + static_cast<int64_t>(a.scatter ? a.scatter[r0 + m] : r0 + m) * N;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + tx * 4 + j;
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + tx * TN + j;
         if (n >= N) continue;
         float v = acc[i][j];
         if constexpr (SWIGLU) v = (v / (1.f + __expf(-v))) * accu[i][j];

@@ -20,7 +20,7 @@ constexpr int kGemmBK = 64;            // bf16 grouped GEMM: K per LDS stage (MX
 constexpr int kGemmPieces = 256;       // MFMA grouped GEMMs: most K-split partial tiles
 constexpr int kMxBlock = 32;           // MXFP8: values per E8M0 scale
 constexpr int kF32BM = 64;             // fp32 grouped GEMM tile
-constexpr int kF32BN = 64;
+constexpr int kF32BN = 32;
 constexpr int kF32BK = 16;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
