@@ -8,8 +8,8 @@
 // multiply-adds on the vector ALUs, summed in K order, so no reduced-precision
 // matrix path touches the data.  64x32 output tiles (so that the small
 // fp32 problems still give most CUs a tile), 16-wide K stages through two
-// LDS buffers (the next stage's loads are issued before the current one is
-// multiplied, one barrier per stage), 4x2 outputs per thread (the swiglu
+// LDS buffers fed from registers that run two stages ahead (one barrier per
+// stage), 4x2 outputs per thread (the swiglu
 // kernel keeps 4x2 gate and 4x2 up sums and applies silu(g)*u before
 // storing).
 #include "moe_internal.h"
@@ -88,14 +88,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) { acc[i][j] = 0.f; accu[i][j] = 0.f; }
 
-    // stage loads go to registers first, so that the next stage's global
-    // loads are in flight while the current one is multiplied
-    float4 av, bv;
-    auto load = [&](int k0) {
+    // stage loads go to registers first: while stage s is multiplied, stage
+    // s + 1 waits in registers (av1, bv1) and stage s + 2 is being loaded
+    auto load = [&](int k0, float4& av, float4& bv) {
       av = *reinterpret_cast<const float4*>(ap + k0);
       bv = *reinterpret_cast<const float4*>(bp + k0);
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const float4& av, const float4& bv) {
       As[buf][lk + 0][lr] = av.x; As[buf][lk + 1][lr] = av.y; As[buf][lk + 2][lr] = av.z;
       As[buf][lk + 3][lr] = av.w;
       if (bl) {
@@ -104,13 +103,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       }
     };
     __syncthreads();                 // the previous tile's reads of both buffers are done
-    load(0);
-    store(0);
+    float4 av1, bv1;
+    load(0, av1, bv1);
+    store(0, av1, bv1);
+    if (BK < K) load(BK, av1, bv1);
     __syncthreads();
     int buf = 0;
     for (int k0 = 0; k0 < K; k0 += BK) {
-      const bool more = k0 + BK < K;
-      if (more) load(k0 + BK);
+      const bool more = k0 + BK < K;          // stage s + 1 exists (in av1, bv1)
+      float4 av2 = av1, bv2 = bv1;
+      if (k0 + 2 * BK < K) load(k0 + 2 * BK, av2, bv2);
 #pragma unroll
       for (int kk = 0; kk < BK; ++kk) {
         float av4[4], bv4[TN], uv4[TN];
@@ -131,8 +133,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
           }
       }
       // the other buffer was last read before the previous barrier
-      if (more) store(buf ^ 1);
+      if (more) store(buf ^ 1, av1, bv1);
       __syncthreads();
+      av1 = av2;
+      bv1 = bv2;
       buf ^= 1;
     }
 
