@@ -21,8 +21,7 @@
 // two adjacent top-k logits are within 2*delta.  Flagged tokens are re-ranked
 // with float64 dot products (exact products, float64 sums) over the
 // candidate set {e : L_k - L_e <= 2*delta}, which provably contains the exact
-// top-k: in the same workgroup on the bf16 path, by route_refine_kernel on
-// the fp32 path.
+// top-k, in the same workgroup that selected them.
 #include "moe_internal.h"
 #include "cdna4.h"
 
@@ -186,10 +185,16 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t0, flo
   }
 }
 
+template <typename ELEM>
+__device__ __forceinline__ void rerank_token(const RouteArgs& a, int64_t t, const float* row,
+                                             const float* meta, float* cv, int* ce, double* cd);
+
 // ----------------------------------------------------------------- f32 path
 // Plain fp32 FMA chains (no reduced-precision matrix path).  Thread = one
 // token (tid % 32) x experts tid/32 + 8 i.  K is summed in chunks of 64 from
-// zero and the chunk sums are added in order.
+// zero and the chunk sums are added in order.  The workgroup then re-ranks
+// its own flagged tokens (one wave per token) from the logits and softmax
+// statistics the selection wrote for them.
 template <int EP>
 __global__ __launch_bounds__(256) void route_f32_kernel(RouteArgs a) {
   constexpr int PER = EP / 8;
@@ -264,6 +269,18 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteArgs a) {
   }
   __syncthreads();
   route_select<EP, 8>(a, t0, lg, delta_s);
+  __syncthreads();                 // this workgroup's flags, logits and statistics are written
+
+  __shared__ float cv[4][kMaxE];     // re-rank: candidate fp32 logits (per wave)
+  __shared__ int ce[4][kMaxE];       //          candidate expert ids
+  __shared__ double cd[4][kMaxE];    //          logits used for the final ranking
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int tok = wave; tok < RT; tok += 4) {
+    const int64_t t = t0 + tok;
+    if (t >= a.T) break;
+    if (__builtin_amdgcn_readfirstlane(a.flag[t]) == 0) continue;
+    rerank_token<float>(a, t, a.logits + t * a.E, a.meta + t * 4, cv[wave], ce[wave], cd[wave]);
+  }
 }
 
 // ------------------------------------------------------------------ refine
@@ -291,7 +308,7 @@ __device__ __forceinline__ int nth_set_bit(unsigned long long m, int i) {
 // sum, band and k-th logit at meta[0..3]; cv / ce / cd are the wave's own
 // kMaxE-entry scratch arrays.  Writes the token's ids and weights.
 template <typename ELEM>
-__device__ void rerank_token(const RouteArgs& a, int64_t t, const float* row, const float* meta,
+__device__ __forceinline__ void rerank_token(const RouteArgs& a, int64_t t, const float* row, const float* meta,
                              float* cv, int* ce, double* cd) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k, H = a.H;
@@ -442,17 +459,6 @@ __device__ void rerank_token(const RouteArgs& a, int64_t t, const float* row, co
   }
 }
 
-template <typename ELEM>
-__global__ __launch_bounds__(256) void route_refine_kernel(RouteArgs a) {
-  __shared__ float cv[4][kMaxE];     // candidate fp32 logits, in candidate order
-  __shared__ int ce[4][kMaxE];       // candidate expert ids
-  __shared__ double cd[4][kMaxE];    // candidate logits used for the final ranking
-  const int wave = threadIdx.x >> 6;
-  const int64_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
-  if (t >= a.T) return;
-  if (a.flag[t] == 0) return;
-  rerank_token<ELEM>(a, t, a.logits + t * a.E, a.meta + t * 4, cv[wave], ce[wave], cd[wave]);
-}
 
 // ---------------------------------------------------------- fused bf16 path
 // One workgroup owns BT tokens and every expert over the whole of H, and
@@ -1028,10 +1034,7 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
   else if (a.E <= 64) err = launch_f32<64>(a, s);
   else if (a.E <= 128) err = launch_f32<128>(a, s);
   else err = launch_f32<256>(a, s);
-  if (err != hipSuccess) return err;
-  const unsigned grid = static_cast<unsigned>((a.T + 3) / 4);
-  hipLaunchKernelGGL((route_refine_kernel<float>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace moe
