@@ -6,20 +6,22 @@
 // Same two operations and tile schedule as the bf16 kernels (all experts in
 // one launch, [Qwen3-MoE page] §2.1), for fp32 workloads: fp32 fused
 // multiply-adds on the vector ALUs, summed in K order, so no reduced-precision
-// matrix path touches the data.  64x32 output tiles (so that the small
-// fp32 problems still give most CUs a tile), 16-wide K stages through two
-// LDS buffers fed from registers that run two stages ahead (one barrier per
-// stage), 4x2 outputs per thread (the swiglu
-// kernel keeps 4x2 gate and 4x2 up sums and applies silu(g)*u before
-// storing).
+// matrix path touches the data.  64x32 output tiles for gate/up (4x2
+// outputs per thread; 4x2 gate and 4x2 up sums, silu(g)*u applied before
+// storing) and 64x16 for down (4x1), so that the small fp32 problems still
+// give most CUs a tile; 16-wide K stages through two LDS buffers fed from
+// registers that run two stages ahead, one barrier per stage.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = kF32BM, BN = kF32BN, BK = kF32BK;
+constexpr int BM = kF32BM, BK = kF32BK;
 
-template <bool SWIGLU, bool GATHER>
+// BN output columns per tile: kF32BN for the gate/up GEMM (N = I, two
+// weight rows per column), kF32BN / 2 for the down GEMM (N = H), so that
+// both give about as many tiles for the small fp32 problems.
+template <bool SWIGLU, bool GATHER, int BN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BR = SWIGLU ? 2 * BN : BN;   // weight rows per tile
   constexpr int TN = BN / 16;                // output columns per thread
@@ -159,7 +161,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 template <bool SWIGLU, bool GATHER>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_f32_kernel<SWIGLU, GATHER>), dim3(a.grid), dim3(256), 0, s, a);
+  constexpr int BN = SWIGLU ? kF32BN : kF32BN / 2;
+  hipLaunchKernelGGL((gemm_f32_kernel<SWIGLU, GATHER, BN>), dim3(a.grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
