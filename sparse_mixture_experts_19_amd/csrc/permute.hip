@@ -17,6 +17,8 @@
 //      the expert offsets, ranks its elements in order (wave match + LDS
 //      prefix) and writes perm / inv; the first chunk also writes counts,
 //      offsets and, when asked, the grouped GEMM's tile prefix.
+// A problem of one chunk (at most 1024 assignments) counts its histogram in
+// pass 2 itself: one launch.
 // When the histogram table is large (chunks x experts above 32768 entries)
 // those sums would cost each chunk too many loads: a separate pass with one
 // workgroup per expert then turns the table into chunk bases and counts
@@ -93,7 +95,20 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(PermuteArgs a, int nb
   const int E = a.E;
   const int bx = blockIdx.x;
   int cnt = 0, before = 0;   // expert tid: rows in all chunks / in chunks before this one
-  if constexpr (INLINE_SCAN) {
+  if (INLINE_SCAN && nb == 1) {
+    // the whole problem is one chunk: its histogram is counted here and no
+    // separate histogram pass runs (out-of-range ids are dropped, as there)
+    red[0][tid] = 0;
+    __syncthreads();
+    for (int64_t f = tid; f < a.M; f += 256) {
+      const unsigned e = static_cast<unsigned>(a.ids[f]);
+      if (e < static_cast<unsigned>(E)) atomicAdd(&red[0][e], 1);
+    }
+    __syncthreads();
+    if (tid < E) cnt = red[0][tid];
+    if (tid < E) a.counts[tid] = cnt;
+    __syncthreads();                 // red is reused below
+  } else if constexpr (INLINE_SCAN) {
     // thread (g, e) sums chunks g, g + G, ... of column e; eight loads in
     // flight per thread
     const int G = 256 / E;
@@ -281,7 +296,8 @@ size_t permute_scratch_bytes(int64_t M, int E) {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   if (a.tile_prefix && a.tile_bm < 1) return hipErrorInvalidValue;
   const int nb = static_cast<int>((a.M + CH - 1) / CH);
-  hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a);
+  // one chunk: the scatter pass counts its histogram itself
+  if (nb > 1) hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, a);
   if (static_cast<int64_t>(nb) * a.E <= kPermInlineScan) {
     hipLaunchKernelGGL(perm_scatter_kernel<true>, dim3(nb), dim3(256), 0, s, a, nb);
   } else {

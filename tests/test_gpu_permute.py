@@ -37,6 +37,8 @@ def _check(ids, E, x=None, dt="bf16"):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 2), (100, 8, 2), (513, 8, 2), (1000, 64, 4),
+                                   # one chunk of 1024 (histogram counted by the scatter pass)
+                                   (512, 8, 2), (128, 256, 8), (1024, 3, 1),
                                    (777, 128, 8), (300, 256, 8), (4096, 1, 1), (2048, 5, 5),
                                    (1025, 256, 1),
                                    # 293 chunks x 128 experts: the separate scan pass
