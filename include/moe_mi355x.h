@@ -35,8 +35,10 @@
  *   validates on the host and enqueues kernels on `stream`: it does not
  *   allocate, copy to the host or synchronise.  The caller owns every buffer;
  *   the library keeps no device memory and no mutable global state besides a
- *   per-device cache of device properties, so calls on different streams may
- *   run concurrently as long as their buffers do not overlap.
+ *   per-device cache of device properties and the device array that
+ *   moe_permute_static uses instead of a workspace, so calls on different
+ *   streams may run concurrently as long as their buffers do not overlap
+ *   (moe_permute_static calls on one GPU share that array and must not).
  * - Results are deterministic: identical inputs give bitwise identical
  *   outputs (no floating-point atomics anywhere).
  * - Limits: 1 <= k <= E, E <= 256, k <= 8, H and I multiples of 64,
